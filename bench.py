@@ -1,0 +1,224 @@
+"""Benchmark of the attention forward pass on one MI355X.
+
+One step = one fa_forward call over the whole workload (all heads), inputs
+resident in HBM.  Prints one JSON line:
+
+  metric / value / unit   attention forward TFLOP/s (algorithmic FLOPs:
+                          4*B*H*N^2*D, half that when causal) over the timed
+                          region, whole job
+  roofline                the forward kernel against MI355X dense fp16/bf16
+                          matrix-core peak (2.5 PFLOP/s): achieved = FLOPs per
+                          launch / mean kernel duration from HIP events around
+                          every timed launch; traffic = HBM bytes per launch
+                          from rocprofv3 counters when a profile of the
+                          current kernel source is committed, else null
+  cpu_baseline            the fp64 oracle timed on this host's cores on a
+                          bounded sample of the same workload (reported
+                          baseline only)
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+
+import argparse
+import hashlib
+import glob
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads  # noqa: E402
+
+METRIC = "attention fwd TFLOP/s + % MFMA fp16 peak, H=32 D=64 N=2048 (1 GPU)"
+PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}  # MI355X dense peaks
+PEAK_HBM_GBS = 8000.0
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "tiled_attention_fa_amd", "csrc")
+    for p in sorted(glob.glob(os.path.join(csrc, "*"))):
+        h.update(os.path.basename(p).encode())
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(workload: str):
+    """HBM bytes per launch from a committed counter profile of the current
+    kernel source, or None."""
+    path = os.path.join(PROFILE_DIR, f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def torch_inputs(w, x, device):
+    import torch
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[w.dtype]
+    out = []
+    for n in "qkv":
+        a = np.ascontiguousarray(x[n])
+        t = torch.from_numpy(a if w.dtype == "f32" else a.view(np.int16)).view(tdt)
+        out.append(t.to(device))
+    return out
+
+
+def cpu_baseline(w, x, budget_s: float = 20.0):
+    """Time the fp64 oracle on a bounded sample of the workload: whole heads,
+    as many as fit the budget (estimated from one head)."""
+    import oracle
+    BH = w.B * w.H
+    q = x["q"].reshape(BH, 1, w.N, w.D)
+    k = x["k"].reshape(BH, 1, w.N, w.D)
+    v = x["v"].reshape(BH, 1, w.N, w.D)
+    t0 = time.perf_counter()
+    _, _, used = oracle.forward(q[:1], k[:1], v[:1], w.dtype, w.scale, w.causal, return_rowsum=True)
+    one = time.perf_counter() - t0
+    heads = int(max(1, min(BH, budget_s / max(one, 1e-6))))
+    t0 = time.perf_counter()
+    _, _, used = oracle.forward(q[:heads], k[:heads], v[:heads], w.dtype, w.scale, w.causal,
+                                return_rowsum=True)
+    dt = time.perf_counter() - t0
+    flops = workloads.flops(w) * heads / BH
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(used), "kind": "oracle",
+            "sample": f"{heads} of {BH} heads of {w.name} (fp64, S and P rows materialised), "
+                      f"{dt:.2f} s"}
+
+
+def parity_sample(w, x, o):
+    """Max abs error of sampled output rows against the oracle."""
+    import oracle
+    rng = np.random.default_rng(0)
+    BH = w.B * w.H
+    bh = rng.integers(0, BH, 64)
+    ri = rng.integers(0, w.N, 64)
+    ref = oracle.rows(x["q"], x["k"], x["v"], w.dtype, w.scale, w.causal, bh, ri)
+    got = o.float().cpu().numpy().astype(np.float64).reshape(BH, w.N, w.D)[bh, ri]
+    return float(np.abs(got - ref).max())
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=workloads.HEADLINE, choices=workloads.ORDER)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="instead of attention, time a plain device copy of this many MiB "
+                         "(reference kernel for scaling HBM byte counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(heads are independent; see the sharding notes in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import tiled_attention_fa_amd as fa
+
+    dev = torch.device("cuda:0")
+    prop = torch.cuda.get_device_properties(dev)
+    log(f"device: {prop.name} {getattr(prop, 'gcnArchName', '')} CUs={prop.multi_processor_count}")
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * 2 ** 20 // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {args.steps} copies of {args.copy_calibration_mib} MiB")
+        return
+
+    w = workloads.get(args.workload)
+    x = workloads.make_inputs(w)
+    q, k, v = torch_inputs(w, x, dev)
+    o = torch.empty_like(q)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        fa.fa_forward(q, k, v, o, scale=w.scale, causal=w.causal, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region: back-to-back launches, an event pair around each.
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    region0 = torch.cuda.Event(enable_timing=True)
+    region1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    region0.record(stream)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    region1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = region0.elapsed_time(region1)
+    kern_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    ms_per_step = total_ms / args.steps
+    flops = workloads.flops(w)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (float(kern_ms.mean()) * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    log(f"kernel mean {kern_ms.mean() * 1e3:.2f} us, median {np.median(kern_ms) * 1e3:.2f} us, "
+        f"step {ms_per_step * 1e3:.2f} us")
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D,
+                   "storage": w.dtype, "causal": w.causal, "parallelism": "none (1 GPU)"},
+        "pct_peak": round(100 * value / peak, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": committed_traffic(w.name),
+            "kernel_us_mean": round(float(kern_ms.mean()) * 1e3, 3),
+            "kernel_us_median": round(float(np.median(kern_ms)) * 1e3, 3),
+            "min_bytes": workloads.min_bytes(w),
+        },
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if not args.no_check:
+        rec["max_abs_err_sampled"] = parity_sample(w, x, o)
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, x)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,87 @@
+"""The C ABI library on the CPU: it loads, exports every symbol include/fa.h
+declares, and rejects bad arguments before touching any device.  No kernel is
+launched here (there is no GPU in this environment)."""
+
+import os
+import re
+import subprocess
+
+import pytest
+
+import tiled_attention_fa_amd as fa
+from tiled_attention_fa_amd._lib import EXPORTS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return fa.load_library()
+
+
+def test_exports_match_header(lib):
+    names = declared_functions()
+    assert names == sorted(EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (fa_\w+)", out))
+    for n in names:
+        assert n in exported, f"{n} declared in fa.h but not exported"
+        assert hasattr(lib, n)
+
+
+def test_library_targets_gfx950_only():
+    out = subprocess.run(["/opt/rocm/lib/llvm/bin/clang-offload-bundler", "--list", "--type=o",
+                          f"--input={fa.library_path()}"], capture_output=True, text=True)
+    if out.returncode == 0 and out.stdout.strip():
+        targets = [t for t in out.stdout.split() if "amdgcn" in t]
+        assert targets and all("gfx950" in t for t in targets), out.stdout
+
+
+def test_version_and_status_strings(lib):
+    assert "gfx950" in fa.fa_version()
+    texts = {c: fa.fa_status_string(c) for c in fa.STATUS_NAMES}
+    assert texts[0] == "ok"
+    assert len(set(texts.values())) == len(texts)
+    assert fa.fa_status_string(12345) == "unknown status"
+
+
+# Fake, well-aligned, non-overlapping addresses: validation never dereferences.
+A, B_, C, O = 0x100000, 0x200000, 0x300000, 0x400000
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(dtype=7), "FA_ERR_DTYPE"),
+    (dict(B=0), "FA_ERR_DIM"),
+    (dict(H=-1), "FA_ERR_DIM"),
+    (dict(N=-5), "FA_ERR_DIM"),
+    (dict(D=0), "FA_ERR_DIM"),
+    (dict(D=80), "FA_ERR_UNSUPPORTED_D"),
+    (dict(D=256), "FA_ERR_UNSUPPORTED_D"),
+    (dict(scale=float("nan")), "FA_ERR_SCALE"),
+    (dict(scale=float("inf")), "FA_ERR_SCALE"),
+    (dict(N=0, q=0, k=0, v=0, o=0), "FA_OK"),
+    (dict(q=0), "FA_ERR_NULL"),
+    (dict(o=0), "FA_ERR_NULL"),
+    (dict(k=A + 8), "FA_ERR_ALIGN"),
+    (dict(o=A), "FA_ERR_ALIAS"),
+    (dict(o=B_ + 64 * 64 * 2 - 16), "FA_ERR_ALIAS"),
+    (dict(N=1 << 25, D=64), "FA_ERR_TOO_LARGE"),
+    (dict(B=1 << 20, H=1 << 20), "FA_ERR_TOO_LARGE"),
+    (dict(), "FA_ERR_DEVICE"),
+])
+def test_validation(lib, args, status):
+    kw = dict(q=A, k=B_, v=C, o=O, B=1, H=1, N=64, D=64, scale=0.125, causal=False, dtype=1)
+    kw.update(args)
+    got = fa.fa_forward_raw(kw["q"], kw["k"], kw["v"], kw["o"], kw["B"], kw["H"], kw["N"], kw["D"],
+                            kw["scale"], kw["causal"], kw["dtype"])
+    if status == "FA_ERR_DEVICE" and got == 0:
+        pytest.skip("a gfx950 device is present; the no-device path is not reachable")
+    assert fa.STATUS_NAMES[got] == status

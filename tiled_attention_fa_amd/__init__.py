@@ -1,0 +1,23 @@
+"""MI355X (gfx950) FlashAttention forward: Python binding of libfa.so.
+
+The binding only marshals arguments: it reads sizes, dtype, pointers and the
+current HIP stream from torch tensors and calls the C ABI declared in
+include/fa.h.  Every step of the computation runs in the library's kernels.
+There is no fallback: if libfa.so is missing, loading fails with an error
+that says how to build it.
+"""
+
+from ._lib import (  # noqa: F401
+    FA_BF16,
+    FA_F16,
+    FA_F32,
+    FAError,
+    STATUS_NAMES,
+    fa_forward,
+    fa_forward_raw,
+    fa_status_string,
+    fa_version,
+    forward,
+    library_path,
+    load_library,
+)

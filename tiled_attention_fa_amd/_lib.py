@@ -1,0 +1,122 @@
+"""ctypes binding of the C ABI in include/fa.h (argument marshalling only)."""
+
+import ctypes
+import math
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libfa.so")
+
+FA_F32, FA_F16, FA_BF16 = 0, 1, 2
+
+STATUS_NAMES = {
+    0: "FA_OK",
+    -1: "FA_ERR_NULL",
+    -2: "FA_ERR_DIM",
+    -3: "FA_ERR_UNSUPPORTED_D",
+    -4: "FA_ERR_DTYPE",
+    -5: "FA_ERR_ALIGN",
+    -6: "FA_ERR_ALIAS",
+    -7: "FA_ERR_LAUNCH",
+    -8: "FA_ERR_SCALE",
+    -9: "FA_ERR_TOO_LARGE",
+    -10: "FA_ERR_DEVICE",
+}
+
+# Every symbol include/fa.h declares.
+EXPORTS = ("fa_forward", "fa_status_string", "fa_version")
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {fa_status_string(status)}")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libfa.so (built in-tree by __graft_entry__.build() or
+    tiled_attention_fa_amd/build.py).  Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; "
+                          f"g.build()'` or `python tiled_attention_fa_amd/build.py` first")
+    lib = ctypes.CDLL(_LIB_PATH)
+    i64, vp = ctypes.c_int64, ctypes.c_void_p
+    lib.fa_forward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float, ctypes.c_int,
+                               ctypes.c_int, vp]
+    lib.fa_forward.restype = ctypes.c_int
+    lib.fa_status_string.argtypes = [ctypes.c_int]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_version.argtypes = []
+    lib.fa_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def fa_status_string(status: int) -> str:
+    return load_library().fa_status_string(int(status)).decode()
+
+
+def fa_version() -> str:
+    return load_library().fa_version().decode()
+
+
+def fa_forward_raw(q: int, k: int, v: int, o: int, B: int, H: int, N: int, D: int, scale: float,
+                   causal: bool, dtype: int, stream: int = 0) -> int:
+    """Direct call of the C entry point with integer addresses; returns the
+    status code (no exception)."""
+    return load_library().fa_forward(q or None, k or None, v or None, o or None, int(B), int(H),
+                                     int(N), int(D), float(scale), int(bool(causal)), int(dtype),
+                                     stream or None)
+
+
+def _dtype_code(t):
+    import torch
+    codes = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported tensor dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def fa_forward(q, k, v, o, scale=None, causal=False, stream=None) -> None:
+    """o <- softmax(scale * q k^T [+ causal mask]) v for torch tensors of shape
+    [B, H, N, D] on the current HIP device (contiguous, one dtype).
+    scale defaults to 1/sqrt(D); stream defaults to torch's current stream.
+    Enqueues the kernel and returns; raises FAError on a rejected call."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [B, H, N, D], got shape {tuple(t.shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{name} must match q in shape, dtype and device")
+    if q.device.type != "cuda":
+        raise ValueError("tensors must be on a HIP device")
+    B, H, N, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(q.device):
+        st = fa_forward_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, H, N, D,
+                            scale, causal, _dtype_code(q), handle)
+    if st != 0:
+        raise FAError(st)
+
+
+def forward(q, k, v, scale=None, causal=False, stream=None):
+    """Allocate o like q and run fa_forward; returns o."""
+    import torch
+    o = torch.empty_like(q)
+    fa_forward(q, k, v, o, scale=scale, causal=causal, stream=stream)
+    return o

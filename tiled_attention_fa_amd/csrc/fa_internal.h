@@ -1,0 +1,33 @@
+// Internal interface between the C ABI (fa_api.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+// One validated forward problem: [BH, N, D] tensors (B and H folded).
+struct Problem {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  int64_t BH;
+  int N;
+  int D;
+  float scale;
+  bool causal;
+};
+
+// Query rows per workgroup of each kernel family (the host sizes grids with
+// these; the kernels assert them at compile time).
+constexpr int kMfmaBlockM = 128;
+constexpr int kF32BlockM = 64;
+
+// Kernel launchers.  Each returns the launch status and touches nothing
+// else.  D must be 64, 96 or 128 and N >= 1 (checked by the caller).
+hipError_t launch_mfma_f16(const Problem& p, hipStream_t stream);
+hipError_t launch_mfma_bf16(const Problem& p, hipStream_t stream);
+hipError_t launch_f32(const Problem& p, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,8 @@
+// bf16 instances of the matrix-core forward kernel (P kept as bf16 hi + lo).
+#include "fa_mfma.h"
+
+namespace fa {
+hipError_t launch_mfma_bf16(const Problem& p, hipStream_t stream) {
+  return mfma::launch<__bf16, true>(p, stream);
+}
+}  // namespace fa

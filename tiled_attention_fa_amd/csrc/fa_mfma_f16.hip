@@ -1,0 +1,8 @@
+// fp16 instances of the matrix-core forward kernel (P rounded to fp16 once).
+#include "fa_mfma.h"
+
+namespace fa {
+hipError_t launch_mfma_f16(const Problem& p, hipStream_t stream) {
+  return mfma::launch<_Float16, false>(p, stream);
+}
+}  // namespace fa
