@@ -1,4 +1,5 @@
-// FlashAttention forward for fp32 storage, on the vector ALUs in fp32.
+// FlashAttention forward for fp32 storage, on the vector ALUs (scores in
+// fp64, everything else in fp32).
 //
 // Same tile loop as the matrix-core kernel ("Android Transformer
 // Optimization: Attention and Mobile GPU Bottlenecks", section "A Complete
@@ -32,7 +33,7 @@ struct Args {
   int N;
   int num_qtiles;
   int total_tiles;
-  float c;      // |scale| * log2(e)
+  double c;     // |scale| * log2(e)
   float qsign;  // -1 when scale < 0 (exact sign flip of Q), else +1
 };
 
@@ -60,7 +61,7 @@ __global__ __launch_bounds__(kBlockM) void fa_forward_f32_kernel(Args a) {
   const float* __restrict__ K = a.k + head;
   const float* __restrict__ V = a.v + head;
   float* __restrict__ O = a.o + head;
-  const float c = a.c;
+  const double cd = a.c;
   const int qrow = qt * kBlockM + tid;
 
   float q[D];
@@ -76,7 +77,8 @@ __global__ __launch_bounds__(kBlockM) void fa_forward_f32_kernel(Args a) {
   float acc[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) acc[d] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  double m_run = -INFINITY;
+  float l_run = 0.f;
 
   const int kv_end = CAUSAL ? min(N, qt * kBlockM + kBlockM) : N;
   for (int k0 = 0; k0 < kv_end; k0 += BN) {
@@ -93,34 +95,40 @@ __global__ __launch_bounds__(kBlockM) void fa_forward_f32_kernel(Args a) {
     }
     __syncthreads();
 
-    float s[BN];
-    float mx = -INFINITY;
+    // Scores in fp64: the products of two fp32 values are exact in fp64 and
+    // the D-term sum keeps ~1e-16 relative error, so large logits do not
+    // lose absolute precision before the exponential.
+    double s[BN];
+    double mx = -INFINITY;
 #pragma unroll
     for (int j = 0; j < BN; ++j) {
-      float dot = 0.f;
+      double dot = 0.0;
 #pragma unroll
       for (int d = 0; d < D; d += 4) {
         const f32x4 kx = *(const f32x4*)(Ks + j * D + d);
-        dot = __builtin_fmaf(q[d], kx[0], dot);
-        dot = __builtin_fmaf(q[d + 1], kx[1], dot);
-        dot = __builtin_fmaf(q[d + 2], kx[2], dot);
-        dot = __builtin_fmaf(q[d + 3], kx[3], dot);
+        dot = __builtin_fma((double)q[d], (double)kx[0], dot);
+        dot = __builtin_fma((double)q[d + 1], (double)kx[1], dot);
+        dot = __builtin_fma((double)q[d + 2], (double)kx[2], dot);
+        dot = __builtin_fma((double)q[d + 3], (double)kx[3], dot);
       }
       const int key = k0 + j;
       if (key >= N || (CAUSAL && key > qrow)) dot = -INFINITY;
       s[j] = dot;
-      mx = fmaxf(mx, dot);
+      mx = dot > mx ? dot : mx;
     }
-    const float m_new = fmaxf(m_run, mx);
-    const float mc = (m_new == -INFINITY) ? 0.f : m_new * c;
-    const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run * c - mc);
+    const double m_new = m_run > mx ? m_run : mx;
+    // exp(scale * (s - m)) = exp2(c * (s - m)); the difference is formed in
+    // fp64 before rounding to fp32, so its error is relative to |s - m|.
+    const float alpha =
+        (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((float)((m_run - m_new) * cd));
     m_run = m_new;
+    float pr[BN];
     float psum = 0.f;
 #pragma unroll
     for (int j = 0; j < BN; ++j) {
-      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], c, -mc));
+      float p = __builtin_amdgcn_exp2f((float)((s[j] - m_new) * cd));
       if (s[j] == -INFINITY) p = 0.f;  // masked; also right when c == 0
-      s[j] = p;
+      pr[j] = p;
       psum += p;
     }
     l_run = l_run * alpha + psum;
@@ -131,10 +139,10 @@ __global__ __launch_bounds__(kBlockM) void fa_forward_f32_kernel(Args a) {
 #pragma unroll
       for (int d = 0; d < D; d += 4) {
         const f32x4 vx = *(const f32x4*)(Vs + j * D + d);
-        acc[d] = __builtin_fmaf(s[j], vx[0], acc[d]);
-        acc[d + 1] = __builtin_fmaf(s[j], vx[1], acc[d + 1]);
-        acc[d + 2] = __builtin_fmaf(s[j], vx[2], acc[d + 2]);
-        acc[d + 3] = __builtin_fmaf(s[j], vx[3], acc[d + 3]);
+        acc[d] = __builtin_fmaf(pr[j], vx[0], acc[d]);
+        acc[d + 1] = __builtin_fmaf(pr[j], vx[1], acc[d + 1]);
+        acc[d + 2] = __builtin_fmaf(pr[j], vx[2], acc[d + 2]);
+        acc[d + 3] = __builtin_fmaf(pr[j], vx[3], acc[d + 3]);
       }
     }
   }
@@ -161,7 +169,7 @@ hipError_t launch_f32(const Problem& p, hipStream_t stream) {
   a.N = p.N;
   a.num_qtiles = (p.N + kBlockM - 1) / kBlockM;
   a.total_tiles = (int)(p.BH * a.num_qtiles);
-  a.c = __builtin_fabsf(p.scale) * 1.4426950408889634f;
+  a.c = __builtin_fabs((double)p.scale) * 1.4426950408889634;
   a.qsign = p.scale < 0.f ? -1.f : 1.f;
   void (*kern)(Args) = nullptr;
   if (p.D == 64) kern = p.causal ? fa_forward_f32_kernel<64, true> : fa_forward_f32_kernel<64, false>;

@@ -10,28 +10,41 @@
 // exp(m_old - m_new), adds the tile's exp(S - m_new) to l and exp(S - m_new) V
 // to the accumulator, and at the end divides the accumulator by l once.
 //
-// gfx950 mapping (not from the pages, which target mobile GPUs):
-//  * A workgroup is 4 wave64s and owns kBlockM = 128 query rows of one
-//    (batch, head); each wave owns 32 of them.  Its Q rows are loaded once
-//    into VGPRs, as the B operand of v_mfma_f32_32x32x16_{f16,bf16}.
-//  * Per iteration a 64-key tile of K is staged in LDS row-major and the
-//    matching V tile is staged transposed (V^T, keys contiguous), both with
-//    16-byte row padding so that the ds_read_b128 operand reads of 8
-//    consecutive lanes hit 8 distinct 4-bank groups.
-//  * Scores are computed transposed, S^T = K Q^T, so each lane holds 16
-//    keys x 1 query per 32-key block: row max and row sum are in-lane,
-//    plus one exchange between the two 32-lane halves.
-//  * The exp'd scores are converted to 16 bits in registers and fed back as
-//    the B operand of O^T += V^T P^T.  The accumulator layout puts, for lane
-//    half h, keys {4h..4h+3, 8+4h..8+4h+3} of each 16-key chunk in
-//    consecutive elements; V^T is stored with the second and third 4-key
-//    groups of every 16 keys swapped so that each lane's A operand is one
-//    contiguous 16-byte read with the same key order.
+// gfx950 mapping (the pages target mobile GPUs; none of this is from them):
+//  * A workgroup is NW wave64s and owns BM = NW * WM query rows of one
+//    (batch, head); each wave owns WM (32 or 64) of them, in WM/32 column
+//    blocks.  A wave's Q rows are loaded once into VGPRs as the B operand of
+//    v_mfma_f32_32x32x16_{f16,bf16}.
+//  * K and V tiles of 64 keys are loaded with 16-byte coalesced loads into
+//    registers one iteration ahead (the loads of tile t+1 are in flight while
+//    tile t is computed) and stored row-major into a double-buffered LDS
+//    area, so one barrier per tile suffices.
+//  * Scores are computed transposed, S^T = K Q^T: each lane holds 16 keys of
+//    one query per 32-key block, so row max and row sum are in-lane plus one
+//    exchange between the two 32-lane halves (v_permlane32_swap).
+//  * P^T goes from the score accumulators straight into the B operand of
+//    O^T += V^T P^T (converted to 16 bits in registers).  The V^T A operand
+//    is read from the row-major V tile with ds_read_b64_tr_b16, whose
+//    16-lane transpose hands each lane 4 keys of one head-dim column; the
+//    source addresses are chosen so that lane half h gets keys
+//    {4h..4h+3, 8+4h..8+4h+3} of each 16-key chunk, the key order in which
+//    the score accumulator layout holds P.
+//  * LDS rows are padded (K by 16 bytes, V by 32 bytes) so that the 16-byte
+//    operand reads of K and the 8-byte transpose reads of V hit distinct
+//    banks within each group of lanes the LDS serves together.
 //  * Softmax runs in base 2: p = exp2(s * c - m * c) with c = |scale| *
-//    log2(e) folded into one FMA; a negative scale flips the sign of Q.
-//  * bf16 keeps P as an unevaluated sum of two bf16 numbers (hi + lo) and
-//    issues two PV products, so P carries ~16 significant bits, as fp16 does
-//    with one.
+//    log2(e) in one FMA; a negative scale flips the sign of Q.  The running
+//    maximum is only raised when a tile's maximum exceeds it by more than
+//    kLazy (in log2 units): otherwise the old maximum stays and the tile's p
+//    values may reach 2^kLazy, which fp32 accumulators and 16-bit P hold
+//    without loss; the rescale of O is then skipped for the whole wave.
+//    The result is the same softmax, exp(s - m) / sum exp(s - m), for any
+//    choice of m.
+//  * fp16: P is rounded once to fp16, and l sums exactly those rounded
+//    values (v_dot2_f32_f16 against 1.0), so the weights applied to V sum to
+//    one.  bf16: P is kept as an unevaluated sum of two bf16 numbers
+//    (hi + lo) and two PV products are issued, so P carries ~16 significant
+//    bits, as with fp16; l sums the fp32 p.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -49,15 +62,13 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
-constexpr int kBlockM = kMfmaBlockM;  // query rows per workgroup
-constexpr int kWaveM = 32;            // query rows per wave
-constexpr int kWaves = kBlockM / kWaveM;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kBlockN = 64;           // keys per iteration
-constexpr int kPad = 8;               // 16-byte LDS row padding (in 16-bit elements)
-constexpr int kXcds = 8;              // MI355X: 8 accelerator complex dies
-static_assert(kWaves == 4, "4 waves per workgroup");
+constexpr int kBlockN = 64;  // keys per iteration
+constexpr int kXcds = 8;     // MI355X: 8 accelerator complex dies, one L2 each
+constexpr float kLazy = 8.f;  // log2 of the largest p the lazy maximum allows
 
 struct Args {
   const uint16_t* q;
@@ -65,7 +76,7 @@ struct Args {
   const uint16_t* v;
   uint16_t* o;
   int N;
-  int num_qtiles;   // ceil(N / kBlockM)
+  int num_qtiles;   // ceil(N / BM)
   int total_tiles;  // BH * num_qtiles
   float c;          // |scale| * log2(e)
   uint32_t qxor;    // 0x80008000 flips the sign of both halves when scale < 0
@@ -92,6 +103,11 @@ struct Ops<_Float16> {
   }
   static __device__ __forceinline__ float hi_to_f32(uint32_t w) {
     return (float)__builtin_bit_cast(f16x2, w)[1];
+  }
+  // acc + w.lo + w.hi, exact products with 1.0 and fp32 accumulation.
+  static __device__ __forceinline__ float add_pair(uint32_t w, float acc) {
+    const f16x2 one = {(_Float16)1.f, (_Float16)1.f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), one, acc, false);
   }
 };
 
@@ -125,7 +141,7 @@ __device__ __forceinline__ int xcd_remap(int wg, int total) {
   return x * per + (x < extra ? x : extra) + slot;
 }
 
-// Both 32-lane halves combined with a symmetric op: after the swap each lane
+// Combine both 32-lane halves with a symmetric op: after the swap each lane
 // holds its own value and its partner's (lane ^ 32), in some order.
 __device__ __forceinline__ float half_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
@@ -138,20 +154,35 @@ __device__ __forceinline__ float half_sum(float x) {
   return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
-// Position of key group g (4 keys) inside its 16-key chunk of V^T: groups 1
-// and 2 trade places (see the header comment).
-__device__ __forceinline__ int vt_group(int g) { return (g == 1 || g == 2) ? 3 - g : g; }
+__device__ __forceinline__ u32x2 tr_read(const uint16_t* p) {
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_u16*)p);
+  return __builtin_bit_cast(u32x2, r);
+}
 
-template <typename T, int D, bool CAUSAL, bool SPLIT_P>
-__global__ __launch_bounds__(kThreads, 2) void fa_forward_kernel(Args a) {
-  constexpr int BN = kBlockN;
-  constexpr int KS = D + kPad;   // K row stride in LDS (elements)
-  constexpr int VS = BN + kPad;  // V^T row stride in LDS (elements)
-  constexpr int DC = D / 16;     // 16-wide contraction chunks of QK^T
-  constexpr int DB = D / 32;     // 32-row blocks of O^T
+template <int D, int WM, int NW>
+struct Shape {
+  static constexpr int BN = kBlockN;
+  static constexpr int BM = WM * NW;
+  static constexpr int QB = WM / 32;     // 32-query column blocks per wave
+  static constexpr int NT = 64 * NW;     // threads per workgroup
+  static constexpr int KS = D + 8;       // K row stride in LDS (elements)
+  static constexpr int VS = D + 16;      // V row stride in LDS (elements)
+  static constexpr int DC = D / 16;      // 16-wide contraction chunks of QK^T
+  static constexpr int DB = D / 32;      // 32-row blocks of O^T
+  static constexpr int CH = BN * D / 8;  // 16-byte chunks per K (or V) tile
+  static constexpr int CPT = (CH + NT - 1) / NT;  // chunks per thread
+  static constexpr int LDS_BYTES = 2 * BN * (KS + VS) * 2;
   static_assert(D % 32 == 0 && D <= 128, "head dim");
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BN * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VS];
+  static_assert(WM == 32 || WM == 64, "queries per wave");
+};
+
+template <typename T, int D, bool CAUSAL, bool SPLIT_P, int WM, int NW>
+__global__ __launch_bounds__(64 * NW) void fa_forward_kernel(Args a) {
+  using S = Shape<D, WM, NW>;
+  constexpr int BN = S::BN, BM = S::BM, QB = S::QB, NT = S::NT, KS = S::KS, VS = S::VS;
+  constexpr int DC = S::DC, DB = S::DB, CH = S::CH, CPT = S::CPT;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BN * VS];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -171,176 +202,255 @@ __global__ __launch_bounds__(kThreads, 2) void fa_forward_kernel(Args a) {
   uint16_t* __restrict__ O = a.o + head;
   const float c = a.c;
 
-  const int q0 = qt * kBlockM + wave * kWaveM;  // first query row of this wave
-  const int qrow = q0 + l32;                    // this lane's query row
+  const int q0 = qt * BM + wave * WM;  // first query row of this wave
 
-  // Q fragment: row qrow, columns 16*ch + 8*hi .. +7 (B operand layout).
-  u32x4 qf[DC];
+  // Q fragments: query q0 + 32*qb + l32, columns 16*ch + 8*hi .. +7.
+  u32x4 qf[DC][QB];
 #pragma unroll
-  for (int ch = 0; ch < DC; ++ch) {
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (qrow < N) x = *(const u32x4*)(Q + (size_t)qrow * D + 16 * ch + 8 * hi);
-    qf[ch] = x ^ a.qxor;
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qrow = q0 + 32 * qb + l32;
+#pragma unroll
+    for (int ch = 0; ch < DC; ++ch) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (qrow < N) x = *(const u32x4*)(Q + (size_t)qrow * D + 16 * ch + 8 * hi);
+      qf[ch][qb] = x ^ a.qxor;
+    }
   }
 
-  f32x16 oacc[DB];
+  f32x16 oacc[DB][QB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
-  float m_run = -INFINITY;  // running max of raw scores q.k (sign-adjusted)
-  float l_run = 0.f;        // this lane's share of the running denominator
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = f32x16{};
+  float m_run[QB], l_run[QB];  // running max of raw scores; this lane's share of l
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.f;
+  }
 
-  const int kv_end = CAUSAL ? min(N, qt * kBlockM + kBlockM) : N;
+  const int kv_end = CAUSAL ? min(N, qt * BM + BM) : N;
   const int ntiles = (kv_end + BN - 1) / BN;
 
+  // Register staging of one K tile and one V tile (rows >= N read as 0).
+  u32x4 kreg[CPT], vreg[CPT];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int idx = tid + i * NT;
+      if (CH % NT == 0 || idx < CH) {
+        const int r = idx / (D / 8), c8 = idx - r * (D / 8);
+        u32x4 kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
+        if (k0 + r < N) {
+          kx = *(const u32x4*)(K + (size_t)(k0 + r) * D + 8 * c8);
+          vx = *(const u32x4*)(V + (size_t)(k0 + r) * D + 8 * c8);
+        }
+        kreg[i] = kx;
+        vreg[i] = vx;
+      }
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int idx = tid + i * NT;
+      if (CH % NT == 0 || idx < CH) {
+        const int r = idx / (D / 8), c8 = idx - r * (D / 8);
+        *(u32x4*)(&Ks[buf][r * KS + 8 * c8]) = kreg[i];
+        *(u32x4*)(&Vs[buf][r * VS + 8 * c8]) = vreg[i];
+      }
+    }
+  };
+
+  // Source row/column of this lane for the V^T transpose reads: within each
+  // 16-lane group g, lane 4*i + j addresses key row i (+4*hi), columns
+  // 16*(g&1) + 4*j .. +3 of the 32-column block.
+  const int grp = lane >> 4, gl = lane & 15;
+  const int tr_row = 4 * hi + (gl >> 2);
+  const int tr_col = 16 * (grp & 1) + 4 * (gl & 3);
+
+  gload(0);
   for (int kt = 0; kt < ntiles; ++kt) {
+    const int buf = kt & 1;
     const int k0 = kt * BN;
-    __syncthreads();  // previous tile's LDS reads are done
-
-    // K tile -> LDS, row-major, 16-byte chunks; rows >= N are zero.
-    constexpr int KCH = BN * D / 8;
-#pragma unroll
-    for (int idx = tid; idx < KCH; idx += kThreads) {
-      const int r = idx / (D / 8), c8 = idx - r * (D / 8);
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (k0 + r < N) x = *(const u32x4*)(K + (size_t)(k0 + r) * D + 8 * c8);
-      *(u32x4*)(Ks + r * KS + 8 * c8) = x;
-    }
-    // V tile -> LDS transposed: each thread moves a 4-key x 4-column block.
-    constexpr int VBL = (BN / 4) * (D / 4);
-#pragma unroll
-    for (int idx = tid; idx < VBL; idx += kThreads) {
-      const int dg = idx % (D / 4), kg = idx / (D / 4);
-      u32x2 rw[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = k0 + 4 * kg + r;
-        u32x2 x = {0u, 0u};
-        if (key < N) x = *(const u32x2*)(V + (size_t)key * D + 4 * dg);
-        rw[r] = x;
-      }
-      const int pos = 16 * (kg >> 2) + 4 * vt_group(kg & 3);
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
-        const int w = cc >> 1, sh = (cc & 1) * 16;
-        const uint32_t e0 = (rw[0][w] >> sh) & 0xffffu, e1 = (rw[1][w] >> sh) & 0xffffu;
-        const uint32_t e2 = (rw[2][w] >> sh) & 0xffffu, e3 = (rw[3][w] >> sh) & 0xffffu;
-        u32x2 out = {e0 | (e1 << 16), e2 | (e3 << 16)};
-        *(u32x2*)(Vt + (4 * dg + cc) * VS + pos) = out;
-      }
-    }
+    lstore(buf);
     __syncthreads();
+    if (kt + 1 < ntiles) gload(k0 + BN);
 
-    // S^T = K Q^T for two 32-key blocks.  s[kb][e] is the score of key
-    // k0 + 32*kb + 8*(e/4) + 4*hi + (e%4) against query qrow.
-    f32x16 s[2];
+    // Causal: a tile whose first key is past this wave's last query
+    // contributes nothing.
+    if (CAUSAL && k0 > q0 + WM - 1) continue;
+
+    // S^T = K Q^T for two 32-key blocks.  s[kb][qb][e] is the score of key
+    // k0 + 32*kb + 8*(e/4) + 4*hi + (e%4) against query q0 + 32*qb + l32.
+    f32x16 s[2][QB];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x16{};
 #pragma unroll
       for (int ch = 0; ch < DC; ++ch) {
-        const u32x4 kf = *(const u32x4*)(Ks + (32 * kb + l32) * KS + 16 * ch + 8 * hi);
-        s[kb] = Ops<T>::mma(kf, qf[ch], s[kb]);
+        const u32x4 kf = *(const u32x4*)(&Ks[buf][(32 * kb + l32) * KS + 16 * ch + 8 * hi]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = Ops<T>::mma(kf, qf[ch][qb], s[kb][qb]);
       }
     }
 
     const bool edge = (k0 + BN > N) || (CAUSAL && (k0 + BN - 1 > q0));
-    if (edge) {
+    uint32_t pk[QB][2][8];  // P packed to 16 bits: [qb][kb][pair]
+    uint32_t pl[QB][2][8];  // bf16 low parts (split P)
+    bool any_raise = false;
+    float alpha[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int qrow = q0 + 32 * qb + l32;
+      if (edge) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = k0 + 32 * kb + 8 * (e >> 2) + 4 * hi + (e & 3);
+            if (key >= N || (CAUSAL && key > qrow)) s[kb][qb][e] = -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = k0 + 32 * kb + 8 * (e >> 2) + 4 * hi + (e & 3);
-          if (key >= N || (CAUSAL && key > qrow)) s[kb][e] = -INFINITY;
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][qb][e]);
+      mx = half_max(mx);
+      // Lazy maximum: raise it only when the tile's maximum is more than
+      // kLazy (log2 units) above it.
+      const bool raise = (m_run[qb] == -INFINITY) || ((mx - m_run[qb]) * c > kLazy);
+      const float m_new = raise ? mx : m_run[qb];
+      alpha[qb] = (m_run[qb] == -INFINITY) ? 0.f
+                  : raise ? __builtin_amdgcn_exp2f((m_run[qb] - m_new) * c) : 1.f;
+      any_raise |= raise;
+      m_run[qb] = m_new;
+      const float mc = (m_new == -INFINITY) ? 0.f : m_new * c;
+
+      float psum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float s0 = s[kb][qb][2 * j], s1 = s[kb][qb][2 * j + 1];
+          float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0, c, -mc));
+          float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1, c, -mc));
+          if (edge) {  // masked keys: exactly 0 (also when c == 0)
+            p0 = s0 == -INFINITY ? 0.f : p0;
+            p1 = s1 == -INFINITY ? 0.f : p1;
+          }
+          const uint32_t w = Ops<T>::pack(p0, p1);
+          pk[qb][kb][j] = w;
+          if constexpr (SPLIT_P) {
+            pl[qb][kb][j] = Ops<T>::pack(p0 - Ops<T>::lo_to_f32(w), p1 - Ops<T>::hi_to_f32(w));
+            psum += p0 + p1;
+          } else {
+            psum = Ops<T>::add_pair(w, psum);
+          }
         }
+      l_run[qb] = l_run[qb] * alpha[qb] + psum;
+    }
+    // Rescale O only if some lane of the wave raised its maximum.
+    if (__builtin_amdgcn_ballot_w64(any_raise)) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) oacc[db][qb] *= alpha[qb];
     }
 
-    // Online softmax update (base 2).
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
-    mx = half_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float mc = (m_new == -INFINITY) ? 0.f : m_new * c;
-    const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run * c - mc);
-    m_run = m_new;
-
-    float psum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][e], c, -mc));
-        if (edge && s[kb][e] == -INFINITY) p = 0.f;  // also right when c == 0
-        s[kb][e] = p;
-        psum += p;
-      }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-
-    // O^T += V^T P^T, one 16-key chunk at a time.
+    // O^T += V^T P^T, one 16-key chunk at a time.  Chunk kc holds pairs
+    // 4*(kc&1) .. +3 of key block kc>>1.
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
-      const int kb = kc >> 1, base = 8 * (kc & 1);
-      u32x4 pf, pl;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float p0 = s[kb][base + 2 * j], p1 = s[kb][base + 2 * j + 1];
-        pf[j] = Ops<T>::pack(p0, p1);
-        if (SPLIT_P)
-          pl[j] = Ops<T>::pack(p0 - Ops<T>::lo_to_f32(pf[j]), p1 - Ops<T>::hi_to_f32(pf[j]));
-      }
+      const int kb = kc >> 1, base = 4 * (kc & 1);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const u32x4 vf = *(const u32x4*)(Vt + (32 * db + l32) * VS + 16 * kc + 8 * hi);
-        oacc[db] = Ops<T>::mma(vf, pf, oacc[db]);
-        if (SPLIT_P) oacc[db] = Ops<T>::mma(vf, pl, oacc[db]);
+        const uint16_t* src = &Vs[buf][(16 * kc + tr_row) * VS + 32 * db + tr_col];
+        const u32x2 v0 = tr_read(src);
+        const u32x2 v1 = tr_read(src + 8 * VS);
+        const u32x4 vf = {v0[0], v0[1], v1[0], v1[1]};
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const u32x4 pf = {pk[qb][kb][base], pk[qb][kb][base + 1], pk[qb][kb][base + 2],
+                            pk[qb][kb][base + 3]};
+          oacc[db][qb] = Ops<T>::mma(vf, pf, oacc[db][qb]);
+          if constexpr (SPLIT_P) {
+            const u32x4 pfl = {pl[qb][kb][base], pl[qb][kb][base + 1], pl[qb][kb][base + 2],
+                               pl[qb][kb][base + 3]};
+            oacc[db][qb] = Ops<T>::mma(vf, pfl, oacc[db][qb]);
+          }
+        }
       }
     }
   }
 
   // Epilogue: divide by the row's denominator once, round, store.
-  const float l = half_sum(l_run);
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  if (qrow < N) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+  for (int qb = 0; qb < QB; ++qb) {
+    const float l = half_sum(l_run[qb]);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const int qrow = q0 + 32 * qb + l32;
+    if (qrow < N) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        // elements 4g..4g+3 are columns d0..d0+3 of row qrow
-        const int d0 = 32 * db + 8 * g + 4 * hi;
-        u32x2 out = {Ops<T>::pack(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
-                     Ops<T>::pack(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
-        *(u32x2*)(O + (size_t)qrow * D + d0) = out;
-      }
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          // elements 4g..4g+3 are columns d0..d0+3 of row qrow
+          const int d0 = 32 * db + 8 * g + 4 * hi;
+          const f32x16& acc = oacc[db][qb];
+          u32x2 out = {Ops<T>::pack(acc[4 * g] * inv, acc[4 * g + 1] * inv),
+                       Ops<T>::pack(acc[4 * g + 2] * inv, acc[4 * g + 3] * inv)};
+          *(u32x2*)(O + (size_t)qrow * D + d0) = out;
+        }
+    }
   }
 }
 
-template <typename T, bool SPLIT_P>
-hipError_t launch(const Problem& p, hipStream_t stream) {
+template <typename T, int D, bool CAUSAL, bool SPLIT_P, int WM, int NW>
+hipError_t launch_one(const Args& base, int64_t BH, hipStream_t stream) {
+  using S = Shape<D, WM, NW>;
+  Args a = base;
+  a.num_qtiles = (a.N + S::BM - 1) / S::BM;
+  a.total_tiles = (int)(BH * a.num_qtiles);
+  void* args[] = {&a};
+  return hipLaunchKernel((const void*)fa_forward_kernel<T, D, CAUSAL, SPLIT_P, WM, NW>,
+                         dim3(a.total_tiles), dim3(S::NT), args, 0, stream);
+}
+
+inline Args make_args(const Problem& p) {
   Args a;
   a.q = (const uint16_t*)p.q;
   a.k = (const uint16_t*)p.k;
   a.v = (const uint16_t*)p.v;
   a.o = (uint16_t*)p.o;
   a.N = p.N;
-  a.num_qtiles = (p.N + kBlockM - 1) / kBlockM;
-  a.total_tiles = (int)(p.BH * a.num_qtiles);
+  a.num_qtiles = 0;
+  a.total_tiles = 0;
   a.c = __builtin_fabsf(p.scale) * 1.4426950408889634f;
   a.qxor = p.scale < 0.f ? 0x80008000u : 0u;
-  void (*kern)(Args) = nullptr;
-#define FA_PICK(DD)                                                                   \
-  if (p.D == DD)                                                                      \
-    kern = p.causal ? fa_forward_kernel<T, DD, true, SPLIT_P> : fa_forward_kernel<T, DD, false, SPLIT_P>;
-  FA_PICK(64)
-  FA_PICK(96)
-  FA_PICK(128)
-#undef FA_PICK
-  if (!kern) return hipErrorInvalidValue;
-  void* args[] = {&a};
-  return hipLaunchKernel((const void*)kern, dim3(a.total_tiles), dim3(kThreads), args, 0, stream);
+  return a;
+}
+
+// Tile shape per head dimension: 4 waves of 32 query rows (128 rows per
+// workgroup).
+template <typename T, bool SPLIT_P>
+hipError_t launch(const Problem& p, hipStream_t stream) {
+  const Args a = make_args(p);
+  switch (p.D) {
+    case 64:
+      return p.causal ? launch_one<T, 64, true, SPLIT_P, 32, 4>(a, p.BH, stream)
+                      : launch_one<T, 64, false, SPLIT_P, 32, 4>(a, p.BH, stream);
+    case 96:
+      return p.causal ? launch_one<T, 96, true, SPLIT_P, 32, 4>(a, p.BH, stream)
+                      : launch_one<T, 96, false, SPLIT_P, 32, 4>(a, p.BH, stream);
+    case 128:
+      return p.causal ? launch_one<T, 128, true, SPLIT_P, 32, 4>(a, p.BH, stream)
+                      : launch_one<T, 128, false, SPLIT_P, 32, 4>(a, p.BH, stream);
+    default:
+      return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace mfma
