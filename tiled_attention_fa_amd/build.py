@@ -29,6 +29,9 @@ def hipcc() -> str:
 def common_flags():
     return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # keep MFMA accumulators in VGPRs: the softmax reads every score
+            # with VALU instructions, which cannot take AGPR operands
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             f"-I{INCLUDE}", f"-I{CSRC}"]
 
 

@@ -50,6 +50,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fa_internal.h"
 
 namespace fa {
@@ -165,24 +167,36 @@ struct Shape {
   static constexpr int BM = WM * NW;
   static constexpr int QB = WM / 32;     // 32-query column blocks per wave
   static constexpr int NT = 64 * NW;     // threads per workgroup
-  static constexpr int KS = D + 8;       // K row stride in LDS (elements)
-  static constexpr int VS = D + 16;      // V row stride in LDS (elements)
+  static constexpr int DP = D <= 64 ? 64 : 128;  // LDS row length (elements)
+  static constexpr int CPR = DP / 8;     // 16-byte chunks per LDS row
   static constexpr int DC = D / 16;      // 16-wide contraction chunks of QK^T
   static constexpr int DB = D / 32;      // 32-row blocks of O^T
-  static constexpr int CH = BN * D / 8;  // 16-byte chunks per K (or V) tile
-  static constexpr int CPT = (CH + NT - 1) / NT;  // chunks per thread
-  static constexpr int LDS_BYTES = 2 * BN * (KS + VS) * 2;
+  static constexpr int TILE = BN * DP;   // elements per LDS tile buffer
+  static constexpr int LOADS = BN * CPR / NT;  // 16-byte loads per thread per tile
   static_assert(D % 32 == 0 && D <= 128, "head dim");
   static_assert(WM == 32 || WM == 64, "queries per wave");
+  static_assert((BN * CPR) % NT == 0, "whole wave-loads per tile");
 };
+
+// LDS tile layouts.  A tile row (one key) is DP elements = CPR chunks of 16
+// bytes, rows back to back (the direct global->LDS loads write each wave's
+// 64 x 16 bytes contiguously, so rows cannot be padded).  Chunks are
+// permuted within a row by an XOR with a function of the row:
+//  * K (read by ds_read_b128, 8 consecutive rows per LDS cycle at one
+//    logical chunk): physical chunk = chunk ^ (row & 7).
+//  * V (read by ds_read_b64_tr_b16, 4 consecutive rows x 2 adjacent chunks
+//    per 16-lane group): physical chunk = chunk ^ (2 * (row & 3)).
+// Both spread the lanes served together over all 32 banks.
+__device__ __forceinline__ int k_swz(int row) { return row & 7; }
+__device__ __forceinline__ int v_swz(int row) { return 2 * (row & 3); }
 
 template <typename T, int D, bool CAUSAL, bool SPLIT_P, int WM, int NW>
 __global__ __launch_bounds__(64 * NW) void fa_forward_kernel(Args a) {
   using S = Shape<D, WM, NW>;
-  constexpr int BN = S::BN, BM = S::BM, QB = S::QB, NT = S::NT, KS = S::KS, VS = S::VS;
-  constexpr int DC = S::DC, DB = S::DB, CH = S::CH, CPT = S::CPT;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BN * VS];
+  constexpr int BN = S::BN, BM = S::BM, QB = S::QB, NT = S::NT, DP = S::DP, CPR = S::CPR;
+  constexpr int DC = S::DC, DB = S::DB, TILE = S::TILE, LOADS = S::LOADS;
+  __shared__ __attribute__((aligned(1024))) uint16_t Ks[2][TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t Vs[2][TILE];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -232,79 +246,102 @@ __global__ __launch_bounds__(64 * NW) void fa_forward_kernel(Args a) {
   const int kv_end = CAUSAL ? min(N, qt * BM + BM) : N;
   const int ntiles = (kv_end + BN - 1) / BN;
 
-  // Register staging of one K tile and one V tile (rows >= N read as 0).
-  u32x4 kreg[CPT], vreg[CPT];
-  auto gload = [&](int k0) {
+  // Direct global -> LDS tile loads.  Load i of this thread fills LDS chunk
+  // p = (i * NT + tid) of the tile: row p / CPR, physical chunk p % CPR,
+  // which holds logical chunk (p % CPR) ^ swz(row).  Rows past N repeat row
+  // N-1 (finite data under a zero weight); chunks past D are not loaded.
+  auto tile_load = [&](uint16_t* dst, const uint16_t* __restrict__ src, int t, auto is_v) {
+    constexpr bool IS_V = decltype(is_v)::value;
+    const int k0 = t * BN;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int idx = tid + i * NT;
-      if (CH % NT == 0 || idx < CH) {
-        const int r = idx / (D / 8), c8 = idx - r * (D / 8);
-        u32x4 kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
-        if (k0 + r < N) {
-          kx = *(const u32x4*)(K + (size_t)(k0 + r) * D + 8 * c8);
-          vx = *(const u32x4*)(V + (size_t)(k0 + r) * D + 8 * c8);
-        }
-        kreg[i] = kx;
-        vreg[i] = vx;
-      }
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int idx = tid + i * NT;
-      if (CH % NT == 0 || idx < CH) {
-        const int r = idx / (D / 8), c8 = idx - r * (D / 8);
-        *(u32x4*)(&Ks[buf][r * KS + 8 * c8]) = kreg[i];
-        *(u32x4*)(&Vs[buf][r * VS + 8 * c8]) = vreg[i];
+    for (int i = 0; i < LOADS; ++i) {
+      const int p = i * NT + tid;
+      const int row = p / CPR, pc = p % CPR;
+      const int lc = pc ^ (IS_V ? v_swz(row) : k_swz(row));
+      const int key = min(k0 + row, N - 1);
+      if (DP == D || lc < D / 8) {
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)(src + (size_t)key * D + 8 * lc),
+            (__attribute__((address_space(3))) void*)(dst + (size_t)(i * NT + wave * 64) * 8), 16, 0,
+            0);
       }
     }
   };
 
-  // Source row/column of this lane for the V^T transpose reads: within each
-  // 16-lane group g, lane 4*i + j addresses key row i (+4*hi), columns
-  // 16*(g&1) + 4*j .. +3 of the 32-column block.
-  const int grp = lane >> 4, gl = lane & 15;
-  const int tr_row = 4 * hi + (gl >> 2);
-  const int tr_col = 16 * (grp & 1) + 4 * (gl & 3);
-
-  gload(0);
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int buf = kt & 1;
-    const int k0 = kt * BN;
-    lstore(buf);
-    __syncthreads();
-    if (kt + 1 < ntiles) gload(k0 + BN);
-
-    // Causal: a tile whose first key is past this wave's last query
-    // contributes nothing.
-    if (CAUSAL && k0 > q0 + WM - 1) continue;
-
-    // S^T = K Q^T for two 32-key blocks.  s[kb][qb][e] is the score of key
-    // k0 + 32*kb + 8*(e/4) + 4*hi + (e%4) against query q0 + 32*qb + l32.
-    f32x16 s[2][QB];
+  // S^T = K Q^T for the two 32-key blocks of the tile in K buffer kbuf.
+  // s[kb][qb][e] is the score of key k0 + 32*kb + 8*(e/4) + 4*hi + (e%4)
+  // against query q0 + 32*qb + l32.  The two key blocks form independent
+  // MFMA chains, issued alternately.
+  auto qk = [&](const uint16_t* kt, f32x16 (&s)[2][QB]) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x16{};
 #pragma unroll
-      for (int ch = 0; ch < DC; ++ch) {
-        const u32x4 kf = *(const u32x4*)(&Ks[buf][(32 * kb + l32) * KS + 16 * ch + 8 * hi]);
+    for (int ch = 0; ch < DC; ++ch)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int row = 32 * kb + l32;
+        const int pc = (2 * ch + hi) ^ k_swz(row);
+        const u32x4 kf = *(const u32x4*)(kt + row * DP + 8 * pc);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) s[kb][qb] = Ops<T>::mma(kf, qf[ch][qb], s[kb][qb]);
       }
-    }
+  };
 
-    const bool edge = (k0 + BN > N) || (CAUSAL && (k0 + BN - 1 > q0));
-    uint32_t pk[QB][2][8];  // P packed to 16 bits: [qb][kb][pair]
-    uint32_t pl[QB][2][8];  // bf16 low parts (split P)
-    bool any_raise = false;
-    float alpha[QB];
+  // V^T transpose-read source of this lane: within each 16-lane group g,
+  // lane 4*i + j addresses key row i (+4*hi) and the 8 bytes at columns
+  // 16*(g&1) + 4*j .. +3 of each 32-column block.
+  const int grp = lane >> 4, gl = lane & 15;
+  const int tr_row = 4 * hi + (gl >> 2);  // + 16*kc (+ 8 for the second read)
+  // chunk of column 32*db + 16*(g&1) + 4*j is 4*db + 2*(g&1) + (j>>1); the
+  // row's swizzle depends on row & 3 = gl >> 2 only
+  const int tr_chunk_lo = (2 * (grp & 1) + ((gl & 3) >> 1)) ^ v_swz(tr_row);
+  const int tr_byte = 8 * (gl & 1);
+
+  uint32_t pk[QB][2][8];  // P packed to 16 bits: [qb][kb][pair]
+  uint32_t pl[QB][2][8];  // bf16 low parts (split P)
+  float alpha[QB];
+  bool any_raise;
+
+  // exp2(s*c - m*c) for one query block, packed to 16 bits; returns this
+  // lane's sum of the packed P.  MASK zeroes masked keys (s == -inf) exactly,
+  // also when c == 0.
+  auto exp_pack = [&](auto mask_tag, f32x16 (&s)[2][QB], int qb, float mc) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float s0 = s[kb][qb][2 * j], s1 = s[kb][qb][2 * j + 1];
+        float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0, c, -mc));
+        float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1, c, -mc));
+        if constexpr (MASK) {
+          p0 = s0 == -INFINITY ? 0.f : p0;
+          p1 = s1 == -INFINITY ? 0.f : p1;
+        }
+        const uint32_t w = Ops<T>::pack(p0, p1);
+        pk[qb][kb][j] = w;
+        if constexpr (SPLIT_P) {
+          pl[qb][kb][j] = Ops<T>::pack(p0 - Ops<T>::lo_to_f32(w), p1 - Ops<T>::hi_to_f32(w));
+          psum += p0 + p1;
+        } else {
+          psum = Ops<T>::add_pair(w, psum);
+        }
+      }
+    return psum;
+  };
+
+  // Full online-softmax update of one tile: row maximum, lazy raise of the
+  // running maximum, exp / pack.  EDGE applies the ragged and causal masks.
+  auto softmax_full = [&](auto edge_tag, int t, f32x16 (&s)[2][QB]) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
+    const int k0 = t * BN;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const int qrow = q0 + 32 * qb + l32;
-      if (edge) {
+      if constexpr (EDGE) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -328,48 +365,60 @@ __global__ __launch_bounds__(64 * NW) void fa_forward_kernel(Args a) {
       any_raise |= raise;
       m_run[qb] = m_new;
       const float mc = (m_new == -INFINITY) ? 0.f : m_new * c;
-
-      float psum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float s0 = s[kb][qb][2 * j], s1 = s[kb][qb][2 * j + 1];
-          float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0, c, -mc));
-          float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1, c, -mc));
-          if (edge) {  // masked keys: exactly 0 (also when c == 0)
-            p0 = s0 == -INFINITY ? 0.f : p0;
-            p1 = s1 == -INFINITY ? 0.f : p1;
-          }
-          const uint32_t w = Ops<T>::pack(p0, p1);
-          pk[qb][kb][j] = w;
-          if constexpr (SPLIT_P) {
-            pl[qb][kb][j] = Ops<T>::pack(p0 - Ops<T>::lo_to_f32(w), p1 - Ops<T>::hi_to_f32(w));
-            psum += p0 + p1;
-          } else {
-            psum = Ops<T>::add_pair(w, psum);
-          }
-        }
+      const float psum = exp_pack(edge_tag, s, qb, mc);
       l_run[qb] = l_run[qb] * alpha[qb] + psum;
     }
-    // Rescale O only if some lane of the wave raised its maximum.
+  };
+
+  // One tile's softmax.  Interior tiles first try the running maximum as it
+  // stands (no row maximum needed): if every lane's sum of P stays within
+  // 2^kLazy, no p exceeds 2^kLazy and the running maximum is kept, as the
+  // lazy rule would keep it.  Otherwise (and on the first and edge tiles)
+  // the full update runs.
+  auto softmax = [&](int t, bool edge, bool first, f32x16 (&s)[2][QB]) {
+    any_raise = false;
+    if (edge) {
+      softmax_full(std::true_type{}, t, s);
+      return;
+    }
+    if (!first) {
+      bool over = false;
+      float psum[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        psum[qb] = exp_pack(std::false_type{}, s, qb, m_run[qb] * c);
+        over |= !(psum[qb] <= __builtin_amdgcn_ldexpf(1.f, (int)kLazy));
+      }
+      if (!__builtin_amdgcn_ballot_w64(over)) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          alpha[qb] = 1.f;
+          l_run[qb] += psum[qb];
+        }
+        return;
+      }
+    }
+    softmax_full(std::false_type{}, t, s);
+  };
+
+  // O^T = O^T * alpha + V^T P^T for the tile in V buffer vt.  Chunk kc (16
+  // keys) holds pairs 4*(kc&1) .. +3 of key block kc>>1.
+  auto pv = [&](const uint16_t* vt) {
     if (__builtin_amdgcn_ballot_w64(any_raise)) {
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) oacc[db][qb] *= alpha[qb];
     }
-
-    // O^T += V^T P^T, one 16-key chunk at a time.  Chunk kc holds pairs
-    // 4*(kc&1) .. +3 of key block kc>>1.
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
       const int kb = kc >> 1, base = 4 * (kc & 1);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const uint16_t* src = &Vs[buf][(16 * kc + tr_row) * VS + 32 * db + tr_col];
-        const u32x2 v0 = tr_read(src);
-        const u32x2 v1 = tr_read(src + 8 * VS);
+        // rows 16*kc + tr_row and +8 share the swizzle (row & 3)
+        const uint16_t* src = vt + (16 * kc + tr_row) * DP + 8 * ((4 * db) ^ tr_chunk_lo);
+        const u32x2 v0 = tr_read((const uint16_t*)((const char*)src + tr_byte));
+        const u32x2 v1 = tr_read((const uint16_t*)((const char*)(src + 8 * DP) + tr_byte));
         const u32x4 vf = {v0[0], v0[1], v1[0], v1[1]};
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
@@ -384,6 +433,33 @@ __global__ __launch_bounds__(64 * NW) void fa_forward_kernel(Args a) {
         }
       }
     }
+  };
+
+  // Tile loop, LDS double-buffered: the loads of tile t+1 go out right after
+  // the barrier of tile t, into the buffers tile t-1 used (every wave has
+  // finished with them once it passes that barrier), and are awaited at the
+  // next barrier.
+  tile_load(Ks[0], K, 0, std::false_type{});
+  tile_load(Vs[0], V, 0, std::true_type{});
+  bool first = true;
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    const int k0 = t * BN;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's tile loads have landed
+    __syncthreads();
+    if (t + 1 < ntiles) {
+      tile_load(Ks[buf ^ 1], K, t + 1, std::false_type{});
+      tile_load(Vs[buf ^ 1], V, t + 1, std::true_type{});
+    }
+    // Causal: a tile whose first key is past this wave's last query
+    // contributes nothing.
+    if (CAUSAL && k0 > q0 + WM - 1) continue;
+    f32x16 s[2][QB];
+    qk(Ks[buf], s);
+    const bool edge = (k0 + BN > N) || (CAUSAL && (k0 + BN - 1 > q0));
+    softmax(t, edge, first, s);
+    first = false;
+    pv(Vs[buf]);
   }
 
   // Epilogue: divide by the row's denominator once, round, store.
