@@ -161,10 +161,11 @@ __device__ __forceinline__ u32x2 tr_read(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, r);
 }
 
-template <int D, int WM, int NW>
+template <int D, int WM, int NW, int KSPLIT>
 struct Shape {
   static constexpr int BN = kBlockN;
-  static constexpr int BM = WM * NW;
+  static constexpr int NQW = NW / KSPLIT;  // waves per key group
+  static constexpr int BM = WM * NQW;    // query rows per workgroup
   static constexpr int QB = WM / 32;     // 32-query column blocks per wave
   static constexpr int NT = 64 * NW;     // threads per workgroup
   static constexpr int DP = D <= 64 ? 64 : 128;  // LDS row length (elements)
@@ -172,10 +173,11 @@ struct Shape {
   static constexpr int DC = D / 16;      // 16-wide contraction chunks of QK^T
   static constexpr int DB = D / 32;      // 32-row blocks of O^T
   static constexpr int TILE = BN * DP;   // elements per LDS tile buffer
-  static constexpr int LOADS = BN * CPR / NT;  // 16-byte loads per thread per tile
+  static constexpr int LOADS = KSPLIT * BN * CPR / NT;  // 16-byte loads per thread per step
   static_assert(D % 32 == 0 && D <= 128, "head dim");
   static_assert(WM == 32 || WM == 64, "queries per wave");
-  static_assert((BN * CPR) % NT == 0, "whole wave-loads per tile");
+  static_assert((KSPLIT * BN * CPR) % NT == 0, "whole wave-loads per step");
+  static_assert(KSPLIT == 1 || KSPLIT == 2, "key groups");
 };
 
 // LDS tile layouts.  A tile row (one key) is DP elements = CPR chunks of 16
@@ -190,16 +192,22 @@ struct Shape {
 __device__ __forceinline__ int k_swz(int row) { return row & 7; }
 __device__ __forceinline__ int v_swz(int row) { return 2 * (row & 3); }
 
-template <typename T, int D, bool CAUSAL, bool SPLIT_P, int WM, int NW>
-__global__ __launch_bounds__(64 * NW) void fa_forward_kernel(Args a) {
-  using S = Shape<D, WM, NW>;
+template <typename T, int D, bool CAUSAL, bool SPLIT_P, int WM, int NW, int KSPLIT, int OCC>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC)))
+void fa_forward_kernel(Args a) {
+  using S = Shape<D, WM, NW, KSPLIT>;
   constexpr int BN = S::BN, BM = S::BM, QB = S::QB, NT = S::NT, DP = S::DP, CPR = S::CPR;
-  constexpr int DC = S::DC, DB = S::DB, TILE = S::TILE, LOADS = S::LOADS;
-  __shared__ __attribute__((aligned(1024))) uint16_t Ks[2][TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t Vs[2][TILE];
+  constexpr int DC = S::DC, DB = S::DB, TILE = S::TILE, LOADS = S::LOADS, NQW = S::NQW;
+  // K tiles [buffer][key group], then V tiles [buffer][key group]
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * 2 * KSPLIT * TILE];
+  auto kbuf = [&](int buf, int g) { return lds + (buf * KSPLIT + g) * TILE; };
+  auto vbuf = [&](int buf, int g) { return lds + ((2 + buf) * KSPLIT + g) * TILE; };
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  // wave-uniform, so everything derived from it lives in SGPRs
+  const int wave_id = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kgrp = wave_id / NQW;  // key group: tiles t with t % KSPLIT == kgrp
+  const int wave = wave_id - kgrp * NQW;  // query slot within the workgroup
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
@@ -246,26 +254,46 @@ __global__ __launch_bounds__(64 * NW) void fa_forward_kernel(Args a) {
   const int kv_end = CAUSAL ? min(N, qt * BM + BM) : N;
   const int ntiles = (kv_end + BN - 1) / BN;
 
-  // Direct global -> LDS tile loads.  Load i of this thread fills LDS chunk
-  // p = (i * NT + tid) of the tile: row p / CPR, physical chunk p % CPR,
-  // which holds logical chunk (p % CPR) ^ swz(row).  Rows past N repeat row
-  // N-1 (finite data under a zero weight); chunks past D are not loaded.
-  auto tile_load = [&](uint16_t* dst, const uint16_t* __restrict__ src, int t, auto is_v) {
+  // Direct global -> LDS loads of one step: tiles KSPLIT*st .. +KSPLIT-1
+  // into dst[0 .. KSPLIT-1], through a buffer resource whose range starts at
+  // the step's first key and ends at key N, so rows past N read as zero
+  // (the hardware range check).  Load i of this thread fills chunk
+  // p = (i * NT + tid) of the step's area: tile p / (BN*CPR), row
+  // (p / CPR) % BN, physical chunk p % CPR, which holds logical chunk
+  // (p % CPR) ^ swz(row).  Chunks past D (D = 96) are not loaded.
+  uint32_t koff[LOADS], voff[LOADS];
+  bool lpred[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int p = i * NT + tid;
+    const int tl = p / (BN * CPR);
+    const int row = (p / CPR) % BN, pc = p % CPR;
+    koff[i] = ((tl * BN + row) * D + 8 * (pc ^ k_swz(row))) * 2;
+    voff[i] = ((tl * BN + row) * D + 8 * (pc ^ v_swz(row))) * 2;
+    lpred[i] = DP == D || (pc ^ k_swz(row)) < D / 8;
+  }
+  // (the V swizzle moves chunks differently, so its predicate is separate)
+  bool vpred[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int p = i * NT + tid;
+    const int row = (p / CPR) % BN, pc = p % CPR;
+    vpred[i] = DP == D || (pc ^ v_swz(row)) < D / 8;
+  }
+  auto step_load = [&](uint16_t* dst, const uint16_t* __restrict__ src, int st, auto is_v) {
     constexpr bool IS_V = decltype(is_v)::value;
-    const int k0 = t * BN;
+#if defined(__HIP_DEVICE_COMPILE__)  // buffer resources exist in device code only
+    const int k0 = KSPLIT * st * BN;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(src + (size_t)k0 * D), 0, (N - k0) * D * 2, 0x00020000);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      const int p = i * NT + tid;
-      const int row = p / CPR, pc = p % CPR;
-      const int lc = pc ^ (IS_V ? v_swz(row) : k_swz(row));
-      const int key = min(k0 + row, N - 1);
-      if (DP == D || lc < D / 8) {
-        __builtin_amdgcn_global_load_lds(
-            (const __attribute__((address_space(1))) void*)(src + (size_t)key * D + 8 * lc),
-            (__attribute__((address_space(3))) void*)(dst + (size_t)(i * NT + wave * 64) * 8), 16, 0,
-            0);
-      }
+      if (IS_V ? vpred[i] : lpred[i])
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (__attribute__((address_space(3))) void*)(dst + (size_t)(i * NT + wave_id * 64) * 8),
+            16, IS_V ? voff[i] : koff[i], 0, 0, 0);
     }
+#endif
   };
 
   // S^T = K Q^T for the two 32-key blocks of the tile in K buffer kbuf.
@@ -435,31 +463,76 @@ __global__ __launch_bounds__(64 * NW) void fa_forward_kernel(Args a) {
     }
   };
 
-  // Tile loop, LDS double-buffered: the loads of tile t+1 go out right after
-  // the barrier of tile t, into the buffers tile t-1 used (every wave has
-  // finished with them once it passes that barrier), and are awaited at the
-  // next barrier.
-  tile_load(Ks[0], K, 0, std::false_type{});
-  tile_load(Vs[0], V, 0, std::true_type{});
+  // Step loop, LDS double-buffered.  Step st holds tiles KSPLIT*st ..
+  // KSPLIT*st + KSPLIT-1; key group g works on tile KSPLIT*st + g (the
+  // groups split the keys of every query row between them).  The loads of
+  // step st+1 go out right after the barrier of step st, into the buffers
+  // step st-1 used (every wave has finished with them once it passes that
+  // barrier), and are awaited at the next barrier.
+  const int nsteps = (ntiles + KSPLIT - 1) / KSPLIT;
+  step_load(kbuf(0, 0), K, 0, std::false_type{});
+  step_load(vbuf(0, 0), V, 0, std::true_type{});
   bool first = true;
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    const int k0 = t * BN;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's tile loads have landed
+  for (int st = 0; st < nsteps; ++st) {
+    const int buf = st & 1;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's loads have landed
     __syncthreads();
-    if (t + 1 < ntiles) {
-      tile_load(Ks[buf ^ 1], K, t + 1, std::false_type{});
-      tile_load(Vs[buf ^ 1], V, t + 1, std::true_type{});
+    if (st + 1 < nsteps) {
+      step_load(kbuf(buf ^ 1, 0), K, st + 1, std::false_type{});
+      step_load(vbuf(buf ^ 1, 0), V, st + 1, std::true_type{});
     }
+    const int t = KSPLIT * st + kgrp;
+    const int k0 = t * BN;
     // Causal: a tile whose first key is past this wave's last query
     // contributes nothing.
-    if (CAUSAL && k0 > q0 + WM - 1) continue;
+    if (t >= ntiles || (CAUSAL && k0 > q0 + WM - 1)) continue;
     f32x16 s[2][QB];
-    qk(Ks[buf], s);
+    qk(kbuf(buf, kgrp), s);
     const bool edge = (k0 + BN > N) || (CAUSAL && (k0 + BN - 1 > q0));
     softmax(t, edge, first, s);
     first = false;
-    pv(Vs[buf]);
+    pv(vbuf(buf, kgrp));
+  }
+
+  if constexpr (KSPLIT == 2) {
+    // Merge the two key groups.  Each holds, per query, a running maximum
+    // m_g, a share l_g of the denominator and an accumulator O_g, all
+    // relative to exp(m_g); with m = max(m_0, m_1) the union of their keys
+    // gives l = sum_g l_g exp(m_g - m) and O = sum_g O_g exp(m_g - m), the
+    // same rescale rule as the online softmax.  Group 1 hands its state to
+    // group 0 through LDS (the tile buffers are free after the barrier).
+    constexpr int PER_LANE = DB * QB * 16 + 2 * QB;  // floats per lane
+    static_assert(NQW * 64 * PER_LANE * 4 <= (int)sizeof(lds), "merge area");
+    float* xch = (float*)lds + (size_t)(wave * 64 + lane) * PER_LANE;
+    __syncthreads();
+    if (kgrp == 1) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) xch[(qb * DB + db) * 16 + e] = oacc[db][qb][e];
+        xch[DB * QB * 16 + 2 * qb] = m_run[qb];
+        xch[DB * QB * 16 + 2 * qb + 1] = l_run[qb];
+      }
+    }
+    __syncthreads();
+    if (kgrp == 1) return;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float m1 = xch[DB * QB * 16 + 2 * qb];
+      const float l1 = xch[DB * QB * 16 + 2 * qb + 1];
+      const float m0 = m_run[qb];
+      const float m = fmaxf(m0, m1);
+      const float a0 = m0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m0 - m) * c);
+      const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m1 - m) * c);
+      l_run[qb] = l_run[qb] * a0 + l1 * a1;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          oacc[db][qb][e] = oacc[db][qb][e] * a0 + xch[(qb * DB + db) * 16 + e] * a1;
+    }
   }
 
   // Epilogue: divide by the row's denominator once, round, store.
@@ -484,14 +557,14 @@ __global__ __launch_bounds__(64 * NW) void fa_forward_kernel(Args a) {
   }
 }
 
-template <typename T, int D, bool CAUSAL, bool SPLIT_P, int WM, int NW>
+template <typename T, int D, bool CAUSAL, bool SPLIT_P, int WM, int NW, int KSPLIT, int OCC>
 hipError_t launch_one(const Args& base, int64_t BH, hipStream_t stream) {
-  using S = Shape<D, WM, NW>;
+  using S = Shape<D, WM, NW, KSPLIT>;
   Args a = base;
   a.num_qtiles = (a.N + S::BM - 1) / S::BM;
   a.total_tiles = (int)(BH * a.num_qtiles);
   void* args[] = {&a};
-  return hipLaunchKernel((const void*)fa_forward_kernel<T, D, CAUSAL, SPLIT_P, WM, NW>,
+  return hipLaunchKernel((const void*)fa_forward_kernel<T, D, CAUSAL, SPLIT_P, WM, NW, KSPLIT, OCC>,
                          dim3(a.total_tiles), dim3(S::NT), args, 0, stream);
 }
 
@@ -516,14 +589,14 @@ hipError_t launch(const Problem& p, hipStream_t stream) {
   const Args a = make_args(p);
   switch (p.D) {
     case 64:
-      return p.causal ? launch_one<T, 64, true, SPLIT_P, 32, 4>(a, p.BH, stream)
-                      : launch_one<T, 64, false, SPLIT_P, 32, 4>(a, p.BH, stream);
+      return p.causal ? launch_one<T, 64, true, SPLIT_P, 32, 8, 2, 4>(a, p.BH, stream)
+                      : launch_one<T, 64, false, SPLIT_P, 32, 8, 2, 4>(a, p.BH, stream);
     case 96:
-      return p.causal ? launch_one<T, 96, true, SPLIT_P, 32, 4>(a, p.BH, stream)
-                      : launch_one<T, 96, false, SPLIT_P, 32, 4>(a, p.BH, stream);
+      return p.causal ? launch_one<T, 96, true, SPLIT_P, 32, 4, 1, 2>(a, p.BH, stream)
+                      : launch_one<T, 96, false, SPLIT_P, 32, 4, 1, 2>(a, p.BH, stream);
     case 128:
-      return p.causal ? launch_one<T, 128, true, SPLIT_P, 32, 4>(a, p.BH, stream)
-                      : launch_one<T, 128, false, SPLIT_P, 32, 4>(a, p.BH, stream);
+      return p.causal ? launch_one<T, 128, true, SPLIT_P, 32, 4, 1, 2>(a, p.BH, stream)
+                      : launch_one<T, 128, false, SPLIT_P, 32, 4, 1, 2>(a, p.BH, stream);
     default:
       return hipErrorInvalidValue;
   }
