@@ -161,23 +161,20 @@ __device__ __forceinline__ u32x2 tr_read(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, r);
 }
 
-template <int D, int WM, int NW, int KSPLIT>
+template <int D, int NW>
 struct Shape {
-  static constexpr int BN = kBlockN;
-  static constexpr int NQW = NW / KSPLIT;  // waves per key group
-  static constexpr int BM = WM * NQW;    // query rows per workgroup
-  static constexpr int QB = WM / 32;     // 32-query column blocks per wave
+  static constexpr int BN = kBlockN;     // keys per tile
+  static constexpr int BM = 32 * NW;     // query rows per workgroup, 32 per wave
   static constexpr int NT = 64 * NW;     // threads per workgroup
   static constexpr int DP = D <= 64 ? 64 : 128;  // LDS row length (elements)
   static constexpr int CPR = DP / 8;     // 16-byte chunks per LDS row
   static constexpr int DC = D / 16;      // 16-wide contraction chunks of QK^T
   static constexpr int DB = D / 32;      // 32-row blocks of O^T
   static constexpr int TILE = BN * DP;   // elements per LDS tile buffer
-  static constexpr int LOADS = KSPLIT * BN * CPR / NT;  // 16-byte loads per thread per step
+  static constexpr int NBUF = 3;         // LDS buffers per operand
+  static constexpr int LOADS = BN * CPR / NT;  // 16-byte loads per thread per tile
   static_assert(D % 32 == 0 && D <= 128, "head dim");
-  static_assert(WM == 32 || WM == 64, "queries per wave");
-  static_assert((KSPLIT * BN * CPR) % NT == 0, "whole wave-loads per step");
-  static_assert(KSPLIT == 1 || KSPLIT == 2, "key groups");
+  static_assert((BN * CPR) % NT == 0, "whole wave-loads per tile");
 };
 
 // LDS tile layouts.  A tile row (one key) is DP elements = CPR chunks of 16
@@ -192,22 +189,20 @@ struct Shape {
 __device__ __forceinline__ int k_swz(int row) { return row & 7; }
 __device__ __forceinline__ int v_swz(int row) { return 2 * (row & 3); }
 
-template <typename T, int D, bool CAUSAL, bool SPLIT_P, int WM, int NW, int KSPLIT, int OCC>
+template <typename T, int D, bool CAUSAL, bool SPLIT_P, int NW, int OCC>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC)))
 void fa_forward_kernel(Args a) {
-  using S = Shape<D, WM, NW, KSPLIT>;
-  constexpr int BN = S::BN, BM = S::BM, QB = S::QB, NT = S::NT, DP = S::DP, CPR = S::CPR;
-  constexpr int DC = S::DC, DB = S::DB, TILE = S::TILE, LOADS = S::LOADS, NQW = S::NQW;
-  // K tiles [buffer][key group], then V tiles [buffer][key group]
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * 2 * KSPLIT * TILE];
-  auto kbuf = [&](int buf, int g) { return lds + (buf * KSPLIT + g) * TILE; };
-  auto vbuf = [&](int buf, int g) { return lds + ((2 + buf) * KSPLIT + g) * TILE; };
+  using S = Shape<D, NW>;
+  constexpr int BN = S::BN, BM = S::BM, NT = S::NT, DP = S::DP, CPR = S::CPR;
+  constexpr int DC = S::DC, DB = S::DB, TILE = S::TILE, NBUF = S::NBUF, LOADS = S::LOADS;
+  // K tiles [buffer], then V tiles [buffer]
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * NBUF * TILE];
+  auto kbuf = [&](int b) { return lds + b * TILE; };
+  auto vbuf = [&](int b) { return lds + (NBUF + b) * TILE; };
 
   const int tid = threadIdx.x;
   // wave-uniform, so everything derived from it lives in SGPRs
-  const int wave_id = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kgrp = wave_id / NQW;  // key group: tiles t with t % KSPLIT == kgrp
-  const int wave = wave_id - kgrp * NQW;  // query slot within the workgroup
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
@@ -224,87 +219,71 @@ void fa_forward_kernel(Args a) {
   uint16_t* __restrict__ O = a.o + head;
   const float c = a.c;
 
-  const int q0 = qt * BM + wave * WM;  // first query row of this wave
+  const int q0 = qt * BM + wave * 32;  // first query row of this wave
+  const int qrow = q0 + l32;           // this lane's query row
 
-  // Q fragments: query q0 + 32*qb + l32, columns 16*ch + 8*hi .. +7.
-  u32x4 qf[DC][QB];
+  // Q fragment: row qrow, columns 16*ch + 8*hi .. +7 (B operand layout).
+  u32x4 qf[DC];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qrow = q0 + 32 * qb + l32;
-#pragma unroll
-    for (int ch = 0; ch < DC; ++ch) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (qrow < N) x = *(const u32x4*)(Q + (size_t)qrow * D + 16 * ch + 8 * hi);
-      qf[ch][qb] = x ^ a.qxor;
-    }
+  for (int ch = 0; ch < DC; ++ch) {
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (qrow < N) x = *(const u32x4*)(Q + (size_t)qrow * D + 16 * ch + 8 * hi);
+    qf[ch] = x ^ a.qxor;
   }
 
-  f32x16 oacc[DB][QB];
+  f32x16 oacc[DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = f32x16{};
-  float m_run[QB], l_run[QB];  // running max of raw scores; this lane's share of l
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m_run[qb] = -INFINITY;
-    l_run[qb] = 0.f;
-  }
+  for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+  float m_run = -INFINITY;  // running (lazy) max of raw scores q.k
+  float l_run = 0.f;        // this lane's share of the running denominator
 
   const int kv_end = CAUSAL ? min(N, qt * BM + BM) : N;
   const int ntiles = (kv_end + BN - 1) / BN;
 
-  // Direct global -> LDS loads of one step: tiles KSPLIT*st .. +KSPLIT-1
-  // into dst[0 .. KSPLIT-1], through a buffer resource whose range starts at
-  // the step's first key and ends at key N, so rows past N read as zero
-  // (the hardware range check).  Load i of this thread fills chunk
-  // p = (i * NT + tid) of the step's area: tile p / (BN*CPR), row
-  // (p / CPR) % BN, physical chunk p % CPR, which holds logical chunk
-  // (p % CPR) ^ swz(row).  Chunks past D (D = 96) are not loaded.
+  // Direct global -> LDS loads of tile t, through a buffer resource whose
+  // range starts at the tile's first key and ends at key N, so rows past N
+  // read as zero (the hardware range check).  Load i of this thread fills
+  // chunk p = i * NT + tid of the tile: row p / CPR, physical chunk p % CPR,
+  // which holds logical chunk (p % CPR) ^ swz(row).  Chunks past D (D = 96)
+  // are not loaded.
   uint32_t koff[LOADS], voff[LOADS];
-  bool lpred[LOADS];
+  bool kpred[LOADS], vpred[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     const int p = i * NT + tid;
-    const int tl = p / (BN * CPR);
-    const int row = (p / CPR) % BN, pc = p % CPR;
-    koff[i] = ((tl * BN + row) * D + 8 * (pc ^ k_swz(row))) * 2;
-    voff[i] = ((tl * BN + row) * D + 8 * (pc ^ v_swz(row))) * 2;
-    lpred[i] = DP == D || (pc ^ k_swz(row)) < D / 8;
-  }
-  // (the V swizzle moves chunks differently, so its predicate is separate)
-  bool vpred[LOADS];
-#pragma unroll
-  for (int i = 0; i < LOADS; ++i) {
-    const int p = i * NT + tid;
-    const int row = (p / CPR) % BN, pc = p % CPR;
+    const int row = p / CPR, pc = p % CPR;
+    koff[i] = (row * D + 8 * (pc ^ k_swz(row))) * 2;
+    voff[i] = (row * D + 8 * (pc ^ v_swz(row))) * 2;
+    kpred[i] = DP == D || (pc ^ k_swz(row)) < D / 8;
     vpred[i] = DP == D || (pc ^ v_swz(row)) < D / 8;
   }
-  auto step_load = [&](uint16_t* dst, const uint16_t* __restrict__ src, int st, auto is_v) {
-    constexpr bool IS_V = decltype(is_v)::value;
+  auto tile_load = [&](int b, int t) {
 #if defined(__HIP_DEVICE_COMPILE__)  // buffer resources exist in device code only
-    const int k0 = KSPLIT * st * BN;
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(src + (size_t)k0 * D), 0, (N - k0) * D * 2, 0x00020000);
+    const int k0 = t * BN;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(K + (size_t)k0 * D), 0, (N - k0) * D * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(V + (size_t)k0 * D), 0, (N - k0) * D * 2, 0x00020000);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      if (IS_V ? vpred[i] : lpred[i])
+      const size_t at = (size_t)(i * NT + wave * 64) * 8;
+      if (kpred[i])
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs, (__attribute__((address_space(3))) void*)(dst + (size_t)(i * NT + wave_id * 64) * 8),
-            16, IS_V ? voff[i] : koff[i], 0, 0, 0);
+            rk, (__attribute__((address_space(3))) void*)(kbuf(b) + at), 16, koff[i], 0, 0, 0);
+      if (vpred[i])
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rv, (__attribute__((address_space(3))) void*)(vbuf(b) + at), 16, voff[i], 0, 0, 0);
     }
 #endif
   };
 
-  // S^T = K Q^T for the two 32-key blocks of the tile in K buffer kbuf.
-  // s[kb][qb][e] is the score of key k0 + 32*kb + 8*(e/4) + 4*hi + (e%4)
-  // against query q0 + 32*qb + l32.  The two key blocks form independent
-  // MFMA chains, issued alternately.
-  auto qk = [&](const uint16_t* kt, f32x16 (&s)[2][QB]) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x16{};
+  // S^T = K Q^T for the two 32-key blocks of the tile at kt.  s[kb][e] is
+  // the score of key k0 + 32*kb + 8*(e/4) + 4*hi + (e%4) against query
+  // qrow.  The two key blocks form independent MFMA chains, issued
+  // alternately.
+  auto qk = [&](const uint16_t* kt, f32x16 (&s)[2]) {
+    s[0] = f32x16{};
+    s[1] = f32x16{};
 #pragma unroll
     for (int ch = 0; ch < DC; ++ch)
 #pragma unroll
@@ -312,8 +291,7 @@ void fa_forward_kernel(Args a) {
         const int row = 32 * kb + l32;
         const int pc = (2 * ch + hi) ^ k_swz(row);
         const u32x4 kf = *(const u32x4*)(kt + row * DP + 8 * pc);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = Ops<T>::mma(kf, qf[ch][qb], s[kb][qb]);
+        s[kb] = Ops<T>::mma(kf, qf[ch], s[kb]);
       }
   };
 
@@ -327,120 +305,73 @@ void fa_forward_kernel(Args a) {
   const int tr_chunk_lo = (2 * (grp & 1) + ((gl & 3) >> 1)) ^ v_swz(tr_row);
   const int tr_byte = 8 * (gl & 1);
 
-  uint32_t pk[QB][2][8];  // P packed to 16 bits: [qb][kb][pair]
-  uint32_t pl[QB][2][8];  // bf16 low parts (split P)
-  float alpha[QB];
-  bool any_raise;
+  auto live = [&](int t) {  // tile t exists and holds keys this wave sees
+    return t < ntiles && (!CAUSAL || t * BN <= q0 + 31);
+  };
+  auto is_edge = [&](int t) {  // tile t needs the ragged / causal masks
+    return (t * BN + BN > N) || (CAUSAL && (t * BN + BN - 1 > q0));
+  };
 
-  // exp2(s*c - m*c) for one query block, packed to 16 bits; returns this
-  // lane's sum of the packed P.  MASK zeroes masked keys (s == -inf) exactly,
-  // also when c == 0.
-  auto exp_pack = [&](auto mask_tag, f32x16 (&s)[2][QB], int qb, float mc) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    float psum = 0.f;
+  // The work of one tile: the row maximum and the lazy-max update, the
+  // rescale of O (only when some lane raised its maximum), then one basic
+  // block without branches: the exponents (FMA) among the MFMAs of the next
+  // tile's scores, the exponentials, and P V of this tile among the
+  // conversions of P to 16 bits and the row sums.  The
+  // next tile's scores are computed even when that tile is not used (past
+  // the end, or causally masked for this wave): one wasted tile per wave
+  // keeps the block free of branches.  Masked scores are -inf and c > 0, so
+  // their p is exactly 0.
+  auto tile_body = [&](const uint16_t* kt_next, const uint16_t* vt, f32x16 (&sc)[2],
+                       f32x16 (&sn)[2]) {
+    float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float s0 = s[kb][qb][2 * j], s1 = s[kb][qb][2 * j + 1];
-        float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0, c, -mc));
-        float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1, c, -mc));
-        if constexpr (MASK) {
-          p0 = s0 == -INFINITY ? 0.f : p0;
-          p1 = s1 == -INFINITY ? 0.f : p1;
-        }
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[kb][e]);
+    mx = half_max(mx);
+    // Lazy maximum: raise it only when the tile's maximum is more than
+    // kLazy (log2 units) above it; otherwise p may reach 2^kLazy.
+    const bool fresh = m_run == -INFINITY;
+    const bool raise = fresh || ((mx - m_run) * c > kLazy);
+    const float m_new = raise ? mx : m_run;
+    const float alpha = fresh ? 0.f : __builtin_amdgcn_exp2f((m_run - m_new) * c);
+    m_run = m_new;
+    const float mc = m_new == -INFINITY ? 0.f : m_new * c;
+    if (__builtin_amdgcn_ballot_w64(raise && !fresh)) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+    }
+    float x[2][16];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) x[kb][e] = __builtin_fmaf(sc[kb][e], c, -mc);
+    qk(kt_next, sn);
+    float p[2][16];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) p[kb][e] = __builtin_amdgcn_exp2f(x[kb][e]);
+    float psum = 0.f;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      // chunk kc (16 keys) = pairs 4*(kc&1) .. +3 of key block kc>>1
+      const int kb = kc >> 1, base = 8 * (kc & 1);
+      u32x4 pf, pfl;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float p0 = p[kb][base + 2 * j], p1 = p[kb][base + 2 * j + 1];
         const uint32_t w = Ops<T>::pack(p0, p1);
-        pk[qb][kb][j] = w;
+        pf[j] = w;
         if constexpr (SPLIT_P) {
-          pl[qb][kb][j] = Ops<T>::pack(p0 - Ops<T>::lo_to_f32(w), p1 - Ops<T>::hi_to_f32(w));
+          pfl[j] = Ops<T>::pack(p0 - Ops<T>::lo_to_f32(w), p1 - Ops<T>::hi_to_f32(w));
           psum += p0 + p1;
         } else {
+          // the sum of the rounded P, so that the weights applied to V sum
+          // to one (this matters when a few keys dominate a row)
           psum = Ops<T>::add_pair(w, psum);
         }
       }
-    return psum;
-  };
-
-  // Full online-softmax update of one tile: row maximum, lazy raise of the
-  // running maximum, exp / pack.  EDGE applies the ragged and causal masks.
-  auto softmax_full = [&](auto edge_tag, int t, f32x16 (&s)[2][QB]) {
-    constexpr bool EDGE = decltype(edge_tag)::value;
-    const int k0 = t * BN;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const int qrow = q0 + 32 * qb + l32;
-      if constexpr (EDGE) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int key = k0 + 32 * kb + 8 * (e >> 2) + 4 * hi + (e & 3);
-            if (key >= N || (CAUSAL && key > qrow)) s[kb][qb][e] = -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][qb][e]);
-      mx = half_max(mx);
-      // Lazy maximum: raise it only when the tile's maximum is more than
-      // kLazy (log2 units) above it.
-      const bool raise = (m_run[qb] == -INFINITY) || ((mx - m_run[qb]) * c > kLazy);
-      const float m_new = raise ? mx : m_run[qb];
-      alpha[qb] = (m_run[qb] == -INFINITY) ? 0.f
-                  : raise ? __builtin_amdgcn_exp2f((m_run[qb] - m_new) * c) : 1.f;
-      any_raise |= raise;
-      m_run[qb] = m_new;
-      const float mc = (m_new == -INFINITY) ? 0.f : m_new * c;
-      const float psum = exp_pack(edge_tag, s, qb, mc);
-      l_run[qb] = l_run[qb] * alpha[qb] + psum;
-    }
-  };
-
-  // One tile's softmax.  Interior tiles first try the running maximum as it
-  // stands (no row maximum needed): if every lane's sum of P stays within
-  // 2^kLazy, no p exceeds 2^kLazy and the running maximum is kept, as the
-  // lazy rule would keep it.  Otherwise (and on the first and edge tiles)
-  // the full update runs.
-  auto softmax = [&](int t, bool edge, bool first, f32x16 (&s)[2][QB]) {
-    any_raise = false;
-    if (edge) {
-      softmax_full(std::true_type{}, t, s);
-      return;
-    }
-    if (!first) {
-      bool over = false;
-      float psum[QB];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        psum[qb] = exp_pack(std::false_type{}, s, qb, m_run[qb] * c);
-        over |= !(psum[qb] <= __builtin_amdgcn_ldexpf(1.f, (int)kLazy));
-      }
-      if (!__builtin_amdgcn_ballot_w64(over)) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          alpha[qb] = 1.f;
-          l_run[qb] += psum[qb];
-        }
-        return;
-      }
-    }
-    softmax_full(std::false_type{}, t, s);
-  };
-
-  // O^T = O^T * alpha + V^T P^T for the tile in V buffer vt.  Chunk kc (16
-  // keys) holds pairs 4*(kc&1) .. +3 of key block kc>>1.
-  auto pv = [&](const uint16_t* vt) {
-    if (__builtin_amdgcn_ballot_w64(any_raise)) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) oacc[db][qb] *= alpha[qb];
-    }
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      const int kb = kc >> 1, base = 4 * (kc & 1);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         // rows 16*kc + tr_row and +8 share the swizzle (row & 3)
@@ -448,123 +379,82 @@ void fa_forward_kernel(Args a) {
         const u32x2 v0 = tr_read((const uint16_t*)((const char*)src + tr_byte));
         const u32x2 v1 = tr_read((const uint16_t*)((const char*)(src + 8 * DP) + tr_byte));
         const u32x4 vf = {v0[0], v0[1], v1[0], v1[1]};
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const u32x4 pf = {pk[qb][kb][base], pk[qb][kb][base + 1], pk[qb][kb][base + 2],
-                            pk[qb][kb][base + 3]};
-          oacc[db][qb] = Ops<T>::mma(vf, pf, oacc[db][qb]);
-          if constexpr (SPLIT_P) {
-            const u32x4 pfl = {pl[qb][kb][base], pl[qb][kb][base + 1], pl[qb][kb][base + 2],
-                               pl[qb][kb][base + 3]};
-            oacc[db][qb] = Ops<T>::mma(vf, pfl, oacc[db][qb]);
-          }
-        }
+        oacc[db] = Ops<T>::mma(vf, pf, oacc[db]);
+        if constexpr (SPLIT_P) oacc[db] = Ops<T>::mma(vf, pfl, oacc[db]);
       }
     }
+    l_run = l_run * alpha + psum;
   };
 
-  // Step loop, LDS double-buffered.  Step st holds tiles KSPLIT*st ..
-  // KSPLIT*st + KSPLIT-1; key group g works on tile KSPLIT*st + g (the
-  // groups split the keys of every query row between them).  The loads of
-  // step st+1 go out right after the barrier of step st, into the buffers
-  // step st-1 used (every wave has finished with them once it passes that
-  // barrier), and are awaited at the next barrier.
-  const int nsteps = (ntiles + KSPLIT - 1) / KSPLIT;
-  step_load(kbuf(0, 0), K, 0, std::false_type{});
-  step_load(vbuf(0, 0), V, 0, std::true_type{});
-  bool first = true;
-  for (int st = 0; st < nsteps; ++st) {
-    const int buf = st & 1;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's loads have landed
-    __syncthreads();
-    if (st + 1 < nsteps) {
-      step_load(kbuf(buf ^ 1, 0), K, st + 1, std::false_type{});
-      step_load(vbuf(buf ^ 1, 0), V, st + 1, std::true_type{});
+  // Software pipeline over NBUF = 3 LDS buffers per operand (tile t in
+  // buffer t % 3).  Step t: pass the barrier (tile t+1, whose loads went
+  // out in step t-1, is then visible, and every wave is done with step
+  // t-1 and so with buffer (t+2) % 3); issue the loads of tile t+2 into
+  // that buffer; then the tile body: softmax of tile t, whose scores were
+  // computed in step t-1, while the scores of tile t+1 are computed, and
+  // P V of tile t.
+  tile_load(0, 0);
+  if (ntiles > 1) tile_load(1, 1);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+  f32x16 sA[2], sB[2];
+  qk(kbuf(0), sA);  // tile 0 holds key 0, which every query sees
+  int b0 = 0;       // buffer of tile t
+  auto step = [&](int t, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+    const int b1 = b0 == NBUF - 1 ? 0 : b0 + 1;
+    const int b2 = b1 == NBUF - 1 ? 0 : b1 + 1;
+    if (t > 0) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile t+1 has landed
+      __syncthreads();
     }
-    const int t = KSPLIT * st + kgrp;
-    const int k0 = t * BN;
-    // Causal: a tile whose first key is past this wave's last query
-    // contributes nothing.
-    if (t >= ntiles || (CAUSAL && k0 > q0 + WM - 1)) continue;
-    f32x16 s[2][QB];
-    qk(kbuf(buf, kgrp), s);
-    const bool edge = (k0 + BN > N) || (CAUSAL && (k0 + BN - 1 > q0));
-    softmax(t, edge, first, s);
-    first = false;
-    pv(vbuf(buf, kgrp));
-  }
-
-  if constexpr (KSPLIT == 2) {
-    // Merge the two key groups.  Each holds, per query, a running maximum
-    // m_g, a share l_g of the denominator and an accumulator O_g, all
-    // relative to exp(m_g); with m = max(m_0, m_1) the union of their keys
-    // gives l = sum_g l_g exp(m_g - m) and O = sum_g O_g exp(m_g - m), the
-    // same rescale rule as the online softmax.  Group 1 hands its state to
-    // group 0 through LDS (the tile buffers are free after the barrier).
-    constexpr int PER_LANE = DB * QB * 16 + 2 * QB;  // floats per lane
-    static_assert(NQW * 64 * PER_LANE * 4 <= (int)sizeof(lds), "merge area");
-    float* xch = (float*)lds + (size_t)(wave * 64 + lane) * PER_LANE;
-    __syncthreads();
-    if (kgrp == 1) {
+    if (t + 2 < ntiles) tile_load(b2, t + 2);
+    if (live(t)) {
+      if (is_edge(t)) {  // ragged / causal masks
+        const int k0 = t * BN;
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) xch[(qb * DB + db) * 16 + e] = oacc[db][qb][e];
-        xch[DB * QB * 16 + 2 * qb] = m_run[qb];
-        xch[DB * QB * 16 + 2 * qb + 1] = l_run[qb];
+          for (int e = 0; e < 16; ++e) {
+            const int key = k0 + 32 * kb + 8 * (e >> 2) + 4 * hi + (e & 3);
+            if (key >= N || (CAUSAL && key > qrow)) sc[kb][e] = -INFINITY;
+          }
       }
+      tile_body(kbuf(b1), vbuf(b0), sc, sn);
     }
-    __syncthreads();
-    if (kgrp == 1) return;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float m1 = xch[DB * QB * 16 + 2 * qb];
-      const float l1 = xch[DB * QB * 16 + 2 * qb + 1];
-      const float m0 = m_run[qb];
-      const float m = fmaxf(m0, m1);
-      const float a0 = m0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m0 - m) * c);
-      const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m1 - m) * c);
-      l_run[qb] = l_run[qb] * a0 + l1 * a1;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          oacc[db][qb][e] = oacc[db][qb][e] * a0 + xch[(qb * DB + db) * 16 + e] * a1;
-    }
+    b0 = b1;
+  };
+  int t = 0;
+  for (; t + 1 < ntiles; t += 2) {
+    step(t, sA, sB);
+    step(t + 1, sB, sA);
   }
+  if (t < ntiles) step(t, sA, sB);
 
   // Epilogue: divide by the row's denominator once, round, store.
+  const float l = half_sum(l_run);
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  if (qrow < N) {
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float l = half_sum(l_run[qb]);
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    const int qrow = q0 + 32 * qb + l32;
-    if (qrow < N) {
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          // elements 4g..4g+3 are columns d0..d0+3 of row qrow
-          const int d0 = 32 * db + 8 * g + 4 * hi;
-          const f32x16& acc = oacc[db][qb];
-          u32x2 out = {Ops<T>::pack(acc[4 * g] * inv, acc[4 * g + 1] * inv),
-                       Ops<T>::pack(acc[4 * g + 2] * inv, acc[4 * g + 3] * inv)};
-          *(u32x2*)(O + (size_t)qrow * D + d0) = out;
-        }
-    }
+      for (int g = 0; g < 4; ++g) {
+        // elements 4g..4g+3 are columns d0..d0+3 of row qrow
+        const int d0 = 32 * db + 8 * g + 4 * hi;
+        u32x2 out = {Ops<T>::pack(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
+                     Ops<T>::pack(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
+        *(u32x2*)(O + (size_t)qrow * D + d0) = out;
+      }
   }
 }
 
-template <typename T, int D, bool CAUSAL, bool SPLIT_P, int WM, int NW, int KSPLIT, int OCC>
+template <typename T, int D, bool CAUSAL, bool SPLIT_P, int NW, int OCC>
 hipError_t launch_one(const Args& base, int64_t BH, hipStream_t stream) {
-  using S = Shape<D, WM, NW, KSPLIT>;
+  using S = Shape<D, NW>;
   Args a = base;
   a.num_qtiles = (a.N + S::BM - 1) / S::BM;
   a.total_tiles = (int)(BH * a.num_qtiles);
   void* args[] = {&a};
-  return hipLaunchKernel((const void*)fa_forward_kernel<T, D, CAUSAL, SPLIT_P, WM, NW, KSPLIT, OCC>,
+  return hipLaunchKernel((const void*)fa_forward_kernel<T, D, CAUSAL, SPLIT_P, NW, OCC>,
                          dim3(a.total_tiles), dim3(S::NT), args, 0, stream);
 }
 
@@ -577,26 +467,29 @@ inline Args make_args(const Problem& p) {
   a.N = p.N;
   a.num_qtiles = 0;
   a.total_tiles = 0;
-  a.c = __builtin_fabsf(p.scale) * 1.4426950408889634f;
+  // A zero (or vanishing) scale becomes 2^-120: the weights stay uniform to
+  // within 1e-6 for any finite score, and masked scores (-inf) still give
+  // exp2(-inf) = 0 without a special case.
+  a.c = fmaxf(__builtin_fabsf(p.scale) * 1.4426950408889634f, 0x1p-120f);
   a.qxor = p.scale < 0.f ? 0x80008000u : 0u;
   return a;
 }
 
 // Tile shape per head dimension: 4 waves of 32 query rows (128 rows per
-// workgroup).
+// workgroup), three LDS buffers per operand.
 template <typename T, bool SPLIT_P>
 hipError_t launch(const Problem& p, hipStream_t stream) {
   const Args a = make_args(p);
   switch (p.D) {
     case 64:
-      return p.causal ? launch_one<T, 64, true, SPLIT_P, 32, 8, 2, 4>(a, p.BH, stream)
-                      : launch_one<T, 64, false, SPLIT_P, 32, 8, 2, 4>(a, p.BH, stream);
+      return p.causal ? launch_one<T, 64, true, SPLIT_P, 4, 2>(a, p.BH, stream)
+                      : launch_one<T, 64, false, SPLIT_P, 4, 2>(a, p.BH, stream);
     case 96:
-      return p.causal ? launch_one<T, 96, true, SPLIT_P, 32, 4, 1, 2>(a, p.BH, stream)
-                      : launch_one<T, 96, false, SPLIT_P, 32, 4, 1, 2>(a, p.BH, stream);
+      return p.causal ? launch_one<T, 96, true, SPLIT_P, 4, 1>(a, p.BH, stream)
+                      : launch_one<T, 96, false, SPLIT_P, 4, 1>(a, p.BH, stream);
     case 128:
-      return p.causal ? launch_one<T, 128, true, SPLIT_P, 32, 4, 1, 2>(a, p.BH, stream)
-                      : launch_one<T, 128, false, SPLIT_P, 32, 4, 1, 2>(a, p.BH, stream);
+      return p.causal ? launch_one<T, 128, true, SPLIT_P, 4, 1>(a, p.BH, stream)
+                      : launch_one<T, 128, false, SPLIT_P, 4, 1>(a, p.BH, stream);
     default:
       return hipErrorInvalidValue;
   }
