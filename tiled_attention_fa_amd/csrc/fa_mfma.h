@@ -11,14 +11,17 @@
 // to the accumulator, and at the end divides the accumulator by l once.
 //
 // gfx950 mapping (the pages target mobile GPUs; none of this is from them):
-//  * A workgroup is NW wave64s and owns BM = NW * WM query rows of one
-//    (batch, head); each wave owns WM (32 or 64) of them, in WM/32 column
-//    blocks.  A wave's Q rows are loaded once into VGPRs as the B operand of
-//    v_mfma_f32_32x32x16_{f16,bf16}.
-//  * K and V tiles of 64 keys are loaded with 16-byte coalesced loads into
-//    registers one iteration ahead (the loads of tile t+1 are in flight while
-//    tile t is computed) and stored row-major into a double-buffered LDS
-//    area, so one barrier per tile suffices.
+//  * A workgroup is NW wave64s (4) and owns 32*NW query rows of one
+//    (batch, head); each wave owns 32 of them and keeps its Q rows in VGPRs
+//    as the B operand of v_mfma_f32_32x32x16_{f16,bf16}.
+//  * Key/value tiles of 64 keys go straight from global memory to LDS
+//    (buffer_load ... lds, 16 bytes per lane) through a buffer resource that
+//    ends at key N, so rows past N read as zero.  Three LDS buffers per
+//    operand: while tile t is used, tile t+1 is resident and tile t+2 is in
+//    flight; one barrier per tile.
+//  * LDS rows are not padded (the direct loads write each wave's 1 KiB
+//    contiguously); 16-byte chunks are XOR-swizzled per row instead, so the
+//    operand reads hit distinct banks.
 //  * Scores are computed transposed, S^T = K Q^T: each lane holds 16 keys of
 //    one query per 32-key block, so row max and row sum are in-lane plus one
 //    exchange between the two 32-lane halves (v_permlane32_swap).
@@ -29,9 +32,10 @@
 //    source addresses are chosen so that lane half h gets keys
 //    {4h..4h+3, 8+4h..8+4h+3} of each 16-key chunk, the key order in which
 //    the score accumulator layout holds P.
-//  * LDS rows are padded (K by 16 bytes, V by 32 bytes) so that the 16-byte
-//    operand reads of K and the 8-byte transpose reads of V hit distinct
-//    banks within each group of lanes the LDS serves together.
+//  * Software pipeline inside each wave: the MFMAs that form the scores of
+//    tile t+1 issue among the FMAs that form the exponents of tile t (the
+//    matrix cores and FMA-type vector instructions of one wave overlap;
+//    v_exp_f32 and v_dot2 mostly do not), in one branch-free basic block.
 //  * Softmax runs in base 2: p = exp2(s * c - m * c) with c = |scale| *
 //    log2(e) in one FMA; a negative scale flips the sign of Q.  The running
 //    maximum is only raised when a tile's maximum exceeds it by more than
