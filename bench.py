@@ -123,6 +123,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=workloads.HEADLINE, choices=workloads.ORDER)
+    ap.add_argument("--settle-s", type=float, default=0.3,
+                    help="seconds of untimed launches before the warm-up steps, so that the "
+                         "GPU clock has left its ramp (it takes tens of ms under this load)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -176,6 +179,14 @@ def main():
         if st != 0:
             raise fa.FAError(st)
 
+    # Clock settle, then the W warm-up steps; neither is timed.
+    settle_launches = 0
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle_s:
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
+        settle_launches += 20
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -242,6 +253,7 @@ def main():
             "min_bytes": workloads.min_bytes(w),
         },
         "median_single_launch_us": round(median_single_us, 3),
+        "untimed_settle": {"seconds": args.settle_s, "launches": settle_launches},
         "device": {"name": prop.name, "arch": getattr(prop, "gcnArchName", ""),
                    "cus": prop.multi_processor_count,
                    "peak_used": f"dense {w.dtype} matrix-core peak {peak} TFLOP/s (published)"},

@@ -19,8 +19,9 @@ struct Problem {
   bool causal;
 };
 
-// Query rows per workgroup of each kernel family (the host sizes grids with
-// these; the kernels assert them at compile time).
+// Smallest number of query rows per workgroup of each kernel family: the
+// host bounds grid sizes with these (larger blocks only mean fewer
+// workgroups).
 constexpr int kMfmaBlockM = 128;
 constexpr int kF32BlockM = 64;
 

@@ -11,14 +11,20 @@
 // to the accumulator, and at the end divides the accumulator by l once.
 //
 // gfx950 mapping (the pages target mobile GPUs; none of this is from them):
-//  * A workgroup is NW wave64s (4) and owns 32*NW query rows of one
+//  * A workgroup is NW wave64s (4 or 8) and owns 32*NW query rows of one
 //    (batch, head); each wave owns 32 of them and keeps its Q rows in VGPRs
-//    as the B operand of v_mfma_f32_32x32x16_{f16,bf16}.
+//    as the B operand of v_mfma_f32_32x32x16_{f16,bf16}.  With eight waves
+//    the two waves that share a SIMD belong to one workgroup and advance in
+//    lockstep (one barrier per tile); waves of different workgroups on one
+//    SIMD would not: the older one wins issue and the younger ends alone.
 //  * Key/value tiles of 64 keys go straight from global memory to LDS
 //    (buffer_load ... lds, 16 bytes per lane) through a buffer resource that
-//    ends at key N, so rows past N read as zero.  Three LDS buffers per
-//    operand: while tile t is used, tile t+1 is resident and tile t+2 is in
-//    flight; one barrier per tile.
+//    ends at key N, so rows past N read as zero.  A ring of four LDS slots
+//    per operand: while tile t is used, tile t+1 is resident and tile t+2
+//    is in flight.  Each slot is an array of its own and the loop is
+//    unrolled over the ring, which lets the compiler see that the transpose
+//    reads of one slot do not touch the loads still landing in another (it
+//    would otherwise make them wait for those loads).
 //  * LDS rows are not padded (the direct loads write each wave's 1 KiB
 //    contiguously); 16-byte chunks are XOR-swizzled per row instead, so the
 //    operand reads hit distinct banks.
@@ -33,22 +39,23 @@
 //    {4h..4h+3, 8+4h..8+4h+3} of each 16-key chunk, the key order in which
 //    the score accumulator layout holds P.
 //  * Software pipeline inside each wave: the MFMAs that form the scores of
-//    tile t+1 issue among the FMAs that form the exponents of tile t (the
-//    matrix cores and FMA-type vector instructions of one wave overlap;
-//    v_exp_f32 and v_dot2 mostly do not), in one branch-free basic block.
+//    tile t+1 issue among the exponent FMAs and half of the exponentials of
+//    tile t, and the P V MFMAs of tile t among the other exponentials, the
+//    16-bit conversions and the row sums.
 //  * Softmax runs in base 2: p = exp2(s * c - m * c) with c = |scale| *
-//    log2(e) in one FMA; a negative scale flips the sign of Q.  The running
-//    maximum is only raised when a tile's maximum exceeds it by more than
-//    kLazy (in log2 units): otherwise the old maximum stays and the tile's p
-//    values may reach 2^kLazy, which fp32 accumulators and 16-bit P hold
-//    without loss; the rescale of O is then skipped for the whole wave.
-//    The result is the same softmax, exp(s - m) / sum exp(s - m), for any
-//    choice of m.
+//    log2(e) in one FMA; a negative scale flips the sign of Q.  p is formed
+//    with the running maximum as it stands and checked afterwards: only
+//    when some exponent of the wave exceeds kLazy (log2 units) does the wave
+//    raise m to the row maximum, rescale O and l, and form p again.  So the
+//    maximum stays out of the common path, tile p values may reach 2^kLazy
+//    (fp32 accumulators and 16-bit P hold that without loss), and the
+//    result is the same softmax, exp(s - m) / sum exp(s - m), for any m.
 //  * fp16: P is rounded once to fp16, and l sums exactly those rounded
-//    values (v_dot2_f32_f16 against 1.0), so the weights applied to V sum to
-//    one.  bf16: P is kept as an unevaluated sum of two bf16 numbers
-//    (hi + lo) and two PV products are issued, so P carries ~16 significant
-//    bits, as with fp16; l sums the fp32 p.
+//    values (v_fma_mix_f32, which widens a half exactly and, unlike v_dot2,
+//    issues beside running MFMAs), so the weights applied to V sum to one.
+//    bf16: P is kept as an unevaluated sum of two bf16 numbers (hi + lo)
+//    and two PV products are issued, so P carries ~16 significant bits, as
+//    with fp16; l sums the fp32 p.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -110,10 +117,16 @@ struct Ops<_Float16> {
   static __device__ __forceinline__ float hi_to_f32(uint32_t w) {
     return (float)__builtin_bit_cast(f16x2, w)[1];
   }
-  // acc + w.lo + w.hi, exact products with 1.0 and fp32 accumulation.
-  static __device__ __forceinline__ float add_pair(uint32_t w, float acc) {
-    const f16x2 one = {(_Float16)1.f, (_Float16)1.f};
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), one, acc, false);
+  // acc + the low / high fp16 half of w, in fp32 (one v_fma_mix_f32 each:
+  // the half is widened exactly, times 1.0, plus acc, rounded once).  Unlike
+  // v_dot2 these issue beside running matrix-core instructions.
+  static __device__ __forceinline__ float add_lo(uint32_t w, float acc) {
+    asm("v_fma_mix_f32 %0, %1, 1.0, %0 op_sel_hi:[1,0,0]" : "+v"(acc) : "v"(w));
+    return acc;
+  }
+  static __device__ __forceinline__ float add_hi(uint32_t w, float acc) {
+    asm("v_fma_mix_f32 %0, %1, 1.0, %0 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(acc) : "v"(w));
+    return acc;
   }
 };
 
@@ -160,6 +173,22 @@ __device__ __forceinline__ float half_sum(float x) {
   return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
+// Maximum of 32 values as a tree of v_max3_f32 (depth 4, not a chain).
+__device__ __forceinline__ float max32(const float (&x)[2][16]) {
+  float a[11];
+#pragma unroll
+  for (int i = 0; i < 10; ++i) {
+    const int j = 3 * i;
+    a[i] = fmaxf(fmaxf(x[j / 16][j % 16], x[(j + 1) / 16][(j + 1) % 16]), x[(j + 2) / 16][(j + 2) % 16]);
+  }
+  a[10] = fmaxf(x[1][14], x[1][15]);
+  const float b0 = fmaxf(fmaxf(a[0], a[1]), a[2]);
+  const float b1 = fmaxf(fmaxf(a[3], a[4]), a[5]);
+  const float b2 = fmaxf(fmaxf(a[6], a[7]), a[8]);
+  const float b3 = fmaxf(a[9], a[10]);
+  return fmaxf(fmaxf(b0, b1), fmaxf(b2, b3));
+}
+
 __device__ __forceinline__ u32x2 tr_read(const uint16_t* p) {
   const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_u16*)p);
   return __builtin_bit_cast(u32x2, r);
@@ -175,7 +204,6 @@ struct Shape {
   static constexpr int DC = D / 16;      // 16-wide contraction chunks of QK^T
   static constexpr int DB = D / 32;      // 32-row blocks of O^T
   static constexpr int TILE = BN * DP;   // elements per LDS tile buffer
-  static constexpr int NBUF = 3;         // LDS buffers per operand
   static constexpr int LOADS = BN * CPR / NT;  // 16-byte loads per thread per tile
   static_assert(D % 32 == 0 && D <= 128, "head dim");
   static_assert((BN * CPR) % NT == 0, "whole wave-loads per tile");
@@ -198,11 +226,27 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC)))
 void fa_forward_kernel(Args a) {
   using S = Shape<D, NW>;
   constexpr int BN = S::BN, BM = S::BM, NT = S::NT, DP = S::DP, CPR = S::CPR;
-  constexpr int DC = S::DC, DB = S::DB, TILE = S::TILE, NBUF = S::NBUF, LOADS = S::LOADS;
-  // K tiles [buffer], then V tiles [buffer]
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * NBUF * TILE];
-  auto kbuf = [&](int b) { return lds + b * TILE; };
-  auto vbuf = [&](int b) { return lds + (NBUF + b) * TILE; };
+  constexpr int DC = S::DC, DB = S::DB, TILE = S::TILE, LOADS = S::LOADS;
+  // A ring of four LDS slots per operand (tile t in slot t % 4), each slot
+  // an array of its own, and the step loop unrolled over the ring: the
+  // compiler can then tell the slots apart, so a transpose read of one slot
+  // does not wait for the global->LDS loads still in flight into another.
+  __shared__ __attribute__((aligned(1024))) uint16_t k0s[TILE], k1s[TILE], k2s[TILE], k3s[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t v0s[TILE], v1s[TILE], v2s[TILE], v3s[TILE];
+  auto kbuf = [&](auto slot) -> uint16_t* {
+    constexpr int j = decltype(slot)::value & 3;
+    if constexpr (j == 0) return k0s;
+    else if constexpr (j == 1) return k1s;
+    else if constexpr (j == 2) return k2s;
+    else return k3s;
+  };
+  auto vbuf = [&](auto slot) -> uint16_t* {
+    constexpr int j = decltype(slot)::value & 3;
+    if constexpr (j == 0) return v0s;
+    else if constexpr (j == 1) return v1s;
+    else if constexpr (j == 2) return v2s;
+    else return v3s;
+  };
 
   const int tid = threadIdx.x;
   // wave-uniform, so everything derived from it lives in SGPRs
@@ -239,7 +283,8 @@ void fa_forward_kernel(Args a) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
   float m_run = -INFINITY;  // running (lazy) max of raw scores q.k
-  float l_run = 0.f;        // this lane's share of the running denominator
+  float mc = 0.f;           // m_run * c once m_run is finite
+  float lp[4] = {0.f, 0.f, 0.f, 0.f};  // this lane's share of the denominator
 
   const int kv_end = CAUSAL ? min(N, qt * BM + BM) : N;
   const int ntiles = (kv_end + BN - 1) / BN;
@@ -261,7 +306,7 @@ void fa_forward_kernel(Args a) {
     kpred[i] = DP == D || (pc ^ k_swz(row)) < D / 8;
     vpred[i] = DP == D || (pc ^ v_swz(row)) < D / 8;
   }
-  auto tile_load = [&](int b, int t) {
+  auto tile_load = [&](int t, uint16_t* kdst, uint16_t* vdst) {
 #if defined(__HIP_DEVICE_COMPILE__)  // buffer resources exist in device code only
     const int k0 = t * BN;
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
@@ -273,10 +318,10 @@ void fa_forward_kernel(Args a) {
       const size_t at = (size_t)(i * NT + wave * 64) * 8;
       if (kpred[i])
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rk, (__attribute__((address_space(3))) void*)(kbuf(b) + at), 16, koff[i], 0, 0, 0);
+            rk, (__attribute__((address_space(3))) void*)(kdst + at), 16, koff[i], 0, 0, 0);
       if (vpred[i])
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rv, (__attribute__((address_space(3))) void*)(vbuf(b) + at), 16, voff[i], 0, 0, 0);
+            rv, (__attribute__((address_space(3))) void*)(vdst + at), 16, voff[i], 0, 0, 0);
     }
 #endif
   };
@@ -316,47 +361,61 @@ void fa_forward_kernel(Args a) {
     return (t * BN + BN > N) || (CAUSAL && (t * BN + BN - 1 > q0));
   };
 
-  // The work of one tile: the row maximum and the lazy-max update, the
-  // rescale of O (only when some lane raised its maximum), then one basic
-  // block without branches: the exponents (FMA) among the MFMAs of the next
-  // tile's scores, the exponentials, and P V of this tile among the
-  // conversions of P to 16 bits and the row sums.  The
-  // next tile's scores are computed even when that tile is not used (past
-  // the end, or causally masked for this wave): one wasted tile per wave
-  // keeps the block free of branches.  Masked scores are -inf and c > 0, so
-  // their p is exactly 0.
+  // The work of one tile.  The exponents x = s*c - m*c are formed with the
+  // running maximum m as it stands, and the next tile's scores (MFMA) issue
+  // among them; p = exp2(x) for the first key block follows.  Only then is
+  // the tile checked: when some x of the wave exceeds kLazy (and always on
+  // the first tile, when m is still -inf) the wave takes the rare path that
+  // raises m to the true row maximum, rescales O and the denominator by
+  // exp(m_old - m_new), and forms x and p again.  Otherwise m stays, p may
+  // reach 2^kLazy, and no rescale is needed; the result is the same softmax
+  // for any m.  Then the second key block's p, the conversion of P to 16
+  // bits, the row sums and P V.  The next tile's scores are computed even
+  // when that tile is not used (past the end, or causally masked for this
+  // wave); masked scores are -inf and c > 0, so their p is exactly 0.
   auto tile_body = [&](const uint16_t* kt_next, const uint16_t* vt, f32x16 (&sc)[2],
-                       f32x16 (&sn)[2]) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[kb][e]);
-    mx = half_max(mx);
-    // Lazy maximum: raise it only when the tile's maximum is more than
-    // kLazy (log2 units) above it; otherwise p may reach 2^kLazy.
-    const bool fresh = m_run == -INFINITY;
-    const bool raise = fresh || ((mx - m_run) * c > kLazy);
-    const float m_new = raise ? mx : m_run;
-    const float alpha = fresh ? 0.f : __builtin_amdgcn_exp2f((m_run - m_new) * c);
-    m_run = m_new;
-    const float mc = m_new == -INFINITY ? 0.f : m_new * c;
-    if (__builtin_amdgcn_ballot_w64(raise && !fresh)) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-    }
+                       f32x16 (&sn)[2], bool first) {
     float x[2][16];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) x[kb][e] = __builtin_fmaf(sc[kb][e], c, -mc);
     qk(kt_next, sn);
+    const float xmax = max32(x);
     float p[2][16];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int e = 0; e < 16; ++e) {
+      p[0][e] = __builtin_amdgcn_exp2f(x[0][e]);
+      // issue these beside the MFMAs above, not after the check below
+      asm volatile("" ::"v"(p[0][e]));
+    }
+    if (__builtin_amdgcn_ballot_w64(first || xmax > kLazy)) {
+      // keeps the compiler from turning this rare path into selects that
+      // would run on every tile
+      asm volatile("" ::: "memory");
+      float sm[2][16];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) p[kb][e] = __builtin_amdgcn_exp2f(x[kb][e]);
-    float psum = 0.f;
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sm[kb][e] = sc[kb][e];
+      const float mx = half_max(max32(sm));  // the row's maximum in this tile
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);  // 0 when m_run = -inf
+      m_run = m_new;
+      mc = m_new == -INFINITY ? 0.f : m_new * c;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lp[i] *= alpha;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) x[kb][e] = __builtin_fmaf(sc[kb][e], c, -mc);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) p[0][e] = __builtin_amdgcn_exp2f(x[0][e]);
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) p[1][e] = __builtin_amdgcn_exp2f(x[1][e]);
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
       // chunk kc (16 keys) = pairs 4*(kc&1) .. +3 of key block kc>>1
@@ -369,11 +428,11 @@ void fa_forward_kernel(Args a) {
         pf[j] = w;
         if constexpr (SPLIT_P) {
           pfl[j] = Ops<T>::pack(p0 - Ops<T>::lo_to_f32(w), p1 - Ops<T>::hi_to_f32(w));
-          psum += p0 + p1;
+          lp[j] += p0 + p1;
         } else {
           // the sum of the rounded P, so that the weights applied to V sum
           // to one (this matters when a few keys dominate a row)
-          psum = Ops<T>::add_pair(w, psum);
+          lp[j] = Ops<T>::add_hi(w, Ops<T>::add_lo(w, lp[j]));
         }
       }
 #pragma unroll
@@ -387,31 +446,34 @@ void fa_forward_kernel(Args a) {
         if constexpr (SPLIT_P) oacc[db] = Ops<T>::mma(vf, pfl, oacc[db]);
       }
     }
-    l_run = l_run * alpha + psum;
   };
 
-  // Software pipeline over NBUF = 3 LDS buffers per operand (tile t in
-  // buffer t % 3).  Step t: pass the barrier (tile t+1, whose loads went
-  // out in step t-1, is then visible, and every wave is done with step
-  // t-1 and so with buffer (t+2) % 3); issue the loads of tile t+2 into
-  // that buffer; then the tile body: softmax of tile t, whose scores were
-  // computed in step t-1, while the scores of tile t+1 are computed, and
-  // P V of tile t.
-  tile_load(0, 0);
-  if (ntiles > 1) tile_load(1, 1);
+  // Software pipeline over the ring.
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  tile_load(0, kbuf(I0{}), vbuf(I0{}));
+  if (ntiles > 1) tile_load(1, kbuf(I1{}), vbuf(I1{}));
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
   f32x16 sA[2], sB[2];
-  qk(kbuf(0), sA);  // tile 0 holds key 0, which every query sees
-  int b0 = 0;       // buffer of tile t
-  auto step = [&](int t, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
-    const int b1 = b0 == NBUF - 1 ? 0 : b0 + 1;
-    const int b2 = b1 == NBUF - 1 ? 0 : b1 + 1;
+  qk(kbuf(I0{}), sA);  // tile 0 holds key 0, which every query sees
+  // Step t (t % 4 == J): pass the barrier (tile t+1, whose loads went out
+  // in step t-1, is then visible, and every wave is done with step t-1);
+  // issue the loads of tile t+2 into slot (t+2) % 4, last read in step
+  // t-2; then the tile body: softmax of tile t, whose scores were computed
+  // in step t-1, while the scores of tile t+1 are computed, and P V of
+  // tile t.
+  auto step = [&](int t, auto J, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+    constexpr int j = decltype(J)::value;
+    using Next = std::integral_constant<int, (j + 1) & 3>;
+    using Pre2 = std::integral_constant<int, (j + 2) & 3>;
     if (t > 0) {
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile t+1 has landed
       __syncthreads();
     }
-    if (t + 2 < ntiles) tile_load(b2, t + 2);
+    if (t + 2 < ntiles) tile_load(t + 2, kbuf(Pre2{}), vbuf(Pre2{}));
     if (live(t)) {
       if (is_edge(t)) {  // ragged / causal masks
         const int k0 = t * BN;
@@ -423,19 +485,18 @@ void fa_forward_kernel(Args a) {
             if (key >= N || (CAUSAL && key > qrow)) sc[kb][e] = -INFINITY;
           }
       }
-      tile_body(kbuf(b1), vbuf(b0), sc, sn);
+      tile_body(kbuf(Next{}), vbuf(J), sc, sn, t == 0);
     }
-    b0 = b1;
   };
-  int t = 0;
-  for (; t + 1 < ntiles; t += 2) {
-    step(t, sA, sB);
-    step(t + 1, sB, sA);
+  for (int t = 0; t < ntiles; t += 4) {
+    step(t, I0{}, sA, sB);
+    if (t + 1 < ntiles) step(t + 1, I1{}, sB, sA);
+    if (t + 2 < ntiles) step(t + 2, I2{}, sA, sB);
+    if (t + 3 < ntiles) step(t + 3, I3{}, sB, sA);
   }
-  if (t < ntiles) step(t, sA, sB);
 
   // Epilogue: divide by the row's denominator once, round, store.
-  const float l = half_sum(l_run);
+  const float l = half_sum((lp[0] + lp[1]) + (lp[2] + lp[3]));
   const float inv = l > 0.f ? 1.f / l : 0.f;
   if (qrow < N) {
 #pragma unroll
@@ -479,21 +540,24 @@ inline Args make_args(const Problem& p) {
   return a;
 }
 
-// Tile shape per head dimension: 4 waves of 32 query rows (128 rows per
-// workgroup), three LDS buffers per operand.
+// Workgroup shape per head dimension and mask (measured on MI355X): eight
+// waves (256 query rows, two waves per SIMD in lockstep) where rows are
+// long and uniform; four waves (128 rows) for causal D = 64, where the
+// finer grain balances the triangle better, and for D = 96 (one wave per
+// SIMD: 128-element LDS rows leave room for one workgroup per CU).
 template <typename T, bool SPLIT_P>
 hipError_t launch(const Problem& p, hipStream_t stream) {
   const Args a = make_args(p);
   switch (p.D) {
     case 64:
       return p.causal ? launch_one<T, 64, true, SPLIT_P, 4, 2>(a, p.BH, stream)
-                      : launch_one<T, 64, false, SPLIT_P, 4, 2>(a, p.BH, stream);
+                      : launch_one<T, 64, false, SPLIT_P, 8, 1>(a, p.BH, stream);
     case 96:
       return p.causal ? launch_one<T, 96, true, SPLIT_P, 4, 1>(a, p.BH, stream)
                       : launch_one<T, 96, false, SPLIT_P, 4, 1>(a, p.BH, stream);
     case 128:
-      return p.causal ? launch_one<T, 128, true, SPLIT_P, 4, 1>(a, p.BH, stream)
-                      : launch_one<T, 128, false, SPLIT_P, 4, 1>(a, p.BH, stream);
+      return p.causal ? launch_one<T, 128, true, SPLIT_P, 8, 1>(a, p.BH, stream)
+                      : launch_one<T, 128, false, SPLIT_P, 8, 1>(a, p.BH, stream);
     default:
       return hipErrorInvalidValue;
   }
