@@ -27,7 +27,7 @@
 //    would otherwise make them wait for those loads).
 //  * LDS rows are not padded (the direct loads write each wave's 1 KiB
 //    contiguously); 16-byte chunks are XOR-swizzled per row instead, so the
-//    operand reads hit distinct banks.
+//    operand reads hit distinct banks of gfx950's 64-bank LDS.
 //  * Scores are computed transposed, S^T = K Q^T: each lane holds 16 keys of
 //    one query per 32-key block, so row max and row sum are in-lane plus one
 //    exchange between the two 32-lane halves (v_permlane32_swap).
@@ -41,7 +41,8 @@
 //  * Software pipeline inside each wave: the MFMAs that form the scores of
 //    tile t+1 issue among the exponent FMAs and half of the exponentials of
 //    tile t, and the P V MFMAs of tile t among the other exponentials, the
-//    16-bit conversions and the row sums.
+//    16-bit conversions and the row sums.  A wave raises its priority
+//    (s_setprio) while it issues the score MFMAs.
 //  * Softmax runs in base 2: p = exp2(s * c - m * c) with c = |scale| *
 //    log2(e) in one FMA; a negative scale flips the sign of Q.  p is formed
 //    with the running maximum as it stands and checked afterwards: only
@@ -213,12 +214,17 @@ struct Shape {
 // bytes, rows back to back (the direct global->LDS loads write each wave's
 // 64 x 16 bytes contiguously, so rows cannot be padded).  Chunks are
 // permuted within a row by an XOR with a function of the row:
-//  * K (read by ds_read_b128, 8 consecutive rows per LDS cycle at one
-//    logical chunk): physical chunk = chunk ^ (row & 7).
+//  * K (read by ds_read_b128, 16 consecutive rows at one logical chunk per
+//    LDS cycle, 64 banks of 4 bytes): with 128-byte rows (DP = 64) rows r
+//    and r+1 start 32 banks apart, so physical chunk = chunk ^ ((row >> 1)
+//    & 7) puts the 16 rows on 16 distinct 4-bank groups; with 256-byte rows
+//    chunk ^ (row & 7) measured faster.
 //  * V (read by ds_read_b64_tr_b16, 4 consecutive rows x 2 adjacent chunks
 //    per 16-lane group): physical chunk = chunk ^ (2 * (row & 3)).
-// Both spread the lanes served together over all 32 banks.
-__device__ __forceinline__ int k_swz(int row) { return row & 7; }
+template <int DP>
+__device__ __forceinline__ int k_swz(int row) {
+  return DP == 64 ? (row >> 1) & 7 : row & 7;
+}
 __device__ __forceinline__ int v_swz(int row) { return 2 * (row & 3); }
 
 template <typename T, int D, bool CAUSAL, bool SPLIT_P, int NW, int OCC>
@@ -301,9 +307,9 @@ void fa_forward_kernel(Args a) {
   for (int i = 0; i < LOADS; ++i) {
     const int p = i * NT + tid;
     const int row = p / CPR, pc = p % CPR;
-    koff[i] = (row * D + 8 * (pc ^ k_swz(row))) * 2;
+    koff[i] = (row * D + 8 * (pc ^ k_swz<DP>(row))) * 2;
     voff[i] = (row * D + 8 * (pc ^ v_swz(row))) * 2;
-    kpred[i] = DP == D || (pc ^ k_swz(row)) < D / 8;
+    kpred[i] = DP == D || (pc ^ k_swz<DP>(row)) < D / 8;
     vpred[i] = DP == D || (pc ^ v_swz(row)) < D / 8;
   }
   auto tile_load = [&](int t, uint16_t* kdst, uint16_t* vdst) {
@@ -338,7 +344,7 @@ void fa_forward_kernel(Args a) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const int row = 32 * kb + l32;
-        const int pc = (2 * ch + hi) ^ k_swz(row);
+        const int pc = (2 * ch + hi) ^ k_swz<DP>(row);
         const u32x4 kf = *(const u32x4*)(kt + row * DP + 8 * pc);
         s[kb] = Ops<T>::mma(kf, qf[ch], s[kb]);
       }
@@ -375,6 +381,9 @@ void fa_forward_kernel(Args a) {
   // wave); masked scores are -inf and c > 0, so their p is exactly 0.
   auto tile_body = [&](const uint16_t* kt_next, const uint16_t* vt, f32x16 (&sc)[2],
                        f32x16 (&sn)[2], bool first) {
+    // raised priority while this wave issues the next tile's score MFMAs,
+    // so that the two waves of a SIMD take turns on the matrix cores
+    __builtin_amdgcn_s_setprio(1);
     float x[2][16];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -414,6 +423,7 @@ void fa_forward_kernel(Args a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) p[0][e] = __builtin_amdgcn_exp2f(x[0][e]);
     }
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int e = 0; e < 16; ++e) p[1][e] = __builtin_amdgcn_exp2f(x[1][e]);
 #pragma unroll
@@ -437,10 +447,13 @@ void fa_forward_kernel(Args a) {
       }
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        // rows 16*kc + tr_row and +8 share the swizzle (row & 3)
-        const uint16_t* src = vt + (16 * kc + tr_row) * DP + 8 * ((4 * db) ^ tr_chunk_lo);
-        const u32x2 v0 = tr_read((const uint16_t*)((const char*)src + tr_byte));
-        const u32x2 v1 = tr_read((const uint16_t*)((const char*)(src + 8 * DP) + tr_byte));
+        // rows 16*kc + tr_row and +8 share the swizzle (row & 3); both
+        // addresses are formed from the slot base (derived one from the
+        // other, the second read lost the alias information that lets the
+        // compiler see it does not touch the slot being loaded)
+        const int col = 2 * 8 * ((4 * db) ^ tr_chunk_lo) + tr_byte;  // bytes
+        const u32x2 v0 = tr_read((const uint16_t*)((const char*)vt + (16 * kc + tr_row) * DP * 2 + col));
+        const u32x2 v1 = tr_read((const uint16_t*)((const char*)vt + (16 * kc + 8 + tr_row) * DP * 2 + col));
         const u32x4 vf = {v0[0], v0[1], v1[0], v1[1]};
         oacc[db] = Ops<T>::mma(vf, pf, oacc[db]);
         if constexpr (SPLIT_P) oacc[db] = Ops<T>::mma(vf, pfl, oacc[db]);
@@ -469,10 +482,10 @@ void fa_forward_kernel(Args a) {
     constexpr int j = decltype(J)::value;
     using Next = std::integral_constant<int, (j + 1) & 3>;
     using Pre2 = std::integral_constant<int, (j + 2) & 3>;
-    if (t > 0) {
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile t+1 has landed
-      __syncthreads();
-    }
+    // unconditional (redundant at t = 0), so that every path into the
+    // transpose reads below passes a wait for the loads of step t-1
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile t+1 has landed
+    __syncthreads();
     if (t + 2 < ntiles) tile_load(t + 2, kbuf(Pre2{}), vbuf(Pre2{}));
     if (live(t)) {
       if (is_edge(t)) {  // ragged / causal masks
@@ -488,11 +501,19 @@ void fa_forward_kernel(Args a) {
       tile_body(kbuf(Next{}), vbuf(J), sc, sn, t == 0);
     }
   };
+  // The guards nest so that step t+2 is only reached through step t+1 (and
+  // its wait for the loads of step t); with flat guards the compiler sees a
+  // path that skips it and makes the transpose reads of step t+2 wait for
+  // those loads.
   for (int t = 0; t < ntiles; t += 4) {
     step(t, I0{}, sA, sB);
-    if (t + 1 < ntiles) step(t + 1, I1{}, sB, sA);
-    if (t + 2 < ntiles) step(t + 2, I2{}, sA, sB);
-    if (t + 3 < ntiles) step(t + 3, I3{}, sB, sA);
+    if (t + 1 < ntiles) {
+      step(t + 1, I1{}, sB, sA);
+      if (t + 2 < ntiles) {
+        step(t + 2, I2{}, sA, sB);
+        if (t + 3 < ntiles) step(t + 3, I3{}, sB, sA);
+      }
+    }
   }
 
   // Epilogue: divide by the row's denominator once, round, store.
