@@ -41,8 +41,7 @@
 //  * Software pipeline inside each wave: the MFMAs that form the scores of
 //    tile t+1 issue among the exponent FMAs and half of the exponentials of
 //    tile t, and the P V MFMAs of tile t among the other exponentials, the
-//    16-bit conversions and the row sums.  A wave raises its priority
-//    (s_setprio) while it issues the score MFMAs.
+//    16-bit conversions and the row sums.
 //  * Softmax runs in base 2: p = exp2(s * c - m * c) with c = |scale| *
 //    log2(e) in one FMA; a negative scale flips the sign of Q.  p is formed
 //    with the running maximum as it stands and checked afterwards: only
@@ -381,9 +380,6 @@ void fa_forward_kernel(Args a) {
   // wave); masked scores are -inf and c > 0, so their p is exactly 0.
   auto tile_body = [&](const uint16_t* kt_next, const uint16_t* vt, f32x16 (&sc)[2],
                        f32x16 (&sn)[2], bool first) {
-    // raised priority while this wave issues the next tile's score MFMAs,
-    // so that the two waves of a SIMD take turns on the matrix cores
-    __builtin_amdgcn_s_setprio(1);
     float x[2][16];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -423,7 +419,6 @@ void fa_forward_kernel(Args a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) p[0][e] = __builtin_amdgcn_exp2f(x[0][e]);
     }
-    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int e = 0; e < 16; ++e) p[1][e] = __builtin_amdgcn_exp2f(x[1][e]);
 #pragma unroll
