@@ -44,18 +44,27 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    """Hash of the kernel sources with comments and whitespace removed, so
-    that a counter profile stays valid across comment-only edits."""
+KERNEL_SOURCES = {
+    # files that define the kernel a workload of each storage type runs
+    "f16": ["fa_api.hip", "fa_internal.h", "fa_mfma.h", "fa_mfma_f16.hip"],
+    "bf16": ["fa_api.hip", "fa_internal.h", "fa_mfma.h", "fa_mfma_bf16.hip"],
+    "f32": ["fa_api.hip", "fa_internal.h", "fa_f32.hip"],
+}
+
+
+def kernel_source_hash(dtype: str) -> str:
+    """Hash of the sources of the kernel that a workload of this storage type
+    runs, with comments and whitespace removed, so that a counter profile
+    stays valid across comment-only edits and edits of other kernels."""
     import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "tiled_attention_fa_amd", "csrc")
-    for p in sorted(glob.glob(os.path.join(csrc, "*"))):
-        text = open(p, encoding="utf-8").read()
+    for name in KERNEL_SOURCES[dtype]:
+        text = open(os.path.join(csrc, name), encoding="utf-8").read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
         text = re.sub(r"//[^\n]*", " ", text)
         text = " ".join(text.split())
-        h.update(os.path.basename(p).encode())
+        h.update(name.encode())
         h.update(text.encode())
     return h.hexdigest()[:16]
 
@@ -67,7 +76,7 @@ def committed_traffic(workload: str):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_source_hash") != kernel_source_hash(workloads.get(workload).dtype):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -258,7 +267,7 @@ def main():
                    "cus": prop.multi_processor_count,
                    "peak_used": f"dense {w.dtype} matrix-core peak {peak} TFLOP/s (published)"},
         "inputs_sha256_16": input_sha,
-        "kernel_source_hash": kernel_source_hash(),
+        "kernel_source_hash": kernel_source_hash(w.dtype),
     }
     if not args.no_check:
         rec["max_abs_err_sampled"] = parity_sample(w, x, o)

@@ -3,15 +3,20 @@
 //
 // Same tile loop as the matrix-core kernel ("Android Transformer
 // Optimization: Attention and Mobile GPU Bottlenecks", section "A Complete
-// Tile Loop"): a workgroup owns a block of query rows and walks over all
-// key/value tiles; per tile it forms the scores, updates the running maximum
-// and denominator, rescales the accumulator by exp(m_old - m_new) and adds
-// exp(S - m_new) V; O is divided by the denominator once at the end.
+// Tile Loop"): per tile the scores are formed, the running maximum and
+// denominator are updated, the accumulator is rescaled by exp(m_old - m_new)
+// and exp(S - m_new) V is added; O is divided by the denominator once at the
+// end.
 //
-// One wave64 per workgroup, one query row per lane: the lane keeps its Q row
-// and its O accumulator in registers (D <= 128 floats each).  K and V tiles
-// of 32 keys are staged in LDS; every lane reads the same K/V element at the
-// same time, which LDS serves as a broadcast.
+// A workgroup owns 64 query rows, one per lane, and has eight waves (four
+// for D > 64).  The key tiles (16 keys) are dealt round-robin to the waves:
+// each wave keeps its own running maximum, denominator and accumulator for
+// the 64 rows over its share of the keys, staging its tiles in an LDS region
+// of its own (so the waves never wait for each other inside the loop).  At
+// the end the waves' partial results are merged with the same rescaling
+// rule: with M the largest of the waves' maxima, O = sum_w exp(m_w - M)
+// acc_w / sum_w exp(m_w - M) l_w.  Every K and V element a wave reads is the
+// same for all its lanes, which LDS serves as a broadcast.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -21,7 +26,11 @@ namespace fa {
 namespace f32k {
 
 constexpr int kBlockM = kF32BlockM;  // query rows per workgroup (= lanes)
-constexpr int kBlockN = 32;          // keys per LDS tile
+constexpr int kBlockN = 16;          // keys per tile
+// waves per workgroup, each a share of the keys: eight while their merge
+// areas (64 rows x D floats each) fit in LDS, else four
+template <int D>
+constexpr int waves_for() { return D <= 64 ? 8 : 4; }
 constexpr int kXcds = 8;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -43,14 +52,31 @@ __device__ __forceinline__ int xcd_remap(int wg, int total) {
   return x * per + (x < extra ? x : extra) + slot;
 }
 
+// LDS writes of one wave made visible to all its lanes.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kBlockM) void fa_forward_f32_kernel(Args a) {
+__global__ __launch_bounds__(kBlockM * waves_for<D>()) void fa_forward_f32_kernel(Args a) {
   constexpr int BN = kBlockN;
-  static_assert(D % 4 == 0 && D <= 128, "head dim");
-  __shared__ __attribute__((aligned(16))) float Ks[BN * D];
-  __shared__ __attribute__((aligned(16))) float Vs[BN * D];
+  constexpr int kWaves = waves_for<D>();
+  static_assert(D % 16 == 0 && D <= 128, "head dim");
+  // Per wave: a K tile and a V tile; after the loop the same memory holds
+  // the waves' accumulators (64 rows x D) for the merge.
+  __shared__ __attribute__((aligned(16))) float tiles[kWaves][kBlockM * D];
+  __shared__ double m_part[kWaves][kBlockM];
+  __shared__ float l_part[kWaves][kBlockM];
+  static_assert(2 * BN * D <= kBlockM * D, "tiles fit in the merge area");
 
   const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  float* Ks = tiles[wave];
+  float* Vs = tiles[wave] + BN * D;
+
   const int logical = xcd_remap(blockIdx.x, a.total_tiles);
   const int bh = logical / a.num_qtiles;
   int qt = logical - bh * a.num_qtiles;
@@ -62,7 +88,7 @@ __global__ __launch_bounds__(kBlockM) void fa_forward_f32_kernel(Args a) {
   const float* __restrict__ V = a.v + head;
   float* __restrict__ O = a.o + head;
   const double cd = a.c;
-  const int qrow = qt * kBlockM + tid;
+  const int qrow = qt * kBlockM + lane;
 
   float q[D];
 #pragma unroll
@@ -81,9 +107,11 @@ __global__ __launch_bounds__(kBlockM) void fa_forward_f32_kernel(Args a) {
   float l_run = 0.f;
 
   const int kv_end = CAUSAL ? min(N, qt * kBlockM + kBlockM) : N;
-  for (int k0 = 0; k0 < kv_end; k0 += BN) {
-    __syncthreads();
-    for (int idx = tid; idx < BN * D / 4; idx += kBlockM) {
+  const int ntiles = (kv_end + BN - 1) / BN;
+  for (int t = wave; t < ntiles; t += kWaves) {
+    const int k0 = t * BN;
+    // this wave's tile: 16 rows of K and of V, 16 bytes per lane per load
+    for (int idx = lane; idx < BN * D / 4; idx += 64) {
       const int r = idx / (D / 4), c4 = idx - r * (D / 4);
       f32x4 kx = {0.f, 0.f, 0.f, 0.f}, vx = {0.f, 0.f, 0.f, 0.f};
       if (k0 + r < N) {
@@ -93,24 +121,30 @@ __global__ __launch_bounds__(kBlockM) void fa_forward_f32_kernel(Args a) {
       *(f32x4*)(Ks + r * D + 4 * c4) = kx;
       *(f32x4*)(Vs + r * D + 4 * c4) = vx;
     }
-    __syncthreads();
+    wave_sync();
 
     // Scores in fp64: the products of two fp32 values are exact in fp64 and
     // the D-term sum keeps ~1e-16 relative error, so large logits do not
-    // lose absolute precision before the exponential.
+    // lose absolute precision before the exponential.  Two partial sums
+    // per key halve the dependent chain.
     double s[BN];
     double mx = -INFINITY;
 #pragma unroll
     for (int j = 0; j < BN; ++j) {
-      double dot = 0.0;
+      double d0 = 0.0, d1 = 0.0;
 #pragma unroll
       for (int d = 0; d < D; d += 4) {
         const f32x4 kx = *(const f32x4*)(Ks + j * D + d);
-        dot = __builtin_fma((double)q[d], (double)kx[0], dot);
-        dot = __builtin_fma((double)q[d + 1], (double)kx[1], dot);
-        dot = __builtin_fma((double)q[d + 2], (double)kx[2], dot);
-        dot = __builtin_fma((double)q[d + 3], (double)kx[3], dot);
+        f32x4 qx = {q[d], q[d + 1], q[d + 2], q[d + 3]};
+        // for D > 64 the widened Q row (2 D registers) would not fit beside
+        // the accumulator: an opaque copy keeps the widening per use
+        if constexpr (D > 64) asm volatile("" : "+v"(qx));
+        d0 = __builtin_fma((double)qx[0], (double)kx[0], d0);
+        d1 = __builtin_fma((double)qx[1], (double)kx[1], d1);
+        d0 = __builtin_fma((double)qx[2], (double)kx[2], d0);
+        d1 = __builtin_fma((double)qx[3], (double)kx[3], d1);
       }
+      double dot = d0 + d1;
       const int key = k0 + j;
       if (key >= N || (CAUSAL && key > qrow)) dot = -INFINITY;
       s[j] = dot;
@@ -119,8 +153,8 @@ __global__ __launch_bounds__(kBlockM) void fa_forward_f32_kernel(Args a) {
     const double m_new = m_run > mx ? m_run : mx;
     // exp(scale * (s - m)) = exp2(c * (s - m)); the difference is formed in
     // fp64 before rounding to fp32, so its error is relative to |s - m|.
-    const float alpha =
-        (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((float)((m_run - m_new) * cd));
+    // A row with no visible key in this tile keeps m_new = m_run.
+    const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((float)((m_run - m_new) * cd));
     m_run = m_new;
     float pr[BN];
     float psum = 0.f;
@@ -145,14 +179,45 @@ __global__ __launch_bounds__(kBlockM) void fa_forward_f32_kernel(Args a) {
         acc[d + 3] = __builtin_fmaf(pr[j], vx[3], acc[d + 3]);
       }
     }
+    wave_sync();  // all lanes are done with the tile before the next one lands
   }
 
-  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  // Merge the waves' partial results.  Each wave publishes its maximum,
+  // denominator and accumulator (row-major, 64 rows x D); then each wave
+  // merges D / kWaves of the columns for all 64 rows.
+  __syncthreads();  // every wave is out of its tile loop (the areas are reused)
+  float* accs = tiles[wave];
+#pragma unroll
+  for (int d = 0; d < D; d += 4)
+    *(f32x4*)(accs + lane * D + d) = f32x4{acc[d], acc[d + 1], acc[d + 2], acc[d + 3]};
+  m_part[wave][lane] = m_run;
+  l_part[wave][lane] = l_run;
+  __syncthreads();
+
+  double M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) M = m_part[w][lane] > M ? m_part[w][lane] : M;
+  float f[kWaves];
+  float L = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const double mw = m_part[w][lane];
+    f[w] = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((float)((mw - M) * cd));
+    L += f[w] * l_part[w][lane];
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  constexpr int DQ = D / kWaves;  // columns merged by this wave
   if (qrow < N) {
 #pragma unroll
-    for (int d = 0; d < D; d += 4) {
-      f32x4 x = {acc[d] * inv, acc[d + 1] * inv, acc[d + 2] * inv, acc[d + 3] * inv};
-      *(f32x4*)(O + (size_t)qrow * D + d) = x;
+    for (int d = 0; d < DQ; d += 4) {
+      const int col = wave * DQ + d;
+      f32x4 out = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const f32x4 x = *(const f32x4*)(tiles[w] + lane * D + col);
+        out += f[w] * x;
+      }
+      *(f32x4*)(O + (size_t)qrow * D + col) = out * inv;
     }
   }
 }
@@ -172,12 +237,22 @@ hipError_t launch_f32(const Problem& p, hipStream_t stream) {
   a.c = __builtin_fabs((double)p.scale) * 1.4426950408889634;
   a.qsign = p.scale < 0.f ? -1.f : 1.f;
   void (*kern)(Args) = nullptr;
-  if (p.D == 64) kern = p.causal ? fa_forward_f32_kernel<64, true> : fa_forward_f32_kernel<64, false>;
-  if (p.D == 96) kern = p.causal ? fa_forward_f32_kernel<96, true> : fa_forward_f32_kernel<96, false>;
-  if (p.D == 128) kern = p.causal ? fa_forward_f32_kernel<128, true> : fa_forward_f32_kernel<128, false>;
+  int waves = 0;
+  if (p.D == 64) {
+    kern = p.causal ? fa_forward_f32_kernel<64, true> : fa_forward_f32_kernel<64, false>;
+    waves = waves_for<64>();
+  }
+  if (p.D == 96) {
+    kern = p.causal ? fa_forward_f32_kernel<96, true> : fa_forward_f32_kernel<96, false>;
+    waves = waves_for<96>();
+  }
+  if (p.D == 128) {
+    kern = p.causal ? fa_forward_f32_kernel<128, true> : fa_forward_f32_kernel<128, false>;
+    waves = waves_for<128>();
+  }
   if (!kern) return hipErrorInvalidValue;
   void* args[] = {&a};
-  return hipLaunchKernel((const void*)kern, dim3(a.total_tiles), dim3(kBlockM), args, 0, stream);
+  return hipLaunchKernel((const void*)kern, dim3(a.total_tiles), dim3(kBlockM * waves), args, 0, stream);
 }
 
 }  // namespace fa
