@@ -15,6 +15,9 @@ resident in HBM.  Prints one JSON line:
   cpu_baseline            the fp64 oracle timed on this host's cores on a
                           bounded sample of the same workload (reported
                           baseline only)
+  naive_three_pass        (16-bit storage) the three-pass attention on the
+                          same inputs: time per call, the tiled pass's
+                          speed-up over it, both byte counts
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -52,14 +55,19 @@ KERNEL_SOURCES = {
 }
 
 
-def kernel_source_hash(dtype: str) -> str:
+# files that define the three kernels of the three-pass comparison path
+NAIVE_SOURCES = {dt: ["fa_api.hip", "fa_internal.h", "fa_mfma.h", "fa_naive.hip"] for dt in ("f16", "bf16")}
+
+
+def kernel_source_hash(dtype: str, sources=None) -> str:
     """Hash of the sources of the kernel that a workload of this storage type
-    runs, with comments and whitespace removed, so that a counter profile
-    stays valid across comment-only edits and edits of other kernels."""
+    runs (or of the files listed), with comments and whitespace removed, so
+    that a counter profile stays valid across comment-only edits and edits
+    of other kernels."""
     import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "tiled_attention_fa_amd", "csrc")
-    for name in KERNEL_SOURCES[dtype]:
+    for name in (sources if sources is not None else KERNEL_SOURCES[dtype]):
         text = open(os.path.join(csrc, name), encoding="utf-8").read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
         text = re.sub(r"//[^\n]*", " ", text)
@@ -69,14 +77,16 @@ def kernel_source_hash(dtype: str) -> str:
     return h.hexdigest()[:16]
 
 
-def committed_traffic(workload: str):
-    """HBM bytes per launch from a committed counter profile of the current
-    kernel source, or None."""
-    path = os.path.join(PROFILE_DIR, f"traffic_{workload}.json")
+def committed_traffic(name: str, sources=None):
+    """HBM bytes per call from a committed counter profile (traffic_<name>.json,
+    name = a workload, or "naive_" + a workload) of the current kernel
+    source, or None."""
+    path = os.path.join(PROFILE_DIR, f"traffic_{name}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("kernel_source_hash") != kernel_source_hash(workloads.get(workload).dtype):
+    dtype = workloads.get(name[len("naive_"):] if name.startswith("naive_") else name).dtype
+    if rec.get("kernel_source_hash") != kernel_source_hash(dtype, sources):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -126,6 +136,52 @@ def parity_sample(w, x, o):
     return float(np.abs(got - ref).max())
 
 
+def naive_leg(w, q, k, v, o, stream, code, lib, steps, tiled_ms):
+    """The three-pass comparison (S and P through HBM) on the same inputs:
+    mean time per call over `steps` back-to-back calls, its bytes against
+    the tiled pass, and its largest difference from the tiled pass's O."""
+    import torch
+    import tiled_attention_fa_amd as fa
+    ws = fa.naive_workspace(q)
+    on = torch.empty_like(o)
+    cargs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), on.data_ptr(), w.B, w.H, w.N, w.D,
+             float(w.scale), int(w.causal), code, ws.data_ptr(), ws.numel(), stream.cuda_stream)
+
+    def call():
+        st = lib.fa_naive_forward(*cargs)
+        if st != 0:
+            raise fa.FAError(st)
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        call()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    nb = workloads.naive_bytes(w)
+    diff = float((on.float() - o.float()).abs().max().item())
+    log(f"three-pass: {ms * 1e3:.2f} us per call ({steps} calls), {nb / (ms * 1e-3) / 1e9:.0f} GB/s "
+        f"algorithmic; tiled pass {ms / tiled_ms:.2f}x faster")
+    return {
+        "ms_per_call": round(ms, 5),
+        "calls": steps,
+        "tiled_speedup": round(ms / tiled_ms, 3),
+        "algorithmic_bytes": nb,
+        "achieved_GBs": round(nb / (ms * 1e-3) / 1e9, 1),
+        "frac_hbm_peak": round(nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "tiled_min_bytes": workloads.min_bytes(w),
+        "bytes_ratio": round(nb / workloads.min_bytes(w), 2),
+        "workspace_bytes": ws.numel(),
+        "traffic": committed_traffic("naive_" + w.name, sources=NAIVE_SOURCES[w.dtype]),
+        "max_abs_diff_vs_tiled": diff,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -137,6 +193,8 @@ def main():
                          "GPU clock has left its ramp (it takes tens of ms under this load)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--no-naive", action="store_true",
+                    help="skip the three-pass comparison leg (16-bit storage only)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of attention, time a plain device copy of this many MiB "
                          "(reference kernel for scaling HBM byte counters)")
@@ -235,6 +293,10 @@ def main():
         singles.append(e0.elapsed_time(e1) * 1e3)
     median_single_us = float(np.median(singles))
 
+    naive = None
+    if w.dtype != "f32" and not args.no_naive:
+        naive = naive_leg(w, q, k, v, o, stream, code, lib, max(10, min(args.steps, 50)), ms_per_step)
+
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -269,6 +331,8 @@ def main():
         "inputs_sha256_16": input_sha,
         "kernel_source_hash": kernel_source_hash(w.dtype),
     }
+    if naive is not None:
+        rec["naive_three_pass"] = naive
     if not args.no_check:
         rec["max_abs_err_sampled"] = parity_sample(w, x, o)
     if not args.no_cpu_baseline:

@@ -19,7 +19,8 @@
  * denominator once at the end; the N x N score matrix never reaches memory.
  *
  * All entry points are plain C, take plain pointers and sizes, never throw,
- * never print and never allocate device memory.
+ * never print and never allocate device memory (the three-pass comparison
+ * path at the end takes its scratch space from the caller).
  */
 #ifndef FA_H_
 #define FA_H_
@@ -48,13 +49,14 @@ typedef enum fa_status {
   FA_ERR_NULL = -1,           /* q, k, v or o is NULL (with N > 0) */
   FA_ERR_DIM = -2,            /* B < 1, H < 1, N < 0 or D < 1 */
   FA_ERR_UNSUPPORTED_D = -3,  /* head dimension not in {64, 96, 128} */
-  FA_ERR_DTYPE = -4,          /* dtype is not an fa_dtype value */
+  FA_ERR_DTYPE = -4,          /* dtype not an fa_dtype value, or not taken by the call */
   FA_ERR_ALIGN = -5,          /* a pointer is not 16-byte aligned */
   FA_ERR_ALIAS = -6,          /* o overlaps q, k or v */
   FA_ERR_LAUNCH = -7,         /* the HIP runtime refused the launch */
   FA_ERR_SCALE = -8,          /* scale is NaN or infinite */
   FA_ERR_TOO_LARGE = -9,      /* N*D >= 2^31, or the grid would overflow */
-  FA_ERR_DEVICE = -10         /* current device is not gfx950, or no device */
+  FA_ERR_DEVICE = -10,        /* current device is not gfx950, or no device */
+  FA_ERR_WORKSPACE = -11      /* workspace NULL, misaligned, too small or overlapping */
 } fa_status;
 
 /*
@@ -85,6 +87,71 @@ typedef enum fa_status {
  */
 int fa_forward(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H,
                int64_t N, int64_t D, float scale, int causal, int dtype, void* stream);
+
+/*
+ * The three-pass ("naive") attention that tiling is measured against:
+ * "Android Transformer Optimization: Attention and Mobile GPU Bottlenecks",
+ * section "The Self-Attention Bottleneck Is Memory Traffic, Not Compute",
+ * and "Flash Attention on Android: tiled SGEMM with RenderScript", sections
+ * "The bottleneck most engineers misdiagnose" and "Benchmark results:
+ * Snapdragon vs. Dimensity", describe it: the full N x N score matrix is
+ * written to memory, read back for the row softmax, and the probabilities
+ * are read back once more for the product with V.  It computes the same O
+ * as fa_forward (same arguments, same masking) and exists to measure what
+ * the tiled pass saves.  Three kernels are enqueued on `stream`:
+ *
+ *   scores:  S[i][j] = scale * q_i . k_j, fp32, [B*H, N, NP] row-major
+ *            with NP = N rounded up to 64 (keys N..NP-1 are not written;
+ *            causal: only the 32-key blocks up to each row block's
+ *            diagonal are);
+ *   softmax: P[i][j] = exp(S[i][j] - max_j S[i][j]) / sum_j exp(...), the
+ *            storage type, [B*H, N, NP] (keys past N, and under the causal
+ *            mask keys past i up to the end of i's 64-key block, get 0);
+ *            within every aligned group of 16 keys the entries are stored
+ *            in the key order 0-3, 8-11, 4-7, 12-15 (the order in which the
+ *            third kernel's matrix-core operand takes them); for FA_BF16 P
+ *            is kept as two bf16 arrays, a rounded value and the rounded
+ *            remainder, whose sum carries 16 significant bits;
+ *   P V:     O = P V, the storage type.
+ *
+ * Only FA_F16 and FA_BF16 are taken (FA_F32 returns FA_ERR_DTYPE).
+ */
+
+/*
+ * fa_naive_workspace_bytes -- bytes of workspace fa_naive_forward needs for
+ * these sizes: B*H*N*NP*4 (S), then B*H*N*NP*2 (P), then for FA_BF16 another
+ * B*H*N*NP*2 (the remainders of P), each part starting on a 256-byte
+ * boundary.  0 when N == 0.  Returns a negative fa_status instead for an
+ * unsupported dtype (FA_ERR_DTYPE), B < 1, H < 1 or N < 0 (FA_ERR_DIM), or
+ * a size that does not fit in int64_t (FA_ERR_TOO_LARGE).  Host only; no
+ * device call.
+ */
+int64_t fa_naive_workspace_bytes(int64_t B, int64_t H, int64_t N, int dtype);
+
+/*
+ * fa_naive_forward -- O = softmax(scale*QK^T [+mask]) V in three passes
+ * through the caller's workspace.
+ *
+ *   q, k, v, o, B, H, N, D, scale, causal, stream
+ *                    as for fa_forward (dtype FA_F16 or FA_BF16 only).
+ *   workspace        device memory of the current device, 256-byte
+ *                    aligned, at least fa_naive_workspace_bytes(B, H, N,
+ *                    dtype) bytes, overlapping none of q, k, v, o.  Its
+ *                    contents on entry do not matter; on return (once the
+ *                    stream has run) it holds S and P as laid out above.
+ *                    The caller owns it and must not use it until the
+ *                    stream has finished the call.
+ *   workspace_bytes  its size in bytes.
+ *
+ * Checks and status codes as for fa_forward, in the same order, then
+ * FA_ERR_TOO_LARGE for N > 2^20, then FA_ERR_WORKSPACE for a NULL,
+ * misaligned, short or overlapping workspace (all before anything is
+ * enqueued).  Asynchronous; allocates nothing.
+ * Calls that share a workspace and overlap in time race.
+ */
+int fa_naive_forward(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H,
+                     int64_t N, int64_t D, float scale, int causal, int dtype, void* workspace,
+                     int64_t workspace_bytes, void* stream);
 
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* fa_status_string(int status);

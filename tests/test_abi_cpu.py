@@ -85,3 +85,80 @@ def test_validation(lib, args, status):
     if status == "FA_ERR_DEVICE" and got == 0:
         pytest.skip("a gfx950 device is present; the no-device path is not reachable")
     assert fa.STATUS_NAMES[got] == status
+
+
+# ------------------------------------------------- three-pass entry points
+
+def _ws(B, H, N, dt):
+    NP = (N + 63) // 64 * 64
+    up = lambda x: (x + 255) // 256 * 256
+    s = B * H * N * NP * 4
+    p = B * H * N * NP * 2
+    p_off = up(s)
+    plo_off = up(p_off + p)
+    return up(plo_off + p) if dt == fa.FA_BF16 else plo_off
+
+
+@pytest.mark.parametrize("B,H,N", [(1, 1, 0), (1, 1, 1), (1, 32, 2048), (4, 32, 2048), (2, 8, 1000),
+                                   (1, 16, 8192), (3, 5, 77)])
+@pytest.mark.parametrize("dt", [1, 2])
+def test_naive_workspace_bytes(lib, B, H, N, dt):
+    assert fa.fa_naive_workspace_bytes(B, H, N, dt) == _ws(B, H, N, dt)
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(dtype=0), "FA_ERR_DTYPE"),
+    (dict(dtype=9), "FA_ERR_DTYPE"),
+    (dict(B=0), "FA_ERR_DIM"),
+    (dict(N=-1), "FA_ERR_DIM"),
+    (dict(B=1 << 40, H=1 << 40), "FA_ERR_TOO_LARGE"),
+    (dict(B=1 << 20, N=1 << 20), "FA_ERR_TOO_LARGE"),
+])
+def test_naive_workspace_bytes_rejects(lib, args, status):
+    kw = dict(B=1, H=1, N=64, dtype=1)
+    kw.update(args)
+    got = fa.fa_naive_workspace_bytes(kw["B"], kw["H"], kw["N"], kw["dtype"])
+    assert fa.STATUS_NAMES[got] == status
+
+
+W = 0x10000000  # fake 256-byte aligned workspace, clear of the tensors
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(dtype=0), "FA_ERR_DTYPE"),
+    (dict(dtype=5), "FA_ERR_DTYPE"),
+    (dict(B=0), "FA_ERR_DIM"),
+    (dict(D=80), "FA_ERR_UNSUPPORTED_D"),
+    (dict(scale=float("nan")), "FA_ERR_SCALE"),
+    (dict(N=0, q=0, k=0, v=0, o=0, ws=0, ws_bytes=0), "FA_OK"),
+    (dict(v=0), "FA_ERR_NULL"),
+    (dict(o=O + 4), "FA_ERR_ALIGN"),
+    (dict(o=C), "FA_ERR_ALIAS"),
+    (dict(N=1 << 25, D=64), "FA_ERR_TOO_LARGE"),
+    (dict(N=(1 << 20) + 1, D=64, q=1 << 40, k=2 << 40, v=3 << 40, o=4 << 40, ws=5 << 40,
+          ws_bytes=1 << 62), "FA_ERR_TOO_LARGE"),
+    (dict(ws=0), "FA_ERR_WORKSPACE"),
+    (dict(ws=W + 128), "FA_ERR_WORKSPACE"),
+    (dict(ws_bytes=-1), "FA_ERR_WORKSPACE"),
+    (dict(ws_bytes="short"), "FA_ERR_WORKSPACE"),
+    (dict(ws=O - 256), "FA_ERR_WORKSPACE"),
+    (dict(ws=A + 4096), "FA_ERR_WORKSPACE"),
+    (dict(ws=A - 8192), "FA_ERR_WORKSPACE"),
+    (dict(), "FA_ERR_DEVICE"),
+    (dict(dtype=2), "FA_ERR_DEVICE"),
+])
+def test_naive_validation(lib, args, status):
+    kw = dict(q=A, k=B_, v=C, o=O, B=1, H=1, N=64, D=64, scale=0.125, causal=False, dtype=1, ws=W)
+    kw.update(args)
+    need = fa.fa_naive_workspace_bytes(kw["B"], kw["H"], max(kw["N"], 0), kw["dtype"]) \
+        if kw["dtype"] in (1, 2) and kw["B"] >= 1 and kw["N"] >= 0 else 1 << 20
+    if "ws_bytes" not in kw:
+        kw["ws_bytes"] = need
+    elif kw["ws_bytes"] == "short":
+        kw["ws_bytes"] = need - 1
+    got = fa.fa_naive_forward_raw(kw["q"], kw["k"], kw["v"], kw["o"], kw["B"], kw["H"], kw["N"],
+                                  kw["D"], kw["scale"], kw["causal"], kw["dtype"], kw["ws"],
+                                  kw["ws_bytes"])
+    if status == "FA_ERR_DEVICE" and got == 0:
+        pytest.skip("a gfx950 device is present; the no-device path is not reachable")
+    assert fa.STATUS_NAMES[got] == status

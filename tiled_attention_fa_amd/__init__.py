@@ -15,9 +15,14 @@ from ._lib import (  # noqa: F401
     STATUS_NAMES,
     fa_forward,
     fa_forward_raw,
+    fa_naive_forward,
+    fa_naive_forward_raw,
+    fa_naive_workspace_bytes,
     fa_status_string,
     fa_version,
     forward,
     library_path,
     load_library,
+    naive_forward,
+    naive_workspace,
 )

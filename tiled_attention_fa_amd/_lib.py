@@ -21,10 +21,12 @@ STATUS_NAMES = {
     -8: "FA_ERR_SCALE",
     -9: "FA_ERR_TOO_LARGE",
     -10: "FA_ERR_DEVICE",
+    -11: "FA_ERR_WORKSPACE",
 }
 
 # Every symbol include/fa.h declares.
-EXPORTS = ("fa_forward", "fa_status_string", "fa_version")
+EXPORTS = ("fa_forward", "fa_naive_forward", "fa_naive_workspace_bytes", "fa_status_string",
+           "fa_version")
 
 _lib = None
 
@@ -53,6 +55,11 @@ def load_library():
     lib.fa_forward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float, ctypes.c_int,
                                ctypes.c_int, vp]
     lib.fa_forward.restype = ctypes.c_int
+    lib.fa_naive_forward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float, ctypes.c_int,
+                                     ctypes.c_int, vp, i64, vp]
+    lib.fa_naive_forward.restype = ctypes.c_int
+    lib.fa_naive_workspace_bytes.argtypes = [i64, i64, i64, ctypes.c_int]
+    lib.fa_naive_workspace_bytes.restype = i64
     lib.fa_status_string.argtypes = [ctypes.c_int]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
@@ -78,6 +85,22 @@ def fa_forward_raw(q: int, k: int, v: int, o: int, B: int, H: int, N: int, D: in
                                      stream or None)
 
 
+def fa_naive_workspace_bytes(B: int, H: int, N: int, dtype: int) -> int:
+    """Workspace bytes of the three-pass path (negative status on bad
+    arguments)."""
+    return int(load_library().fa_naive_workspace_bytes(int(B), int(H), int(N), int(dtype)))
+
+
+def fa_naive_forward_raw(q: int, k: int, v: int, o: int, B: int, H: int, N: int, D: int,
+                         scale: float, causal: bool, dtype: int, workspace: int, workspace_bytes: int,
+                         stream: int = 0) -> int:
+    """Direct call of the three-pass entry point; returns the status code."""
+    return load_library().fa_naive_forward(q or None, k or None, v or None, o or None, int(B), int(H),
+                                           int(N), int(D), float(scale), int(bool(causal)),
+                                           int(dtype), workspace or None, int(workspace_bytes),
+                                           stream or None)
+
+
 def _dtype_code(t):
     import torch
     codes = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
@@ -86,12 +109,7 @@ def _dtype_code(t):
     return codes[t.dtype]
 
 
-def fa_forward(q, k, v, o, scale=None, causal=False, stream=None) -> None:
-    """o <- softmax(scale * q k^T [+ causal mask]) v for torch tensors of shape
-    [B, H, N, D] on the current HIP device (contiguous, one dtype).
-    scale defaults to 1/sqrt(D); stream defaults to torch's current stream.
-    Enqueues the kernel and returns; raises FAError on a rejected call."""
-    import torch
+def _check_qkvo(q, k, v, o):
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
         if t.dim() != 4:
             raise ValueError(f"{name} must be [B, H, N, D], got shape {tuple(t.shape)}")
@@ -101,12 +119,26 @@ def fa_forward(q, k, v, o, scale=None, causal=False, stream=None) -> None:
             raise ValueError(f"{name} must match q in shape, dtype and device")
     if q.device.type != "cuda":
         raise ValueError("tensors must be on a HIP device")
+
+
+def _stream_handle(stream, device):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def fa_forward(q, k, v, o, scale=None, causal=False, stream=None) -> None:
+    """o <- softmax(scale * q k^T [+ causal mask]) v for torch tensors of shape
+    [B, H, N, D] on the current HIP device (contiguous, one dtype).
+    scale defaults to 1/sqrt(D); stream defaults to torch's current stream.
+    Enqueues the kernel and returns; raises FAError on a rejected call."""
+    import torch
+    _check_qkvo(q, k, v, o)
     B, H, N, D = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
-    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    handle = _stream_handle(stream, q.device)
     with torch.cuda.device(q.device):
         st = fa_forward_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, H, N, D,
                             scale, causal, _dtype_code(q), handle)
@@ -119,4 +151,46 @@ def forward(q, k, v, scale=None, causal=False, stream=None):
     import torch
     o = torch.empty_like(q)
     fa_forward(q, k, v, o, scale=scale, causal=causal, stream=stream)
+    return o
+
+
+def naive_workspace(q):
+    """A uint8 device tensor big enough for the three-pass path on tensors
+    shaped and typed like q (torch's allocator returns 256-byte aligned
+    blocks)."""
+    import torch
+    B, H, N, _ = q.shape
+    n = fa_naive_workspace_bytes(B, H, N, _dtype_code(q))
+    if n < 0:
+        raise FAError(n)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+
+
+def fa_naive_forward(q, k, v, o, workspace, scale=None, causal=False, stream=None) -> None:
+    """The three-pass attention (S and P through `workspace`, a uint8 device
+    tensor from naive_workspace); same result as fa_forward.  Enqueues and
+    returns; raises FAError on a rejected call."""
+    import torch
+    _check_qkvo(q, k, v, o)
+    if workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    B, H, N, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    handle = _stream_handle(stream, q.device)
+    with torch.cuda.device(q.device):
+        st = fa_naive_forward_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, H, N, D,
+                                  scale, causal, _dtype_code(q), workspace.data_ptr(),
+                                  workspace.numel() * workspace.element_size(), handle)
+    if st != 0:
+        raise FAError(st)
+
+
+def naive_forward(q, k, v, scale=None, causal=False, stream=None, workspace=None):
+    """Allocate o (and the workspace unless given) and run the three-pass
+    path; returns o."""
+    import torch
+    o = torch.empty_like(q)
+    ws = workspace if workspace is not None else naive_workspace(q)
+    fa_naive_forward(q, k, v, o, ws, scale=scale, causal=causal, stream=stream)
     return o

@@ -37,6 +37,61 @@ int check_device() {
   return state == 1 ? FA_OK : FA_ERR_DEVICE;
 }
 
+// Checks shared by both forward entry points, in the documented order
+// (dtype, sizes, head dim, scale, N == 0, pointers, alignment, size limits,
+// aliasing).  *BH receives B * H.  Returns FA_OK, a negative status, or 1
+// for an accepted N == 0 call (nothing to do).
+int validate(const void* q, const void* k, const void* v, const void* o, int64_t B, int64_t H,
+             int64_t N, int64_t D, float scale, int dtype, int64_t block_m, int64_t* BH) {
+  if (B < 1 || H < 1 || N < 0 || D < 1) return FA_ERR_DIM;
+  if (!head_dim_supported(D)) return FA_ERR_UNSUPPORTED_D;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  if (N == 0) return 1;
+  if (!q || !k || !v || !o) return FA_ERR_NULL;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) return FA_ERR_ALIGN;
+
+  // Sizes: per-head indexing is 32-bit; the grid is one workgroup per block
+  // of query rows of every head, and its work-item count must fit in 32
+  // bits (at most 512 work-items per 64 rows: 8 * N + 512 per head bounds
+  // every kernel's total).
+  if (N * D >= ((int64_t)1 << 31)) return FA_ERR_TOO_LARGE;
+  if (B > ((int64_t)1 << 31) / H) return FA_ERR_TOO_LARGE;
+  *BH = B * H;
+  const int64_t qtiles = (N + block_m - 1) / block_m;
+  if (*BH > (((int64_t)1 << 31) - 1) / qtiles) return FA_ERR_TOO_LARGE;
+  if (*BH > (int64_t)UINT32_MAX / (8 * N + 512)) return FA_ERR_TOO_LARGE;
+  const int64_t elem = dtype == FA_F32 ? 4 : 2;
+  if (*BH > INT64_MAX / (N * D * elem)) return FA_ERR_TOO_LARGE;
+  const size_t bytes = (size_t)(*BH * N * D * elem);
+  if (ranges_overlap(o, bytes, q, bytes) || ranges_overlap(o, bytes, k, bytes) ||
+      ranges_overlap(o, bytes, v, bytes))
+    return FA_ERR_ALIAS;
+  return FA_OK;
+}
+
+constexpr int64_t kWsAlign = 256;
+// Longest rows of the three-pass path (a workgroup's 128 rows of P then
+// span less than 2^31 bytes; the workspace for one such head is already
+// 12 TiB).
+constexpr int64_t kNaiveMaxN = (int64_t)1 << 20;
+
+int64_t align_up(int64_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+// Workspace of the three-pass path: S (fp32, BH x N x NP), then P (16-bit,
+// BH x N x NP), then for bf16 the low parts of P (same size); each part
+// starts on a 256-byte boundary.  Returns the offsets, or false when the
+// total does not fit in int64.
+bool naive_layout(int64_t BH, int64_t N, int dtype, int64_t* p_off, int64_t* plo_off, int64_t* total) {
+  const int64_t NP = (N + 63) / 64 * 64;
+  if (N > 0 && BH > INT64_MAX / 16 / N / NP) return false;  // 4 + 2 + 2 bytes per entry, with room
+  const int64_t s_bytes = BH * N * NP * 4;
+  const int64_t p_bytes = BH * N * NP * 2;
+  *p_off = align_up(s_bytes);
+  *plo_off = align_up(*p_off + p_bytes);
+  *total = dtype == FA_BF16 ? align_up(*plo_off + p_bytes) : *plo_off;
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -44,27 +99,11 @@ extern "C" {
 int fa_forward(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H,
                int64_t N, int64_t D, float scale, int causal, int dtype, void* stream) {
   if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
-  if (B < 1 || H < 1 || N < 0 || D < 1) return FA_ERR_DIM;
-  if (!head_dim_supported(D)) return FA_ERR_UNSUPPORTED_D;
-  if (!isfinite(scale)) return FA_ERR_SCALE;
-  if (N == 0) return FA_OK;
-  if (!q || !k || !v || !o) return FA_ERR_NULL;
-  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) return FA_ERR_ALIGN;
-
-  // Sizes: per-head indexing is 32-bit, the grid is one workgroup per block
-  // of query rows of every head.
+  int64_t BH = 0;
   const int64_t block_m = dtype == FA_F32 ? fa::kF32BlockM : fa::kMfmaBlockM;
-  if (N * D >= ((int64_t)1 << 31)) return FA_ERR_TOO_LARGE;
-  if (B > ((int64_t)1 << 31) / H) return FA_ERR_TOO_LARGE;
-  const int64_t BH = B * H;
-  const int64_t qtiles = (N + block_m - 1) / block_m;
-  if (BH > (((int64_t)1 << 31) - 1) / qtiles) return FA_ERR_TOO_LARGE;
-  const int64_t elem = dtype == FA_F32 ? 4 : 2;
-  if (BH > INT64_MAX / (N * D * elem)) return FA_ERR_TOO_LARGE;
-  const size_t bytes = (size_t)(BH * N * D * elem);
-  if (ranges_overlap(o, bytes, q, bytes) || ranges_overlap(o, bytes, k, bytes) ||
-      ranges_overlap(o, bytes, v, bytes))
-    return FA_ERR_ALIAS;
+  const int st = validate(q, k, v, o, B, H, N, D, scale, dtype, block_m, &BH);
+  if (st == 1) return FA_OK;
+  if (st != FA_OK) return st;
 
   const int dev = check_device();
   if (dev != FA_OK) return dev;
@@ -89,19 +128,69 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, int64_t B, 
   return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+int64_t fa_naive_workspace_bytes(int64_t B, int64_t H, int64_t N, int dtype) {
+  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (B < 1 || H < 1 || N < 0) return FA_ERR_DIM;
+  if (B > INT64_MAX / H) return FA_ERR_TOO_LARGE;
+  int64_t p_off, plo_off, total;
+  if (!naive_layout(B * H, N, dtype, &p_off, &plo_off, &total)) return FA_ERR_TOO_LARGE;
+  return total;
+}
+
+int fa_naive_forward(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H,
+                     int64_t N, int64_t D, float scale, int causal, int dtype, void* workspace,
+                     int64_t workspace_bytes, void* stream) {
+  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  int64_t BH = 0;
+  const int st = validate(q, k, v, o, B, H, N, D, scale, dtype, fa::kMfmaBlockM, &BH);
+  if (st == 1) return FA_OK;
+  if (st != FA_OK) return st;
+  if (N > kNaiveMaxN) return FA_ERR_TOO_LARGE;
+  int64_t p_off, plo_off, total;
+  if (!naive_layout(BH, N, dtype, &p_off, &plo_off, &total)) return FA_ERR_TOO_LARGE;
+  if (!workspace || ((uintptr_t)workspace & (kWsAlign - 1)) || workspace_bytes < total)
+    return FA_ERR_WORKSPACE;
+  const size_t bytes = (size_t)(BH * N * D * 2);
+  if (ranges_overlap(workspace, (size_t)total, q, bytes) || ranges_overlap(workspace, (size_t)total, k, bytes) ||
+      ranges_overlap(workspace, (size_t)total, v, bytes) || ranges_overlap(workspace, (size_t)total, o, bytes))
+    return FA_ERR_WORKSPACE;
+
+  const int dev = check_device();
+  if (dev != FA_OK) return dev;
+
+  fa::NaiveProblem p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.s = workspace;
+  p.p = (char*)workspace + p_off;
+  p.plo = dtype == FA_BF16 ? (char*)workspace + plo_off : nullptr;
+  p.BH = BH;
+  p.N = (int)N;
+  p.NP = (int)((N + 63) / 64 * 64);
+  p.D = (int)D;
+  p.scale = scale;
+  p.causal = causal != 0;
+  hipStream_t s = (hipStream_t)stream;
+  const hipError_t err = dtype == FA_F16 ? fa::launch_naive_f16(p, s) : fa::launch_naive_bf16(p, s);
+  return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "a tensor pointer is NULL";
     case FA_ERR_DIM: return "invalid sizes (need B >= 1, H >= 1, N >= 0, D >= 1)";
     case FA_ERR_UNSUPPORTED_D: return "unsupported head dimension (supported: 64, 96, 128)";
-    case FA_ERR_DTYPE: return "unknown dtype (FA_F32, FA_F16 or FA_BF16)";
+    case FA_ERR_DTYPE: return "dtype not accepted here (fa_forward: FA_F32, FA_F16, FA_BF16; naive: FA_F16, FA_BF16)";
     case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
     case FA_ERR_ALIAS: return "output overlaps an input";
     case FA_ERR_LAUNCH: return "kernel launch failed";
     case FA_ERR_SCALE: return "scale is not finite";
-    case FA_ERR_TOO_LARGE: return "problem too large (N*D must be < 2^31)";
+    case FA_ERR_TOO_LARGE: return "problem too large (N*D must be < 2^31 and the grid must fit)";
     case FA_ERR_DEVICE: return "current HIP device is not a gfx950 (MI355X)";
+    case FA_ERR_WORKSPACE: return "workspace NULL, not 256-byte aligned, too small or overlapping a tensor";
     default: return "unknown status";
   }
 }

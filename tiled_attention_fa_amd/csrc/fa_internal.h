@@ -19,6 +19,26 @@ struct Problem {
   bool causal;
 };
 
+// One validated three-pass problem: the forward problem plus the caller's
+// workspace, cut into the fp32 score matrix S [BH, N, N] and the
+// probabilities P [BH, N, NP] (NP = N rounded up to 64; for bf16 a second
+// array of the low parts).
+struct NaiveProblem {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  void* s;
+  void* p;
+  void* plo;
+  int64_t BH;
+  int N;
+  int NP;
+  int D;
+  float scale;
+  bool causal;
+};
+
 // Smallest number of query rows per workgroup of each kernel family: the
 // host bounds grid sizes with these (larger blocks only mean fewer
 // workgroups).
@@ -30,5 +50,7 @@ constexpr int kF32BlockM = 64;
 hipError_t launch_mfma_f16(const Problem& p, hipStream_t stream);
 hipError_t launch_mfma_bf16(const Problem& p, hipStream_t stream);
 hipError_t launch_f32(const Problem& p, hipStream_t stream);
+hipError_t launch_naive_f16(const NaiveProblem& p, hipStream_t stream);
+hipError_t launch_naive_bf16(const NaiveProblem& p, hipStream_t stream);
 
 }  // namespace fa

@@ -267,8 +267,8 @@ void fa_forward_kernel(Args a) {
   const int N = a.N;
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint16_t* __restrict__ Q = a.q + head;
-  const uint16_t* __restrict__ K = a.k + head;
-  const uint16_t* __restrict__ V = a.v + head;
+  [[maybe_unused]] const uint16_t* __restrict__ K = a.k + head;
+  [[maybe_unused]] const uint16_t* __restrict__ V = a.v + head;
   uint16_t* __restrict__ O = a.o + head;
   const float c = a.c;
 
@@ -314,10 +314,13 @@ void fa_forward_kernel(Args a) {
   auto tile_load = [&](int t, uint16_t* kdst, uint16_t* vdst) {
 #if defined(__HIP_DEVICE_COMPILE__)  // buffer resources exist in device code only
     const int k0 = t * BN;
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(K + (size_t)k0 * D), 0, (N - k0) * D * 2, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(V + (size_t)k0 * D), 0, (N - k0) * D * 2, 0x00020000);
+    // bytes from key k0 to the end of the head: below 2^32 (N * D < 2^31),
+    // formed in unsigned arithmetic, passed as the 32-bit record count
+    const int bytes = (int)((uint32_t)(N - k0) * (uint32_t)(2 * D));
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(K + (size_t)k0 * D), 0, bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(V + (size_t)k0 * D), 0, bytes, 0x00020000);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const size_t at = (size_t)(i * NT + wave * 64) * 8;

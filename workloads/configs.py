@@ -84,9 +84,18 @@ def score_matrix_bytes(n: int, itemsize: int) -> int:
     return n * n * itemsize
 
 
-def naive_extra_bytes(w: Workload) -> int:
-    """HBM traffic that a three-pass attention adds on top of min_bytes: the
-    score matrix is written once and read back twice (softmax, then the
-    product with V), per head, in the storage type."""
-    item = 4 if w.dtype == "f32" else 2
-    return 3 * w.B * w.H * score_matrix_bytes(w.N, item)
+def naive_bytes(w: Workload) -> int:
+    """HBM traffic a three-pass attention needs at the least, as built here:
+    min_bytes, plus the fp32 score matrix written once and read once, plus
+    the probabilities written once and read once (2 bytes per entry; 4 for
+    bf16 storage, which keeps P as a rounded value and its remainder), over
+    the visible entries of each head (N^2, or N(N+1)/2 under the causal
+    mask).  The pages count the same round trips of the n x n matrix
+    ("Android Transformer Optimization: Attention and Mobile GPU
+    Bottlenecks", section "The Self-Attention Bottleneck Is Memory Traffic,
+    Not Compute")."""
+    if w.dtype == "f32":
+        raise ValueError("the three-pass path takes 16-bit storage only")
+    p_item = 4 if w.dtype == "bf16" else 2
+    vis = w.N * (w.N + 1) // 2 if w.causal else w.N * w.N
+    return min_bytes(w) + w.B * w.H * vis * (4 + 4 + 2 * p_item)
