@@ -66,10 +66,10 @@ class Oracle:
         lib = ctypes.CDLL(path)
         i64, vp = ctypes.c_int64, ctypes.c_void_p
         lib.fa_oracle_forward.argtypes = [vp, vp, vp, ctypes.c_int, i64, i64, i64, i64,
-                                          ctypes.c_double, ctypes.c_int, vp, vp, ctypes.c_int]
+                                          ctypes.c_double, ctypes.c_int, vp, vp, vp, ctypes.c_int]
         lib.fa_oracle_forward.restype = ctypes.c_int
         lib.fa_oracle_rows.argtypes = [vp, vp, vp, ctypes.c_int, i64, i64, i64, i64,
-                                       ctypes.c_double, ctypes.c_int, vp, vp, i64, vp,
+                                       ctypes.c_double, ctypes.c_int, vp, vp, i64, vp, vp,
                                        ctypes.c_int]
         lib.fa_oracle_rows.restype = ctypes.c_int
         for name, arg in (("f16", ctypes.c_uint16), ("bf16", ctypes.c_uint16),
@@ -90,31 +90,38 @@ class Oracle:
         return out.reshape(np.shape(bits))
 
     def forward(self, q, k, v, dtype: str, scale: float, causal: bool, nthreads: int = 0,
-                return_rowsum: bool = False):
+                return_rowsum: bool = False, return_lse: bool = False):
         """O = softmax(scale * Q K^T [+ causal mask]) V for every (b, h), in fp64.
 
         q, k, v: [B, H, N, D] storage-bit arrays.  Returns O (fp64,
         [B, H, N, D]); with return_rowsum also the sum of each P row
-        ([B, H, N]) and the number of threads used."""
+        ([B, H, N]) and the number of threads used; with return_lse (and not
+        return_rowsum) (O, lse) where lse [B, H, N] is the log-sum-exp of each
+        row of scale * Q K^T over its visible keys."""
         q, k, v = _check(q, k, v, dtype)
         B, H, N, D = q.shape
         o = np.empty((B, H, N, D), dtype=np.float64)
         rs = np.empty((B, H, N), dtype=np.float64) if return_rowsum else None
+        lse = np.empty((B, H, N), dtype=np.float64) if return_lse else None
         used = self.lib.fa_oracle_forward(q.ctypes.data, k.ctypes.data, v.ctypes.data,
                                           DTYPE_CODES[dtype], B, H, N, D, float(scale),
                                           int(bool(causal)), o.ctypes.data,
                                           rs.ctypes.data if rs is not None else None,
+                                          lse.ctypes.data if lse is not None else None,
                                           int(nthreads))
         if used < 0:
             raise RuntimeError("oracle rejected its arguments")
         if return_rowsum:
-            return o, rs, used
+            return (o, rs, used, lse) if return_lse else (o, rs, used)
+        if return_lse:
+            return o, lse
         return o
 
     def rows(self, q, k, v, dtype: str, scale: float, causal: bool, bh_idx, row_idx,
-             nthreads: int = 0, return_threads: bool = False):
+             nthreads: int = 0, return_threads: bool = False, return_lse: bool = False):
         """Selected output rows: row r is query row_idx[r] of flattened head
-        bh_idx[r] (= b*H + h).  Returns an [nrows, D] fp64 array."""
+        bh_idx[r] (= b*H + h).  Returns an [nrows, D] fp64 array (with
+        return_lse, also the rows' log-sum-exp, [nrows])."""
         q, k, v = _check(q, k, v, dtype)
         B, H, N, D = q.shape
         bh = np.ascontiguousarray(bh_idx, dtype=np.int64).reshape(-1)
@@ -126,15 +133,20 @@ class Oracle:
         bh_sorted = np.ascontiguousarray(bh[order])
         ri_sorted = np.ascontiguousarray(ri[order])
         out_sorted = np.empty((bh.size, D), dtype=np.float64)
+        lse_sorted = np.empty(bh.size, dtype=np.float64)
         used = self.lib.fa_oracle_rows(q.ctypes.data, k.ctypes.data, v.ctypes.data,
                                        DTYPE_CODES[dtype], B, H, N, D, float(scale),
                                        int(bool(causal)), bh_sorted.ctypes.data,
                                        ri_sorted.ctypes.data, bh.size, out_sorted.ctypes.data,
-                                       int(nthreads))
+                                       lse_sorted.ctypes.data, int(nthreads))
         if used < 0:
             raise RuntimeError("oracle rejected its arguments")
         out = np.empty_like(out_sorted)
         out[order] = out_sorted
+        lse = np.empty_like(lse_sorted)
+        lse[order] = lse_sorted
+        if return_lse:
+            return (out, lse, used) if return_threads else (out, lse)
         return (out, used) if return_threads else out
 
 
@@ -156,9 +168,11 @@ def decode(bits, dtype):
     return load().decode(bits, dtype)
 
 
-def forward(q, k, v, dtype, scale, causal, nthreads=0, return_rowsum=False):
-    return load().forward(q, k, v, dtype, scale, causal, nthreads, return_rowsum)
+def forward(q, k, v, dtype, scale, causal, nthreads=0, return_rowsum=False, return_lse=False):
+    return load().forward(q, k, v, dtype, scale, causal, nthreads, return_rowsum, return_lse)
 
 
-def rows(q, k, v, dtype, scale, causal, bh_idx, row_idx, nthreads=0, return_threads=False):
-    return load().rows(q, k, v, dtype, scale, causal, bh_idx, row_idx, nthreads, return_threads)
+def rows(q, k, v, dtype, scale, causal, bh_idx, row_idx, nthreads=0, return_threads=False,
+         return_lse=False):
+    return load().rows(q, k, v, dtype, scale, causal, bh_idx, row_idx, nthreads, return_threads,
+                       return_lse)

@@ -112,10 +112,14 @@ static void decode_span(const void* buf, int dtype, int64_t offset, int64_t coun
  *   qrow: D values; Kh, Vh: N x D row-major for this head.
  *   s, p: scratch rows of N doubles (the materialised S[i,:] and P[i,:]).
  *   orow: D outputs.  *psum receives sum_j P[i,j] after normalisation.
+ *   *plse receives the log-sum-exp of the row's scores, ln sum_j exp(S[i,j])
+ *   = m + ln sum_j exp(S[i,j] - m): the running maximum and denominator of
+ *   the first page's section "The Essence of FlashAttention: Reordering the
+ *   Computation" folded into one number (m + ln l).
  */
 static void attend_row(const double* qrow, const double* Kh, const double* Vh, int64_t i, int64_t N,
                        int64_t D, double scale, int causal, double* s, double* p, double* orow,
-                       double* psum) {
+                       double* psum, double* plse) {
   /* S[i, j] = scale * <Q[i,:], K[j,:]>; masked keys get -inf. */
   for (int64_t j = 0; j < N; ++j) {
     if (causal && j > i) {
@@ -141,6 +145,7 @@ static void attend_row(const double* qrow, const double* Kh, const double* Vh, i
     total += p[j];
   }
   if (psum) *psum = total;
+  if (plse) *plse = m + log(denom);
   /* O[i, :] = sum_j P[i, j] * V[j, :]. */
   for (int64_t d = 0; d < D; ++d) orow[d] = 0.0;
   for (int64_t j = 0; j < N; ++j) {
@@ -170,12 +175,13 @@ static int set_threads(int nthreads) {
 /*
  * Full forward pass.  q, k, v: [B, H, N, D] in storage type dtype.
  * o: [B, H, N, D] fp64 output.  rowsum (optional): [B, H, N], sum of each P
- * row.  Heads are processed one after another, the rows of a head in
- * parallel.  Returns the number of threads used, or -1 on bad arguments.
+ * row.  lse (optional): [B, H, N], log-sum-exp of each score row.  Heads are
+ * processed one after another, the rows of a head in parallel.  Returns the
+ * number of threads used, or -1 on bad arguments.
  */
 int fa_oracle_forward(const void* q, const void* k, const void* v, int dtype, int64_t B, int64_t H,
                       int64_t N, int64_t D, double scale, int causal, double* o, double* rowsum,
-                      int nthreads) {
+                      double* lse, int nthreads) {
   if (!valid_args(q, k, v, dtype, B, H, N, D) || !o) return -1;
   int used = set_threads(nthreads);
   if (N == 0) return used;
@@ -200,7 +206,7 @@ int fa_oracle_forward(const void* q, const void* k, const void* v, int dtype, in
 #pragma omp for schedule(dynamic, 16)
       for (int64_t i = 0; i < N; ++i) {
         attend_row(Qh + i * D, Kh, Vh, i, N, D, scale, causal, s, p, o + base + i * D,
-                   rowsum ? rowsum + bh * N + i : NULL);
+                   rowsum ? rowsum + bh * N + i : NULL, lse ? lse + bh * N + i : NULL);
       }
       free(s);
       free(p);
@@ -215,11 +221,13 @@ int fa_oracle_forward(const void* q, const void* k, const void* v, int dtype, in
 /*
  * Selected output rows only, for checks at sizes where the full pass is too
  * slow.  Row r is query row_idx[r] of flattened head bh_idx[r] (= b*H + h).
- * o_rows: [nrows, D] fp64.  Returns threads used, or -1 on bad arguments.
+ * o_rows: [nrows, D] fp64.  lse_rows (optional): [nrows], each row's
+ * log-sum-exp.  Returns threads used, or -1 on bad arguments.
  */
 int fa_oracle_rows(const void* q, const void* k, const void* v, int dtype, int64_t B, int64_t H,
                    int64_t N, int64_t D, double scale, int causal, const int64_t* bh_idx,
-                   const int64_t* row_idx, int64_t nrows, double* o_rows, int nthreads) {
+                   const int64_t* row_idx, int64_t nrows, double* o_rows, double* lse_rows,
+                   int nthreads) {
   if (!valid_args(q, k, v, dtype, B, H, N, D) || !o_rows || (nrows > 0 && (!bh_idx || !row_idx)))
     return -1;
   for (int64_t r = 0; r < nrows; ++r)
@@ -252,7 +260,8 @@ int fa_oracle_rows(const void* q, const void* k, const void* v, int dtype, int64
         cached = bh;
       }
       decode_span(q, dtype, base + row_idx[r] * D, D, qrow);
-      attend_row(qrow, Kh, Vh, row_idx[r], N, D, scale, causal, s, p, o_rows + r * D, NULL);
+      attend_row(qrow, Kh, Vh, row_idx[r], N, D, scale, causal, s, p, o_rows + r * D, NULL,
+                 lse_rows ? lse_rows + r : NULL);
     }
     free(Kh);
     free(Vh);

@@ -373,6 +373,112 @@ def check_rows_match_forward(orc):
         _close(got, full[bh, ri], 0.0, f"rows vs forward causal={causal}")
 
 
+def brute_force_lse(qf, kf, scale, causal):
+    """ln sum_j exp(scale * q_i . k_j) over the visible keys, in 40-digit
+    decimal arithmetic without the max-subtraction, one (N, D) head."""
+    getcontext().prec = 40
+    N, D = qf.shape
+    sc = Decimal(float(scale))
+    out = np.zeros(N)
+    for i in range(N):
+        tot = Decimal(0)
+        for j in range(N):
+            if causal and j > i:
+                continue
+            s = sum((Decimal(float(qf[i, d])) * Decimal(float(kf[j, d])) for d in range(D)),
+                    Decimal(0))
+            tot += (s * sc).exp()
+        out[i] = float(tot.ln())
+    return out
+
+
+def check_lse_brute_force_decimal(orc):
+    """The log-sum-exp output on tiny heads against the 40-digit evaluation."""
+    cases = [((1, 1, 1, 2), 1.0), ((1, 2, 5, 4), None), ((2, 1, 8, 4), 0.9), ((1, 1, 7, 3), -0.6)]
+    seed = 77
+    for dtype in DTYPES:
+        for causal in (False, True):
+            for shape, scale in cases:
+                seed += 1
+                q = rand_bits(shape, dtype, seed, 1.5)
+                k = rand_bits(shape, dtype, seed + 1000, 1.5)
+                v = rand_bits(shape, dtype, seed + 2000)
+                sc = scale if scale is not None else 1.0 / math.sqrt(shape[3])
+                _, lse = orc.forward(q, k, v, dtype, sc, causal, return_lse=True)
+                qf, kf = (np_decode(t, dtype) for t in (q, k))
+                for b in range(shape[0]):
+                    for h in range(shape[1]):
+                        ref = brute_force_lse(qf[b, h], kf[b, h], sc, causal)
+                        _close(lse[b, h], ref, 1e-13,
+                               f"lse brute force {dtype} causal={causal} shape={shape} head={b},{h}")
+
+
+def check_lse_closed_forms(orc):
+    """Log-sum-exp closed forms: one key gives the score itself; identical
+    keys give s + ln(visible count); a zero scale gives ln(visible count);
+    two keys give max + ln(1 + exp(-|s0 - s1|)); and torch.logsumexp of the
+    masked float64 scores (a library routine) on a ragged head."""
+    import torch
+    for dtype in DTYPES:
+        q, k, v = (rand_bits((1, 2, 1, 32), dtype, s) for s in (301, 302, 303))
+        _, lse = orc.forward(q, k, v, dtype, 0.3, False, return_lse=True)
+        qf, kf = np_decode(q, dtype), np_decode(k, dtype)
+        ref = 0.3 * np.einsum("bhnd,bhnd->bhn", qf, kf)
+        _close(lse, ref, 1e-14, f"lse one key {dtype}")
+    N = 37
+    q = rand_bits((1, 1, N, 16), "f16", 311)
+    k1 = rand_bits((1, 1, 1, 16), "f16", 312)
+    k = np.ascontiguousarray(np.broadcast_to(k1, (1, 1, N, 16)))
+    v = rand_bits((1, 1, N, 16), "f16", 313)
+    qf, kf = np_decode(q, "f16")[0, 0], np_decode(k1, "f16")[0, 0, 0]
+    for causal in (False, True):
+        cnt = np.arange(1, N + 1) if causal else np.full(N, N)
+        _, lse = orc.forward(q, k, v, "f16", 0.25, causal, return_lse=True)
+        _close(lse[0, 0], 0.25 * qf @ kf + np.log(cnt), 1e-13, f"lse identical keys causal={causal}")
+        _, lse0 = orc.forward(q, rand_bits((1, 1, N, 16), "f16", 314), v, "f16", 0.0, causal,
+                              return_lse=True)
+        _close(lse0[0, 0], np.log(cnt), 1e-14, f"lse zero scale causal={causal}")
+    q, k, v = (rand_bits((1, 1, 2, 8), "f32", s, 1.3) for s in (321, 322, 323))
+    qf, kf = np_decode(q, "f32")[0, 0], np_decode(k, "f32")[0, 0]
+    _, lse = orc.forward(q, k, v, "f32", 0.7, False, return_lse=True)
+    for i in range(2):
+        s0, s1 = 0.7 * float(qf[i] @ kf[0]), 0.7 * float(qf[i] @ kf[1])
+        ref = max(s0, s1) + math.log1p(math.exp(-abs(s0 - s1)))
+        _close(lse[0, 0, i], ref, 1e-14, f"lse two keys row {i}")
+    shape = (1, 2, 83, 64)
+    q, k, v = (rand_bits(shape, "bf16", s, 2.0) for s in (331, 332, 333))
+    qt, kt = (torch.from_numpy(np_decode(t, "bf16")) for t in (q, k))
+    for causal in (False, True):
+        s = 0.125 * torch.matmul(qt, kt.transpose(-1, -2).contiguous())
+        if causal:
+            s = s.masked_fill(torch.triu(torch.ones(83, 83, dtype=torch.bool), 1), float("-inf"))
+        ref = torch.logsumexp(s, dim=-1).numpy()
+        _, lse = orc.forward(q, k, v, "bf16", 0.125, causal, return_lse=True)
+        _close(lse, ref, 1e-12, f"lse torch.logsumexp causal={causal}")
+
+
+def check_lse_key_shift_and_rows(orc):
+    """Adding one vector u to every key shifts row i's scores, hence its
+    log-sum-exp, by scale * q_i . u; the selected-rows entry point returns the
+    same log-sum-exp as the full pass."""
+    dtype = "f32"
+    shape = (1, 1, 40, 16)
+    q = dyadic_bits(shape, dtype, 341)
+    k = dyadic_bits(shape, dtype, 342)
+    u = dyadic_bits((1, 1, 1, 16), dtype, 343)
+    v = rand_bits(shape, dtype, 344)
+    ks = np.ascontiguousarray((k + u).astype(np.float32))
+    for causal in (False, True):
+        _, a = orc.forward(q, k, v, dtype, 0.2, causal, return_lse=True)
+        _, b = orc.forward(q, ks, v, dtype, 0.2, causal, return_lse=True)
+        shift = 0.2 * (np_decode(q, dtype)[0, 0] @ np_decode(u, dtype)[0, 0, 0])
+        _close(b[0, 0] - a[0, 0], shift, 1e-12, f"lse key shift causal={causal}")
+        bh = np.zeros(10, dtype=np.int64)
+        ri = np.arange(0, 40, 4)
+        _, lr = orc.rows(q, k, v, dtype, 0.2, causal, bh, ri, return_lse=True)
+        _close(lr, a[0, 0, ri], 0.0, f"lse rows vs forward causal={causal}")
+
+
 CHECKS = [
     check_decode_known_values,
     check_decode_all_16bit_patterns,
@@ -391,4 +497,7 @@ CHECKS = [
     check_causal_prefix,
     check_head_independence,
     check_rows_match_forward,
+    check_lse_brute_force_decimal,
+    check_lse_closed_forms,
+    check_lse_key_shift_and_rows,
 ]

@@ -35,6 +35,9 @@ MUTANTS = {
     "head_offset_ignores_batch": ("const int64_t base = bh * N * D;\n    decode_span(q",
                                   "const int64_t base = (bh % H) * N * D;\n    decode_span(q"),
     "accumulator_not_reset": ("for (int64_t d = 0; d < D; ++d) orow[d] = 0.0;", ""),
+    "lse_drops_max": ("if (plse) *plse = m + log(denom);", "if (plse) *plse = log(denom);"),
+    "lse_base_two": ("if (plse) *plse = m + log(denom);", "if (plse) *plse = m + log2(denom);"),
+    "lse_of_normalised_sum": ("if (plse) *plse = m + log(denom);", "if (plse) *plse = m + log(total);"),
 }
 
 
