@@ -193,6 +193,12 @@ def main():
                          "GPU clock has left its ramp (it takes tens of ms under this load)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--heads", type=int, default=0,
+                    help="run the workload with this many heads instead (same recipe and seed); "
+                         "for the few-head cases that split-KV is for")
+    ap.add_argument("--splits", type=int, default=1,
+                    help="key ranges per query block (fa_forward_ex split-KV; 0: the library's "
+                         "suggestion for this device); 1 times fa_forward itself")
     ap.add_argument("--no-naive", action="store_true",
                     help="skip the three-pass comparison leg (16-bit storage only)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -226,6 +232,8 @@ def main():
         return
 
     w = workloads.get(args.workload)
+    if args.heads:
+        w = w.with_(H=args.heads)
     x = workloads.make_inputs(w)
     input_sha = {n: hashlib.sha256(np.ascontiguousarray(x[n]).tobytes()).hexdigest()[:16]
                  for n in "qkv"}
@@ -241,8 +249,19 @@ def main():
     cargs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), w.B, w.H, w.N, w.D,
              float(w.scale), int(w.causal), code, stream.cuda_stream)
 
+    splits = args.splits
+    if splits != 1:
+        if splits == 0:
+            splits = fa.fa_splitkv_suggest(w.B, w.H, w.N, w.D, code, w.causal)
+        ws = fa.splitkv_workspace(q, splits, w.causal)
+        fa.fa_forward_ex(q, k, v, o, None, scale=w.scale, causal=w.causal, num_splits=splits,
+                         workspace=ws, stream=stream)
+        xargs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), None, w.B, w.H, w.N, w.D,
+                 float(w.scale), int(w.causal), code, splits, ws.data_ptr(), ws.numel(),
+                 stream.cuda_stream)
+
     def step():
-        st = lib.fa_forward(*cargs)
+        st = lib.fa_forward(*cargs) if splits == 1 else lib.fa_forward_ex(*xargs)
         if st != 0:
             raise fa.FAError(st)
 
@@ -274,7 +293,9 @@ def main():
     value = flops / (ms_per_step * 1e-3) / 1e12
     # Per-launch duration of the forward kernel: the launches are
     # back-to-back on one stream, so the region time over K is the mean
-    # kernel duration plus the (small) gap between kernels.
+    # kernel duration plus the (small) gap between kernels.  With splits
+    # the step is two kernels (the ranges, then the merge) and this is
+    # their sum.
     kern_us = ms_per_step * 1e3
     achieved = flops / (kern_us * 1e-6) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
@@ -311,7 +332,8 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D,
-                   "storage": w.dtype, "causal": w.causal, "parallelism": "none (1 GPU)"},
+                   "storage": w.dtype, "causal": w.causal, "parallelism": "none (1 GPU)",
+                   "splits": splits},
         "pct_peak": round(100 * value / peak, 2),
         "roofline": {
             "bound": "mfma",

@@ -56,7 +56,8 @@ typedef enum fa_status {
   FA_ERR_SCALE = -8,          /* scale is NaN or infinite */
   FA_ERR_TOO_LARGE = -9,      /* N*D >= 2^31, or the grid would overflow */
   FA_ERR_DEVICE = -10,        /* current device is not gfx950, or no device */
-  FA_ERR_WORKSPACE = -11      /* workspace NULL, misaligned, too small or overlapping */
+  FA_ERR_WORKSPACE = -11,     /* workspace NULL, misaligned, too small or overlapping */
+  FA_ERR_SPLITS = -12         /* num_splits outside 0..64 */
 } fa_status;
 
 /*
@@ -87,6 +88,72 @@ typedef enum fa_status {
  */
 int fa_forward(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H,
                int64_t N, int64_t D, float scale, int causal, int dtype, void* stream);
+
+/*
+ * fa_forward_ex -- fa_forward with two additions beside the same tile loop:
+ *
+ * Log-sum-exp output.  The online softmax of "Android Transformer
+ * Optimization: Attention and Mobile GPU Bottlenecks", sections "The
+ * Essence of FlashAttention: Reordering the Computation" and "A Complete
+ * Tile Loop", ends each row with a running maximum m and denominator l;
+ * lse = m + ln l = ln sum_j exp(scale * q_i . k_j) over the visible keys,
+ * in natural-log units of the scaled scores.
+ *
+ * Split-KV.  Each query block's key tiles are cut into num_splits even
+ * ranges, one workgroup each, so that short or few heads still fill the
+ * device.  Each range leaves its own normalised partial O_r and lse_r in
+ * the workspace; a second kernel merges them by the same rescaling rule
+ * that the tile loop applies between tiles: with lse = ln sum_r
+ * exp(lse_r), O = sum_r exp(lse_r - lse) O_r.
+ *
+ *   q, k, v, o, B, H, N, D, scale, causal, dtype, stream
+ *                    as for fa_forward.
+ *   lse              NULL, or device pointer to B*H*N floats ([B, H, N],
+ *                    4-byte aligned, overlapping none of q, k, v, o) that
+ *                    receive each row's log-sum-exp.
+ *   num_splits       1: no split (workspace unused, may be NULL);
+ *                    2..64: that many key ranges per query block;
+ *                    0: the value fa_splitkv_suggest returns.
+ *   workspace        for num_splits != 1: device memory of the current
+ *                    device, 256-byte aligned, at least
+ *                    fa_forward_ex_workspace_bytes(...) bytes, overlapping
+ *                    none of q, k, v, o, lse.  Layout: fp32 partials
+ *                    [splits, B*H, N, D], then their log-sum-exp
+ *                    [splits, B*H, N], each on a 256-byte boundary.  Owned by
+ *                    the caller; calls that share it and overlap in time
+ *                    race.
+ *   workspace_bytes  its size.
+ *
+ * Checks as fa_forward, then FA_ERR_SPLITS, FA_ERR_ALIGN / FA_ERR_ALIAS for
+ * lse, FA_ERR_TOO_LARGE for the larger grid, FA_ERR_WORKSPACE, in that
+ * order, all before anything is enqueued.  Enqueues one kernel (two with
+ * splits: the ranges, then the merge).  O agrees with fa_forward's to the
+ * same tolerance; the ranges change the order of the arithmetic only.
+ */
+int fa_forward_ex(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                  int64_t H, int64_t N, int64_t D, float scale, int causal, int dtype,
+                  int num_splits, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * fa_forward_ex_workspace_bytes -- workspace bytes fa_forward_ex needs
+ * (0 when num_splits resolves to 1 or N == 0).  num_splits 0 resolves as
+ * fa_splitkv_suggest does (so it queries the current device).  Negative
+ * fa_status on bad arguments (FA_ERR_SPLITS, FA_ERR_DTYPE, FA_ERR_DIM,
+ * FA_ERR_UNSUPPORTED_D, FA_ERR_TOO_LARGE, FA_ERR_DEVICE).
+ */
+int64_t fa_forward_ex_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int dtype,
+                                      int causal, int num_splits);
+
+/*
+ * fa_splitkv_suggest -- key ranges per query block that fill the current
+ * device: 1 when B*H times the query blocks already occupy every resident
+ * workgroup slot, else enough ranges to do so, at most 16 and leaving each
+ * range at least 16 key tiles (shorter ranges lose more to the merge than
+ * they gain).  Returns >= 1, or a negative fa_status
+ * (FA_ERR_DTYPE, FA_ERR_DIM, FA_ERR_UNSUPPORTED_D, FA_ERR_TOO_LARGE,
+ * FA_ERR_DEVICE when no device is current).
+ */
+int fa_splitkv_suggest(int64_t B, int64_t H, int64_t N, int64_t D, int dtype, int causal);
 
 /*
  * The three-pass ("naive") attention that tiling is measured against:

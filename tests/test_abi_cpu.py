@@ -162,3 +162,86 @@ def test_naive_validation(lib, args, status):
     if status == "FA_ERR_DEVICE" and got == 0:
         pytest.skip("a gfx950 device is present; the no-device path is not reachable")
     assert fa.STATUS_NAMES[got] == status
+
+
+# ----------------------------------------- fa_forward_ex (LSE, split-KV)
+
+def _ex_ws(B, H, N, D, S):
+    if S <= 1 or N == 0:
+        return 0
+    up = lambda x: (x + 255) // 256 * 256
+    lse_off = up(S * B * H * N * D * 4)
+    return up(lse_off + S * B * H * N * 4)
+
+
+@pytest.mark.parametrize("B,H,N,D,S", [(1, 1, 64, 64, 1), (1, 1, 64, 64, 2), (2, 8, 1000, 96, 2),
+                                       (1, 32, 2048, 64, 3), (1, 1, 0, 128, 4), (3, 5, 77, 128, 64)])
+def test_ex_workspace_bytes(lib, B, H, N, D, S):
+    for dt in (0, 1, 2):
+        assert fa.fa_forward_ex_workspace_bytes(B, H, N, D, dt, False, S) == _ex_ws(B, H, N, D, S)
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(S=-1), "FA_ERR_SPLITS"),
+    (dict(S=65), "FA_ERR_SPLITS"),
+    (dict(dtype=7), "FA_ERR_DTYPE"),
+    (dict(B=0), "FA_ERR_DIM"),
+    (dict(D=80), "FA_ERR_UNSUPPORTED_D"),
+])
+def test_ex_workspace_bytes_rejects(lib, args, status):
+    kw = dict(B=1, H=1, N=64, D=64, dtype=1, S=2)
+    kw.update(args)
+    got = fa.fa_forward_ex_workspace_bytes(kw["B"], kw["H"], kw["N"], kw["D"], kw["dtype"], False, kw["S"])
+    assert fa.STATUS_NAMES[got] == status
+
+
+L_ = 0x500000  # fake lse address, clear of the tensors and the workspace
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(dtype=9), "FA_ERR_DTYPE"),
+    (dict(H=0), "FA_ERR_DIM"),
+    (dict(D=32), "FA_ERR_UNSUPPORTED_D"),
+    (dict(scale=float("-inf")), "FA_ERR_SCALE"),
+    (dict(N=0, q=0, k=0, v=0, o=0, ws=0, S=7), "FA_OK"),
+    (dict(k=0), "FA_ERR_NULL"),
+    (dict(v=C + 2), "FA_ERR_ALIGN"),
+    (dict(o=B_), "FA_ERR_ALIAS"),
+    (dict(S=-2), "FA_ERR_SPLITS"),
+    (dict(S=65), "FA_ERR_SPLITS"),
+    (dict(lse=L_ + 2), "FA_ERR_ALIGN"),
+    (dict(lse=O + 64), "FA_ERR_ALIAS"),
+    (dict(lse=A), "FA_ERR_ALIAS"),
+    (dict(ws=0), "FA_ERR_WORKSPACE"),
+    (dict(ws=W + 64), "FA_ERR_WORKSPACE"),
+    (dict(ws_bytes="short"), "FA_ERR_WORKSPACE"),
+    (dict(ws=C - 256), "FA_ERR_WORKSPACE"),
+    (dict(ws=L_ - 256), "FA_ERR_WORKSPACE"),
+    (dict(B=1 << 12, H=1 << 12, N=64, D=64, S=64, q=1 << 40, k=2 << 40, v=3 << 40, o=4 << 40,
+          lse=0, ws=5 << 40, ws_bytes=1 << 60), "FA_ERR_TOO_LARGE"),
+    (dict(S=1, ws=0, ws_bytes=0), "FA_ERR_DEVICE"),
+    (dict(), "FA_ERR_DEVICE"),
+    (dict(dtype=0), "FA_ERR_DEVICE"),
+    (dict(S=0), "FA_ERR_DEVICE"),
+])
+def test_ex_validation(lib, args, status):
+    kw = dict(q=A, k=B_, v=C, o=O, lse=L_, B=1, H=1, N=64, D=64, scale=0.125, causal=False, dtype=1,
+              S=2, ws=W)
+    kw.update(args)
+    if "ws_bytes" not in kw or kw["ws_bytes"] == "short":
+        need = _ex_ws(kw["B"], kw["H"], kw["N"], kw["D"], max(kw["S"], 1)) if kw["S"] >= 0 else 1 << 20
+        kw["ws_bytes"] = need - 1 if kw.get("ws_bytes") == "short" else need
+    got = fa.fa_forward_ex_raw(kw["q"], kw["k"], kw["v"], kw["o"], kw["lse"], kw["B"], kw["H"], kw["N"],
+                               kw["D"], kw["scale"], kw["causal"], kw["dtype"], kw["S"], kw["ws"],
+                               kw["ws_bytes"])
+    if status == "FA_ERR_DEVICE" and got == 0:
+        pytest.skip("a gfx950 device is present; the no-device path is not reachable")
+    assert fa.STATUS_NAMES[got] == status
+
+
+def test_splitkv_suggest_without_device(lib):
+    got = fa.fa_splitkv_suggest(1, 32, 2048, 64, 1, False)
+    if got >= 1:
+        pytest.skip("a device is present")
+    assert fa.STATUS_NAMES[got] == "FA_ERR_DEVICE"
+    assert fa.STATUS_NAMES[fa.fa_splitkv_suggest(1, 32, 2048, 80, 1, False)] == "FA_ERR_UNSUPPORTED_D"

@@ -14,15 +14,21 @@ from ._lib import (  # noqa: F401
     FAError,
     STATUS_NAMES,
     fa_forward,
+    fa_forward_ex,
+    fa_forward_ex_raw,
+    fa_forward_ex_workspace_bytes,
     fa_forward_raw,
     fa_naive_forward,
     fa_naive_forward_raw,
     fa_naive_workspace_bytes,
+    fa_splitkv_suggest,
     fa_status_string,
     fa_version,
     forward,
+    forward_ex,
     library_path,
     load_library,
     naive_forward,
     naive_workspace,
+    splitkv_workspace,
 )

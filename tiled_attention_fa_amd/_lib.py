@@ -22,11 +22,12 @@ STATUS_NAMES = {
     -9: "FA_ERR_TOO_LARGE",
     -10: "FA_ERR_DEVICE",
     -11: "FA_ERR_WORKSPACE",
+    -12: "FA_ERR_SPLITS",
 }
 
 # Every symbol include/fa.h declares.
-EXPORTS = ("fa_forward", "fa_naive_forward", "fa_naive_workspace_bytes", "fa_status_string",
-           "fa_version")
+EXPORTS = ("fa_forward", "fa_forward_ex", "fa_forward_ex_workspace_bytes", "fa_naive_forward",
+           "fa_naive_workspace_bytes", "fa_splitkv_suggest", "fa_status_string", "fa_version")
 
 _lib = None
 
@@ -55,6 +56,14 @@ def load_library():
     lib.fa_forward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float, ctypes.c_int,
                                ctypes.c_int, vp]
     lib.fa_forward.restype = ctypes.c_int
+    lib.fa_forward_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float, ctypes.c_int,
+                                  ctypes.c_int, ctypes.c_int, vp, i64, vp]
+    lib.fa_forward_ex.restype = ctypes.c_int
+    lib.fa_forward_ex_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                                                  ctypes.c_int]
+    lib.fa_forward_ex_workspace_bytes.restype = i64
+    lib.fa_splitkv_suggest.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
+    lib.fa_splitkv_suggest.restype = ctypes.c_int
     lib.fa_naive_forward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float, ctypes.c_int,
                                      ctypes.c_int, vp, i64, vp]
     lib.fa_naive_forward.restype = ctypes.c_int
@@ -83,6 +92,28 @@ def fa_forward_raw(q: int, k: int, v: int, o: int, B: int, H: int, N: int, D: in
     return load_library().fa_forward(q or None, k or None, v or None, o or None, int(B), int(H),
                                      int(N), int(D), float(scale), int(bool(causal)), int(dtype),
                                      stream or None)
+
+
+def fa_forward_ex_raw(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, N: int, D: int,
+                      scale: float, causal: bool, dtype: int, num_splits: int, workspace: int,
+                      workspace_bytes: int, stream: int = 0) -> int:
+    """Direct call of fa_forward_ex with integer addresses; returns the
+    status code."""
+    return load_library().fa_forward_ex(q or None, k or None, v or None, o or None, lse or None,
+                                        int(B), int(H), int(N), int(D), float(scale),
+                                        int(bool(causal)), int(dtype), int(num_splits),
+                                        workspace or None, int(workspace_bytes), stream or None)
+
+
+def fa_forward_ex_workspace_bytes(B: int, H: int, N: int, D: int, dtype: int, causal: bool,
+                                  num_splits: int) -> int:
+    return int(load_library().fa_forward_ex_workspace_bytes(int(B), int(H), int(N), int(D), int(dtype),
+                                                            int(bool(causal)), int(num_splits)))
+
+
+def fa_splitkv_suggest(B: int, H: int, N: int, D: int, dtype: int, causal: bool) -> int:
+    return int(load_library().fa_splitkv_suggest(int(B), int(H), int(N), int(D), int(dtype),
+                                                 int(bool(causal))))
 
 
 def fa_naive_workspace_bytes(B: int, H: int, N: int, dtype: int) -> int:
@@ -194,3 +225,57 @@ def naive_forward(q, k, v, scale=None, causal=False, stream=None, workspace=None
     ws = workspace if workspace is not None else naive_workspace(q)
     fa_naive_forward(q, k, v, o, ws, scale=scale, causal=causal, stream=stream)
     return o
+
+
+def splitkv_workspace(q, num_splits=0, causal=False):
+    """A uint8 device tensor big enough for fa_forward_ex on tensors shaped
+    and typed like q with this split count (0: the suggestion)."""
+    import torch
+    B, H, N, D = q.shape
+    n = fa_forward_ex_workspace_bytes(B, H, N, D, _dtype_code(q), causal, num_splits)
+    if n < 0:
+        raise FAError(n)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+
+
+def fa_forward_ex(q, k, v, o, lse=None, scale=None, causal=False, num_splits=1, workspace=None,
+                  stream=None) -> None:
+    """fa_forward_ex on torch tensors: o <- attention, lse (optional float32
+    [B, H, N] tensor) <- each row's log-sum-exp; num_splits key ranges per
+    query block (0: the suggestion), workspace a uint8 device tensor from
+    splitkv_workspace (needed unless the split count resolves to 1).
+    Enqueues and returns; raises FAError on a rejected call."""
+    import torch
+    _check_qkvo(q, k, v, o)
+    B, H, N, D = q.shape
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N)
+                            or not lse.is_contiguous() or lse.device != q.device):
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    handle = _stream_handle(stream, q.device)
+    ws_ptr, ws_bytes = (workspace.data_ptr(), workspace.numel() * workspace.element_size()) \
+        if workspace is not None else (0, 0)
+    with torch.cuda.device(q.device):
+        st = fa_forward_ex_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                               lse.data_ptr() if lse is not None else 0, B, H, N, D, scale, causal,
+                               _dtype_code(q), num_splits, ws_ptr, ws_bytes, handle)
+    if st != 0:
+        raise FAError(st)
+
+
+def forward_ex(q, k, v, scale=None, causal=False, num_splits=1, lse=False, workspace=None,
+               stream=None):
+    """O (and, with lse=True, the [B, H, N] float32 log-sum-exp) through
+    fa_forward_ex; num_splits 0 takes the suggestion.  Allocates o, the lse
+    tensor and (unless given) the workspace with torch; returns o or
+    (o, lse)."""
+    import torch
+    o = torch.empty_like(q)
+    B, H, N, _ = q.shape
+    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse else None
+    with torch.cuda.device(q.device):
+        ws = workspace if workspace is not None else splitkv_workspace(q, num_splits, causal)
+    fa_forward_ex(q, k, v, o, lse_t, scale=scale, causal=causal, num_splits=num_splits, workspace=ws,
+                  stream=stream)
+    return (o, lse_t) if lse else o

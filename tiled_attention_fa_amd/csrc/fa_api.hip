@@ -92,6 +92,53 @@ bool naive_layout(int64_t BH, int64_t N, int dtype, int64_t* p_off, int64_t* plo
   return true;
 }
 
+constexpr int kMaxSplits = 64;
+std::atomic<int> g_cus[kMaxDevices];  // CU count per device, 0 = not queried yet
+
+// CUs of the current device (cached), or a negative status.
+int current_cus() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_DEVICE;
+  int cus = g_cus[dev].load(std::memory_order_relaxed);
+  if (cus == 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+      return FA_ERR_DEVICE;
+    g_cus[dev].store(cus, std::memory_order_relaxed);
+  }
+  return cus;
+}
+
+// Key-range splits that fill the device: enough workgroups for every
+// resident slot, while each range keeps at least 16 key tiles (measured on
+// MI355X: below that the partials' round trip through memory and the merge
+// cost more than the extra workgroups gain).
+int suggest_splits(int64_t BH, int64_t N, int64_t D, int dtype, bool causal, int cus) {
+  const bool f32 = dtype == FA_F32;
+  const int64_t block_m = f32 ? fa::kF32BlockM : 32 * fa::mfma_waves((int)D, causal);
+  const int64_t per_cu = f32 ? 1 : fa::mfma_wgs_per_cu((int)D, causal);
+  const int64_t bn = f32 ? 16 : 64;
+  const int64_t total = BH * ((N + block_m - 1) / block_m);
+  const int64_t slots = (int64_t)cus * per_cu;
+  if (N == 0 || total >= slots) return 1;
+  int64_t s = slots / total;
+  const int64_t by_tiles = ((N + bn - 1) / bn) / 16;
+  if (s > by_tiles) s = by_tiles;
+  if (s > 16) s = 16;
+  return s < 1 ? 1 : (int)s;
+}
+
+// Workspace of split-KV: the fp32 partials [splits, BH, N, D], then their
+// log-sum-exp [splits, BH, N], each on a 256-byte boundary.  -1 when the
+// size does not fit in int64.
+int64_t split_layout(int64_t BH, int64_t N, int64_t D, int splits, int64_t* lse_off) {
+  *lse_off = 0;
+  if (splits <= 1 || N == 0) return 0;
+  if (BH > INT64_MAX / 8 / splits / N / (D + 1)) return -1;
+  const int64_t o_bytes = (int64_t)splits * BH * N * D * 4;
+  *lse_off = align_up(o_bytes);
+  return align_up(*lse_off + (int64_t)splits * BH * N * 4);
+}
+
 }  // namespace
 
 extern "C" {
@@ -177,6 +224,115 @@ int fa_naive_forward(const void* q, const void* k, const void* v, void* o, int64
   return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+int fa_splitkv_suggest(int64_t B, int64_t H, int64_t N, int64_t D, int dtype, int causal) {
+  if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (B < 1 || H < 1 || N < 0 || D < 1) return FA_ERR_DIM;
+  if (!head_dim_supported(D)) return FA_ERR_UNSUPPORTED_D;
+  if (B > ((int64_t)1 << 31) / H) return FA_ERR_TOO_LARGE;
+  const int cus = current_cus();
+  if (cus < 0) return cus;
+  return suggest_splits(B * H, N, D, dtype, causal != 0, cus);
+}
+
+int64_t fa_forward_ex_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int dtype, int causal,
+                                      int num_splits) {
+  if (num_splits < 0 || num_splits > kMaxSplits) return FA_ERR_SPLITS;
+  int splits = num_splits;
+  if (splits == 0) {
+    splits = fa_splitkv_suggest(B, H, N, D, dtype, causal);
+    if (splits < 0) return splits;
+  }
+  if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (B < 1 || H < 1 || N < 0 || D < 1) return FA_ERR_DIM;
+  if (!head_dim_supported(D)) return FA_ERR_UNSUPPORTED_D;
+  if (B > ((int64_t)1 << 31) / H) return FA_ERR_TOO_LARGE;
+  int64_t lse_off;
+  const int64_t bytes = split_layout(B * H, N, D, splits, &lse_off);
+  return bytes < 0 ? FA_ERR_TOO_LARGE : bytes;
+}
+
+int fa_forward_ex(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                  int64_t N, int64_t D, float scale, int causal, int dtype, int num_splits, void* workspace,
+                  int64_t workspace_bytes, void* stream) {
+  if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  int64_t BH = 0;
+  const int64_t block_m = dtype == FA_F32 ? fa::kF32BlockM : fa::kMfmaBlockM;
+  const int st = validate(q, k, v, o, B, H, N, D, scale, dtype, block_m, &BH);
+  if (st == 1) return FA_OK;
+  if (st != FA_OK) return st;
+  if (num_splits < 0 || num_splits > kMaxSplits) return FA_ERR_SPLITS;
+  const int64_t elem = dtype == FA_F32 ? 4 : 2;
+  const size_t bytes = (size_t)(BH * N * D * elem);
+  if (lse != nullptr) {
+    if ((uintptr_t)lse & 3u) return FA_ERR_ALIGN;
+    const size_t lbytes = (size_t)(BH * N * 4);
+    if (ranges_overlap(lse, lbytes, q, bytes) || ranges_overlap(lse, lbytes, k, bytes) ||
+        ranges_overlap(lse, lbytes, v, bytes) || ranges_overlap(lse, lbytes, o, bytes))
+      return FA_ERR_ALIAS;
+  }
+  int splits = num_splits;
+  if (splits == 0) {
+    const int cus = current_cus();
+    if (cus < 0) return cus;
+    splits = suggest_splits(BH, N, D, dtype, causal != 0, cus);
+  }
+  // grid: every (head, query block, range) is one workgroup
+  const int64_t qtiles = (N + block_m - 1) / block_m;
+  if (BH * splits > (((int64_t)1 << 31) - 1) / qtiles) return FA_ERR_TOO_LARGE;
+  if (BH * splits > (int64_t)UINT32_MAX / (8 * N + 512)) return FA_ERR_TOO_LARGE;
+  int64_t lse_off = 0;
+  if (splits > 1) {
+    const int64_t need = split_layout(BH, N, D, splits, &lse_off);
+    if (need < 0) return FA_ERR_TOO_LARGE;
+    if (!workspace || ((uintptr_t)workspace & (kWsAlign - 1)) || workspace_bytes < need)
+      return FA_ERR_WORKSPACE;
+    if (ranges_overlap(workspace, (size_t)need, q, bytes) || ranges_overlap(workspace, (size_t)need, k, bytes) ||
+        ranges_overlap(workspace, (size_t)need, v, bytes) || ranges_overlap(workspace, (size_t)need, o, bytes) ||
+        (lse != nullptr && ranges_overlap(workspace, (size_t)need, lse, (size_t)(BH * N * 4))))
+      return FA_ERR_WORKSPACE;
+  }
+
+  const int dev = check_device();
+  if (dev != FA_OK) return dev;
+
+  fa::Problem p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.BH = BH;
+  p.N = (int)N;
+  p.D = (int)D;
+  p.scale = scale;
+  p.causal = causal != 0;
+  p.splits = splits;
+  p.lse = splits == 1 ? lse : nullptr;
+  if (splits > 1) {
+    p.part_o = (float*)workspace;
+    p.part_lse = (float*)((char*)workspace + lse_off);
+  }
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t err;
+  switch (dtype) {
+    case FA_F16: err = fa::launch_mfma_f16(p, s); break;
+    case FA_BF16: err = fa::launch_mfma_bf16(p, s); break;
+    default: err = fa::launch_f32(p, s); break;
+  }
+  if (err == hipSuccess && splits > 1) {
+    fa::MergeProblem m;
+    m.part_o = p.part_o;
+    m.part_lse = p.part_lse;
+    m.o = o;
+    m.lse = lse;
+    m.rows = BH * N;
+    m.D = (int)D;
+    m.splits = splits;
+    m.dtype = dtype;
+    err = fa::launch_split_merge(m, s);
+  }
+  return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
@@ -191,6 +347,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_TOO_LARGE: return "problem too large (N*D must be < 2^31 and the grid must fit)";
     case FA_ERR_DEVICE: return "current HIP device is not a gfx950 (MI355X)";
     case FA_ERR_WORKSPACE: return "workspace NULL, not 256-byte aligned, too small or overlapping a tensor";
+    case FA_ERR_SPLITS: return "num_splits out of range (0 for the suggestion, else 1..64)";
     default: return "unknown status";
   }
 }

@@ -41,9 +41,13 @@ struct Args {
   float* o;
   int N;
   int num_qtiles;
-  int total_tiles;
-  double c;     // |scale| * log2(e)
-  float qsign;  // -1 when scale < 0 (exact sign flip of Q), else +1
+  int total_tiles;  // BH * num_qtiles * splits
+  double c;         // |scale| * log2(e)
+  float qsign;      // -1 when scale < 0 (exact sign flip of Q), else +1
+  int splits;       // key-range splits per query block (1: O written directly)
+  float* part_o;    // splits > 1: [splits, BH, N, D] normalised partial O
+  float* part_lse;  // splits > 1: [splits, BH, N] partial log-sum-exp
+  float* lse;       // splits == 1, optional: [BH, N] log-sum-exp
 };
 
 __device__ __forceinline__ int xcd_remap(int wg, int total) {
@@ -78,8 +82,11 @@ __global__ __launch_bounds__(kBlockM * waves_for<D>()) void fa_forward_f32_kerne
   float* Vs = tiles[wave] + BN * D;
 
   const int logical = xcd_remap(blockIdx.x, a.total_tiles);
-  const int bh = logical / a.num_qtiles;
-  int qt = logical - bh * a.num_qtiles;
+  const int per_head = a.num_qtiles * a.splits;
+  const int bh = logical / per_head;
+  const int rem = logical - bh * per_head;
+  int qt = rem / a.splits;
+  const int split = rem - qt * a.splits;
   if (CAUSAL) qt = a.num_qtiles - 1 - qt;
   const int N = a.N;
   const size_t head = (size_t)bh * (size_t)N * D;
@@ -108,7 +115,10 @@ __global__ __launch_bounds__(kBlockM * waves_for<D>()) void fa_forward_f32_kerne
 
   const int kv_end = CAUSAL ? min(N, qt * kBlockM + kBlockM) : N;
   const int ntiles = (kv_end + BN - 1) / BN;
-  for (int t = wave; t < ntiles; t += kWaves) {
+  // this workgroup's share of the key tiles (all of them when splits == 1)
+  const int t_lo = split * ntiles / a.splits;
+  const int t_hi = (split + 1) * ntiles / a.splits;
+  for (int t = t_lo + wave; t < t_hi; t += kWaves) {
     const int k0 = t * BN;
     // this wave's tile: 16 rows of K and of V, 16 bytes per lane per load
     for (int idx = lane; idx < BN * D / 4; idx += 64) {
@@ -206,7 +216,12 @@ __global__ __launch_bounds__(kBlockM * waves_for<D>()) void fa_forward_f32_kerne
     L += f[w] * l_part[w][lane];
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
+  // log-sum-exp of the row's scaled scores, ln 2 * (M*c + log2 L); -inf
+  // when this key range held no key of the row
+  const float lse = L > 0.f ? (float)((M * cd + (double)__builtin_amdgcn_logf(L)) * 0.6931471805599453) : -INFINITY;
   constexpr int DQ = D / kWaves;  // columns merged by this wave
+  const bool part = a.splits > 1;
+  float* dst = part ? a.part_o + ((size_t)split * (a.total_tiles / per_head) * N + (size_t)bh * N) * D : nullptr;
   if (qrow < N) {
 #pragma unroll
     for (int d = 0; d < DQ; d += 4) {
@@ -217,7 +232,16 @@ __global__ __launch_bounds__(kBlockM * waves_for<D>()) void fa_forward_f32_kerne
         const f32x4 x = *(const f32x4*)(tiles[w] + lane * D + col);
         out += f[w] * x;
       }
-      *(f32x4*)(O + (size_t)qrow * D + col) = out * inv;
+      if (part)
+        *(f32x4*)(dst + (size_t)qrow * D + col) = out * inv;
+      else
+        *(f32x4*)(O + (size_t)qrow * D + col) = out * inv;
+    }
+    if (wave == 0) {
+      if (part)
+        a.part_lse[((size_t)split * (a.total_tiles / per_head) + bh) * N + qrow] = lse;
+      else if (a.lse != nullptr)
+        a.lse[(size_t)bh * N + qrow] = lse;
     }
   }
 }
@@ -233,9 +257,13 @@ hipError_t launch_f32(const Problem& p, hipStream_t stream) {
   a.o = (float*)p.o;
   a.N = p.N;
   a.num_qtiles = (p.N + kBlockM - 1) / kBlockM;
-  a.total_tiles = (int)(p.BH * a.num_qtiles);
+  a.splits = p.splits;
+  a.total_tiles = (int)(p.BH * a.num_qtiles * a.splits);
   a.c = __builtin_fabs((double)p.scale) * 1.4426950408889634;
   a.qsign = p.scale < 0.f ? -1.f : 1.f;
+  a.part_o = p.part_o;
+  a.part_lse = p.part_lse;
+  a.lse = p.lse;
   void (*kern)(Args) = nullptr;
   int waves = 0;
   if (p.D == 64) {

@@ -17,7 +17,39 @@ struct Problem {
   int D;
   float scale;
   bool causal;
+  // Key-range split (split-KV): with splits > 1 each query block's key
+  // tiles are cut into `splits` ranges, one workgroup each, and the kernel
+  // writes normalised fp32 partials part_o [splits, BH, N, D] and their
+  // log-sum-exp part_lse [splits, BH, N] for the merge kernel instead of o.
+  int splits = 1;
+  float* part_o = nullptr;
+  float* part_lse = nullptr;
+  // Optional [BH, N] log-sum-exp of each row's scaled scores (splits == 1;
+  // with splits > 1 the merge kernel writes it).
+  float* lse = nullptr;
 };
+
+// Merge of split-KV partials: O = sum_s exp(lse_s - lse) O_s with
+// lse = ln sum_s exp(lse_s), O in the storage type (dtype as in fa.h).
+struct MergeProblem {
+  const float* part_o;
+  const float* part_lse;
+  void* o;
+  float* lse;  // optional
+  int64_t rows;  // BH * N
+  int D;
+  int splits;
+  int dtype;
+};
+
+// Workgroup shape of the matrix-core kernel per head dimension and mask:
+// waves per workgroup (32 query rows each) and workgroups resident per CU.
+// Eight waves (256 rows, two waves per SIMD in lockstep) where rows are long
+// and uniform; four waves for causal D = 64, where the finer grain balances
+// the triangle better (two workgroups per CU), and for D = 96 (one wave per
+// SIMD: 128-element LDS rows leave room for one workgroup per CU).
+constexpr int mfma_waves(int D, bool causal) { return D == 96 || (D == 64 && causal) ? 4 : 8; }
+constexpr int mfma_wgs_per_cu(int D, bool causal) { return D == 64 && causal ? 2 : 1; }
 
 // One validated three-pass problem: the forward problem plus the caller's
 // workspace, cut into the fp32 score matrix S [BH, N, N] and the
@@ -50,6 +82,7 @@ constexpr int kF32BlockM = 64;
 hipError_t launch_mfma_f16(const Problem& p, hipStream_t stream);
 hipError_t launch_mfma_bf16(const Problem& p, hipStream_t stream);
 hipError_t launch_f32(const Problem& p, hipStream_t stream);
+hipError_t launch_split_merge(const MergeProblem& p, hipStream_t stream);
 hipError_t launch_naive_f16(const NaiveProblem& p, hipStream_t stream);
 hipError_t launch_naive_bf16(const NaiveProblem& p, hipStream_t stream);
 

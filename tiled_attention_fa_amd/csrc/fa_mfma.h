@@ -90,7 +90,11 @@ struct Args {
   uint16_t* o;
   int N;
   int num_qtiles;   // ceil(N / BM)
-  int total_tiles;  // BH * num_qtiles
+  int total_tiles;  // BH * num_qtiles * splits
+  int splits;       // key-range splits per query block (1: O written directly)
+  float* part_o;    // splits > 1: [splits, BH, N, D] fp32 partial O (normalised)
+  float* part_lse;  // splits > 1: [splits, BH, N] partial log-sum-exp
+  float* lse;       // splits == 1, optional: [BH, N] log-sum-exp of the scaled scores
   float c;          // |scale| * log2(e)
   uint32_t qxor;    // 0x80008000 flips the sign of both halves when scale < 0
 };
@@ -261,8 +265,11 @@ void fa_forward_kernel(Args a) {
   const int hi = lane >> 5;
 
   const int logical = xcd_remap(blockIdx.x, a.total_tiles);
-  const int bh = logical / a.num_qtiles;
-  int qt = logical - bh * a.num_qtiles;
+  const int per_head = a.num_qtiles * a.splits;
+  const int bh = logical / per_head;
+  const int rem = logical - bh * per_head;
+  int qt = rem / a.splits;
+  const int split = rem - qt * a.splits;
   if (CAUSAL) qt = a.num_qtiles - 1 - qt;  // longest rows first
   const int N = a.N;
   const size_t head = (size_t)bh * (size_t)N * D;
@@ -293,6 +300,10 @@ void fa_forward_kernel(Args a) {
 
   const int kv_end = CAUSAL ? min(N, qt * BM + BM) : N;
   const int ntiles = (kv_end + BN - 1) / BN;
+  // This workgroup's share of the key tiles: an even cut of [0, ntiles)
+  // into `splits` ranges (the whole range when splits == 1).
+  const int t_lo = split * ntiles / a.splits;
+  const int t_hi = (split + 1) * ntiles / a.splits;
 
   // Direct global -> LDS loads of tile t, through a buffer resource whose
   // range starts at the tile's first key and ends at key N, so rows past N
@@ -362,8 +373,8 @@ void fa_forward_kernel(Args a) {
   const int tr_chunk_lo = (2 * (grp & 1) + ((gl & 3) >> 1)) ^ v_swz(tr_row);
   const int tr_byte = 8 * (gl & 1);
 
-  auto live = [&](int t) {  // tile t exists and holds keys this wave sees
-    return t < ntiles && (!CAUSAL || t * BN <= q0 + 31);
+  auto live = [&](int t) {  // tile t is in range and holds keys this wave sees
+    return t < t_hi && (!CAUSAL || t * BN <= q0 + 31);
   };
   auto is_edge = [&](int t) {  // tile t needs the ragged / causal masks
     return (t * BN + BN > N) || (CAUSAL && (t * BN + BN - 1 > q0));
@@ -464,12 +475,16 @@ void fa_forward_kernel(Args a) {
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
-  tile_load(0, kbuf(I0{}), vbuf(I0{}));
-  if (ntiles > 1) tile_load(1, kbuf(I1{}), vbuf(I1{}));
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  __syncthreads();
   f32x16 sA[2], sB[2];
-  qk(kbuf(I0{}), sA);  // tile 0 holds key 0, which every query sees
+  if (t_lo < t_hi) {
+    tile_load(t_lo, kbuf(I0{}), vbuf(I0{}));
+    if (t_lo + 1 < t_hi) tile_load(t_lo + 1, kbuf(I1{}), vbuf(I1{}));
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    // the first tile of the range holds the first key that any row of the
+    // range sees (a causal row sees a prefix of the keys)
+    qk(kbuf(I0{}), sA);
+  }
   // Step t (t % 4 == J): pass the barrier (tile t+1, whose loads went out
   // in step t-1, is then visible, and every wave is done with step t-1);
   // issue the loads of tile t+2 into slot (t+2) % 4, last read in step
@@ -484,7 +499,7 @@ void fa_forward_kernel(Args a) {
     // transpose reads below passes a wait for the loads of step t-1
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile t+1 has landed
     __syncthreads();
-    if (t + 2 < ntiles) tile_load(t + 2, kbuf(Pre2{}), vbuf(Pre2{}));
+    if (t + 2 < t_hi) tile_load(t + 2, kbuf(Pre2{}), vbuf(Pre2{}));
     if (live(t)) {
       if (is_edge(t)) {  // ragged / causal masks
         const int k0 = t * BN;
@@ -496,20 +511,20 @@ void fa_forward_kernel(Args a) {
             if (key >= N || (CAUSAL && key > qrow)) sc[kb][e] = -INFINITY;
           }
       }
-      tile_body(kbuf(Next{}), vbuf(J), sc, sn, t == 0);
+      tile_body(kbuf(Next{}), vbuf(J), sc, sn, t == t_lo);
     }
   };
   // The guards nest so that step t+2 is only reached through step t+1 (and
   // its wait for the loads of step t); with flat guards the compiler sees a
   // path that skips it and makes the transpose reads of step t+2 wait for
   // those loads.
-  for (int t = 0; t < ntiles; t += 4) {
+  for (int t = t_lo; t < t_hi; t += 4) {
     step(t, I0{}, sA, sB);
-    if (t + 1 < ntiles) {
+    if (t + 1 < t_hi) {
       step(t + 1, I1{}, sB, sA);
-      if (t + 2 < ntiles) {
+      if (t + 2 < t_hi) {
         step(t + 2, I2{}, sA, sB);
-        if (t + 3 < ntiles) step(t + 3, I3{}, sB, sA);
+        if (t + 3 < t_hi) step(t + 3, I3{}, sB, sA);
       }
     }
   }
@@ -517,6 +532,26 @@ void fa_forward_kernel(Args a) {
   // Epilogue: divide by the row's denominator once, round, store.
   const float l = half_sum((lp[0] + lp[1]) + (lp[2] + lp[3]));
   const float inv = l > 0.f ? 1.f / l : 0.f;
+  // log-sum-exp of the scaled scores: ln(sum_j exp(scale*s_j)) =
+  // ln 2 * (m*c + log2 l); -inf when the range held no key of the row
+  const float lse = l > 0.f ? (mc + __builtin_amdgcn_logf(l)) * 0.69314718055994531f : -INFINITY;
+  if (a.splits > 1) {
+    if (qrow < N) {
+      const size_t row = ((size_t)split * (a.total_tiles / per_head) + bh) * N + qrow;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = 32 * db + 8 * g + 4 * hi;
+          const float4 out = {oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv, oacc[db][4 * g + 2] * inv,
+                              oacc[db][4 * g + 3] * inv};
+          *(float4*)(a.part_o + row * D + d0) = out;
+        }
+      if (hi == 0) a.part_lse[row] = lse;
+    }
+    return;
+  }
+  if (a.lse != nullptr && qrow < N && hi == 0) a.lse[(size_t)bh * N + qrow] = lse;
   if (qrow < N) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -536,7 +571,7 @@ hipError_t launch_one(const Args& base, int64_t BH, hipStream_t stream) {
   using S = Shape<D, NW>;
   Args a = base;
   a.num_qtiles = (a.N + S::BM - 1) / S::BM;
-  a.total_tiles = (int)(BH * a.num_qtiles);
+  a.total_tiles = (int)(BH * a.num_qtiles * a.splits);
   void* args[] = {&a};
   return hipLaunchKernel((const void*)fa_forward_kernel<T, D, CAUSAL, SPLIT_P, NW, OCC>,
                          dim3(a.total_tiles), dim3(S::NT), args, 0, stream);
@@ -551,6 +586,10 @@ inline Args make_args(const Problem& p) {
   a.N = p.N;
   a.num_qtiles = 0;
   a.total_tiles = 0;
+  a.splits = p.splits;
+  a.part_o = p.part_o;
+  a.part_lse = p.part_lse;
+  a.lse = p.lse;
   // A zero (or vanishing) scale becomes 2^-120: the weights stay uniform to
   // within 1e-6 for any finite score, and masked scores (-inf) still give
   // exp2(-inf) = 0 without a special case.
@@ -559,24 +598,21 @@ inline Args make_args(const Problem& p) {
   return a;
 }
 
-// Workgroup shape per head dimension and mask (measured on MI355X): eight
-// waves (256 query rows, two waves per SIMD in lockstep) where rows are
-// long and uniform; four waves (128 rows) for causal D = 64, where the
-// finer grain balances the triangle better, and for D = 96 (one wave per
-// SIMD: 128-element LDS rows leave room for one workgroup per CU).
+// Workgroup shape per head dimension and mask: mfma_waves (measured on
+// MI355X).  D = 64 causal runs two workgroups per CU (waves_per_eu 2).
 template <typename T, bool SPLIT_P>
 hipError_t launch(const Problem& p, hipStream_t stream) {
   const Args a = make_args(p);
   switch (p.D) {
     case 64:
-      return p.causal ? launch_one<T, 64, true, SPLIT_P, 4, 2>(a, p.BH, stream)
-                      : launch_one<T, 64, false, SPLIT_P, 8, 1>(a, p.BH, stream);
+      return p.causal ? launch_one<T, 64, true, SPLIT_P, mfma_waves(64, true), 2>(a, p.BH, stream)
+                      : launch_one<T, 64, false, SPLIT_P, mfma_waves(64, false), 1>(a, p.BH, stream);
     case 96:
-      return p.causal ? launch_one<T, 96, true, SPLIT_P, 4, 1>(a, p.BH, stream)
-                      : launch_one<T, 96, false, SPLIT_P, 4, 1>(a, p.BH, stream);
+      return p.causal ? launch_one<T, 96, true, SPLIT_P, mfma_waves(96, true), 1>(a, p.BH, stream)
+                      : launch_one<T, 96, false, SPLIT_P, mfma_waves(96, false), 1>(a, p.BH, stream);
     case 128:
-      return p.causal ? launch_one<T, 128, true, SPLIT_P, 8, 1>(a, p.BH, stream)
-                      : launch_one<T, 128, false, SPLIT_P, 8, 1>(a, p.BH, stream);
+      return p.causal ? launch_one<T, 128, true, SPLIT_P, mfma_waves(128, true), 1>(a, p.BH, stream)
+                      : launch_one<T, 128, false, SPLIT_P, mfma_waves(128, false), 1>(a, p.BH, stream);
     default:
       return hipErrorInvalidValue;
   }
