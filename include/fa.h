@@ -57,7 +57,8 @@ typedef enum fa_status {
   FA_ERR_TOO_LARGE = -9,      /* N*D >= 2^31, or the grid would overflow */
   FA_ERR_DEVICE = -10,        /* current device is not gfx950, or no device */
   FA_ERR_WORKSPACE = -11,     /* workspace NULL, misaligned, too small or overlapping */
-  FA_ERR_SPLITS = -12         /* num_splits outside 0..64 */
+  FA_ERR_SPLITS = -12,        /* num_splits outside 0..64 */
+  FA_ERR_STRIDE = -13         /* negative strides, rows shorter than D, overlapping o rows */
 } fa_status;
 
 /*
@@ -88,6 +89,38 @@ typedef enum fa_status {
  */
 int fa_forward(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H,
                int64_t N, int64_t D, float scale, int causal, int dtype, void* stream);
+
+/*
+ * fa_forward_strided -- fa_forward on tensors laid out by strides, with
+ * grouped key/value heads.  The operation is fa_forward's, per (b, h), with
+ * query head h attending to key/value head h / (H / H_kv): H_kv == H is
+ * ordinary multi-head attention, 1 < H_kv < H grouped-query attention,
+ * H_kv == 1 multi-query attention (the sharing of K/V heads is not on the
+ * pages; it is how LLM layers lay out the same computation).
+ *
+ *   q, o        device pointers, H heads: element (b, h, n, d) at
+ *               base[b*s[0] + h*s[1] + n*s[2] + d] with s = q_strides /
+ *               o_strides (host arrays of 3 int64, in elements).
+ *   k, v        the same with H_kv heads and k_strides / v_strides.
+ *               Dense [B, H, N, D] is {H*N*D, N*D, D}; the [B, N, H, D]
+ *               layout of many LLM stacks is {N*H*D, D, H*D}.
+ *   B, H, H_kv  batch, query heads, key/value heads (H % H_kv == 0).
+ *   N, D, scale, causal, dtype, stream   as for fa_forward.
+ *
+ * Requirements, checked in this order after fa_forward's dtype, size, head
+ * dimension, scale and N == 0 checks: no NULL pointer (FA_ERR_NULL);
+ * strides >= 0 (FA_ERR_STRIDE); pointers 16-byte aligned and every stride a
+ * multiple of 16 bytes (FA_ERR_ALIGN); every row stride >= D, and the
+ * (b, h, n) rows of o pairwise disjoint (FA_ERR_STRIDE); N*D < 2^31 and
+ * max(N, 64) row strides below 2^32 bytes for every tensor (FA_ERR_TOO_LARGE);
+ * the span of o overlapping none of the spans of q, k, v (FA_ERR_ALIAS);
+ * the device (FA_ERR_DEVICE).  Inputs may overlap one another.
+ * Asynchronous, one kernel, allocates nothing.
+ */
+int fa_forward_strided(const void* q, const int64_t* q_strides, const void* k,
+                       const int64_t* k_strides, const void* v, const int64_t* v_strides, void* o,
+                       const int64_t* o_strides, int64_t B, int64_t H, int64_t H_kv, int64_t N,
+                       int64_t D, float scale, int causal, int dtype, void* stream);
 
 /*
  * fa_forward_ex -- fa_forward with two additions beside the same tile loop:

@@ -245,3 +245,50 @@ def test_splitkv_suggest_without_device(lib):
         pytest.skip("a device is present")
     assert fa.STATUS_NAMES[got] == "FA_ERR_DEVICE"
     assert fa.STATUS_NAMES[fa.fa_splitkv_suggest(1, 32, 2048, 80, 1, False)] == "FA_ERR_UNSUPPORTED_D"
+
+
+# ------------------------------------------------------ fa_forward_strided
+
+DENSE = (4 * 64 * 64, 64 * 64, 64)          # [B, H=4, N=64, D=64]
+BNHD = (64 * 4 * 64, 64, 4 * 64)            # [B, N, H=4, D]
+KV2 = (2 * 64 * 64, 64 * 64, 64)            # [B, H_kv=2, N, D]
+BIG = 1 << 24                               # spacing of the fake bases
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(dtype=3), "FA_ERR_DTYPE"),
+    (dict(Hkv=3), "FA_ERR_DIM"),
+    (dict(Hkv=0), "FA_ERR_DIM"),
+    (dict(D=48), "FA_ERR_UNSUPPORTED_D"),
+    (dict(scale=float("nan")), "FA_ERR_SCALE"),
+    (dict(N=0, q=0, qs=None), "FA_OK"),
+    (dict(qs=None), "FA_ERR_NULL"),
+    (dict(v=0), "FA_ERR_NULL"),
+    (dict(ks=(KV2[0], -64, 64)), "FA_ERR_STRIDE"),
+    (dict(q=BIG + 8), "FA_ERR_ALIGN"),
+    (dict(vs=(KV2[0], KV2[1], 68)), "FA_ERR_ALIGN"),
+    (dict(qs=(DENSE[0], DENSE[1], 56)), "FA_ERR_STRIDE"),
+    (dict(os=(DENSE[0], 64, 64)), "FA_ERR_STRIDE"),
+    (dict(os=(0, DENSE[1], 64), B=2), "FA_ERR_STRIDE"),
+    (dict(os=BNHD), "FA_ERR_DEVICE"),
+    (dict(os=(DENSE[0], 64 * 64 * 2, 128)), "FA_ERR_DEVICE"),
+    (dict(ks=(0, 0, 64)), "FA_ERR_DEVICE"),
+    (dict(ks=(KV2[0], KV2[1], 1 << 26)), "FA_ERR_TOO_LARGE"),
+    (dict(N=1 << 25, H=1, Hkv=1, qs=(64 << 25, 64 << 25, 64), ks=(64 << 25, 64 << 25, 64),
+          vs=(64 << 25, 64 << 25, 64), os=(64 << 25, 64 << 25, 64), q=1 << 40, k=2 << 40, v=3 << 40,
+          o=4 << 40), "FA_ERR_TOO_LARGE"),
+    (dict(o=1 * BIG + 4096), "FA_ERR_ALIAS"),
+    (dict(o=3 * BIG - 1024, os=BNHD), "FA_ERR_ALIAS"),
+    (dict(), "FA_ERR_DEVICE"),
+    (dict(dtype=0), "FA_ERR_DEVICE"),
+])
+def test_strided_validation(lib, args, status):
+    kw = dict(q=1 * BIG, k=2 * BIG, v=3 * BIG, o=4 * BIG, qs=DENSE, ks=KV2, vs=KV2, os=DENSE,
+              B=1, H=4, Hkv=2, N=64, D=64, scale=0.125, causal=False, dtype=1)
+    kw.update(args)
+    got = fa.fa_forward_strided_raw(kw["q"], kw["qs"], kw["k"], kw["ks"], kw["v"], kw["vs"], kw["o"],
+                                    kw["os"], kw["B"], kw["H"], kw["Hkv"], kw["N"], kw["D"],
+                                    kw["scale"], kw["causal"], kw["dtype"])
+    if status == "FA_ERR_DEVICE" and got == 0:
+        pytest.skip("a gfx950 device is present; the no-device path is not reachable")
+    assert fa.STATUS_NAMES[got] == status

@@ -18,6 +18,8 @@ from ._lib import (  # noqa: F401
     fa_forward_ex_raw,
     fa_forward_ex_workspace_bytes,
     fa_forward_raw,
+    fa_forward_strided,
+    fa_forward_strided_raw,
     fa_naive_forward,
     fa_naive_forward_raw,
     fa_naive_workspace_bytes,

@@ -23,11 +23,13 @@ STATUS_NAMES = {
     -10: "FA_ERR_DEVICE",
     -11: "FA_ERR_WORKSPACE",
     -12: "FA_ERR_SPLITS",
+    -13: "FA_ERR_STRIDE",
 }
 
 # Every symbol include/fa.h declares.
-EXPORTS = ("fa_forward", "fa_forward_ex", "fa_forward_ex_workspace_bytes", "fa_naive_forward",
-           "fa_naive_workspace_bytes", "fa_splitkv_suggest", "fa_status_string", "fa_version")
+EXPORTS = ("fa_forward", "fa_forward_ex", "fa_forward_ex_workspace_bytes", "fa_forward_strided",
+           "fa_naive_forward", "fa_naive_workspace_bytes", "fa_splitkv_suggest", "fa_status_string",
+           "fa_version")
 
 _lib = None
 
@@ -56,6 +58,9 @@ def load_library():
     lib.fa_forward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float, ctypes.c_int,
                                ctypes.c_int, vp]
     lib.fa_forward.restype = ctypes.c_int
+    lib.fa_forward_strided.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                       ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
+    lib.fa_forward_strided.restype = ctypes.c_int
     lib.fa_forward_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float, ctypes.c_int,
                                   ctypes.c_int, ctypes.c_int, vp, i64, vp]
     lib.fa_forward_ex.restype = ctypes.c_int
@@ -92,6 +97,19 @@ def fa_forward_raw(q: int, k: int, v: int, o: int, B: int, H: int, N: int, D: in
     return load_library().fa_forward(q or None, k or None, v or None, o or None, int(B), int(H),
                                      int(N), int(D), float(scale), int(bool(causal)), int(dtype),
                                      stream or None)
+
+
+def fa_forward_strided_raw(q: int, q_strides, k: int, k_strides, v: int, v_strides, o: int, o_strides,
+                           B: int, H: int, H_kv: int, N: int, D: int, scale: float, causal: bool,
+                           dtype: int, stream: int = 0) -> int:
+    """Direct call of fa_forward_strided with integer addresses and stride
+    triples (or None); returns the status code."""
+    def arr(s):
+        return None if s is None else (ctypes.c_int64 * 3)(*[int(x) for x in s])
+    return load_library().fa_forward_strided(q or None, arr(q_strides), k or None, arr(k_strides),
+                                             v or None, arr(v_strides), o or None, arr(o_strides),
+                                             int(B), int(H), int(H_kv), int(N), int(D), float(scale),
+                                             int(bool(causal)), int(dtype), stream or None)
 
 
 def fa_forward_ex_raw(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, N: int, D: int,
@@ -279,3 +297,35 @@ def forward_ex(q, k, v, scale=None, causal=False, num_splits=1, lse=False, works
     fa_forward_ex(q, k, v, o, lse_t, scale=scale, causal=causal, num_splits=num_splits, workspace=ws,
                   stream=stream)
     return (o, lse_t) if lse else o
+
+
+def fa_forward_strided(q, k, v, o, scale=None, causal=False, stream=None) -> None:
+    """o <- attention for torch tensors of any strides with a contiguous last
+    dimension: q and o [B, H, N, D], k and v [B, H_kv, N, D] with H_kv
+    dividing H (grouped / multi-query heads).  A [B, N, H, D] tensor x is
+    passed as x.transpose(1, 2).  Enqueues and returns; raises FAError on a
+    rejected call."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-d, got shape {tuple(t.shape)}")
+        if t.stride(3) != 1:
+            raise ValueError(f"{name} must have a contiguous last dimension")
+        if t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{name} must match q in dtype and device")
+    B, H, N, D = q.shape
+    Hk = k.shape[1]
+    if tuple(o.shape) != (B, H, N, D) or tuple(k.shape) != (B, Hk, N, D) or tuple(v.shape) != (B, Hk, N, D):
+        raise ValueError("shapes must be q, o: [B, H, N, D] and k, v: [B, H_kv, N, D]")
+    if q.device.type != "cuda":
+        raise ValueError("tensors must be on a HIP device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    handle = _stream_handle(stream, q.device)
+    st = lambda t: t.stride()[:3]
+    with torch.cuda.device(q.device):
+        r = fa_forward_strided_raw(q.data_ptr(), st(q), k.data_ptr(), st(k), v.data_ptr(), st(v),
+                                   o.data_ptr(), st(o), B, H, Hk, N, D, scale, causal, _dtype_code(q),
+                                   handle)
+    if r != 0:
+        raise FAError(r)

@@ -92,6 +92,67 @@ bool naive_layout(int64_t BH, int64_t N, int dtype, int64_t* p_off, int64_t* plo
   return true;
 }
 
+fa::Problem dense_problem(const void* q, const void* k, const void* v, void* o, int64_t H, int64_t BH,
+                          int64_t N, int64_t D, float scale, int causal) {
+  fa::Problem p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.BH = BH;
+  p.N = (int)N;
+  p.D = (int)D;
+  p.scale = scale;
+  p.causal = causal != 0;
+  p.H = (int)H;
+  p.group = 1;
+  p.lq = p.lk = p.lv = p.lo = fa::dense_layout(H, N, D);
+  return p;
+}
+
+hipError_t launch_kernel(const fa::Problem& p, int dtype, hipStream_t s) {
+  switch (dtype) {
+    case FA_F16: return fa::launch_mfma_f16(p, s);
+    case FA_BF16: return fa::launch_mfma_bf16(p, s);
+    default: return fa::launch_f32(p, s);
+  }
+}
+
+int launch_forward(const fa::Problem& p, int dtype, hipStream_t s) {
+  return launch_kernel(p, dtype, s) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+// Elements from a tensor's base to one past its last element, for the
+// (b, h, n) extents and strides given (d contiguous, D wide); -1 when that
+// does not fit in int64.
+int64_t extent_elems(const int64_t* st, int64_t B, int64_t Hx, int64_t N, int64_t D) {
+  const __int128 e = (__int128)(B - 1) * st[0] + (__int128)(Hx - 1) * st[1] + (__int128)(N - 1) * st[2] + D;
+  return e > (__int128)(INT64_MAX / 8) ? -1 : (int64_t)e;
+}
+
+// No two (b, h, n) rows of a written tensor share an element: with the
+// dimensions of more than one entry ordered by stride, each stride reaches
+// past everything the smaller ones span.
+bool rows_disjoint(const int64_t* st, int64_t B, int64_t Hx, int64_t N, int64_t D) {
+  int64_t s[3] = {st[0], st[1], st[2]}, c[3] = {B, Hx, N};
+  for (int i = 0; i < 3; ++i)
+    for (int j = i + 1; j < 3; ++j)
+      if (s[j] < s[i]) {
+        const int64_t ts = s[i], tc = c[i];
+        s[i] = s[j];
+        c[i] = c[j];
+        s[j] = ts;
+        c[j] = tc;
+      }
+  __int128 span = D;  // elements spanned by the dimensions placed so far
+  for (int i = 0; i < 3; ++i) {
+    if (c[i] <= 1) continue;
+    if ((__int128)s[i] < span) return false;
+    span += (__int128)s[i] * (c[i] - 1);
+  }
+  return true;
+}
+
 constexpr int kMaxSplits = 64;
 std::atomic<int> g_cus[kMaxDevices];  // CU count per device, 0 = not queried yet
 
@@ -155,24 +216,8 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, int64_t B, 
   const int dev = check_device();
   if (dev != FA_OK) return dev;
 
-  fa::Problem p;
-  p.q = q;
-  p.k = k;
-  p.v = v;
-  p.o = o;
-  p.BH = BH;
-  p.N = (int)N;
-  p.D = (int)D;
-  p.scale = scale;
-  p.causal = causal != 0;
-  hipStream_t s = (hipStream_t)stream;
-  hipError_t err;
-  switch (dtype) {
-    case FA_F16: err = fa::launch_mfma_f16(p, s); break;
-    case FA_BF16: err = fa::launch_mfma_bf16(p, s); break;
-    default: err = fa::launch_f32(p, s); break;
-  }
-  return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+  fa::Problem p = dense_problem(q, k, v, o, H, BH, N, D, scale, causal);
+  return launch_forward(p, dtype, (hipStream_t)stream);
 }
 
 int64_t fa_naive_workspace_bytes(int64_t B, int64_t H, int64_t N, int dtype) {
@@ -295,16 +340,7 @@ int fa_forward_ex(const void* q, const void* k, const void* v, void* o, float* l
   const int dev = check_device();
   if (dev != FA_OK) return dev;
 
-  fa::Problem p;
-  p.q = q;
-  p.k = k;
-  p.v = v;
-  p.o = o;
-  p.BH = BH;
-  p.N = (int)N;
-  p.D = (int)D;
-  p.scale = scale;
-  p.causal = causal != 0;
+  fa::Problem p = dense_problem(q, k, v, o, H, BH, N, D, scale, causal);
   p.splits = splits;
   p.lse = splits == 1 ? lse : nullptr;
   if (splits > 1) {
@@ -312,12 +348,7 @@ int fa_forward_ex(const void* q, const void* k, const void* v, void* o, float* l
     p.part_lse = (float*)((char*)workspace + lse_off);
   }
   hipStream_t s = (hipStream_t)stream;
-  hipError_t err;
-  switch (dtype) {
-    case FA_F16: err = fa::launch_mfma_f16(p, s); break;
-    case FA_BF16: err = fa::launch_mfma_bf16(p, s); break;
-    default: err = fa::launch_f32(p, s); break;
-  }
+  hipError_t err = launch_kernel(p, dtype, s);
   if (err == hipSuccess && splits > 1) {
     fa::MergeProblem m;
     m.part_o = p.part_o;
@@ -331,6 +362,60 @@ int fa_forward_ex(const void* q, const void* k, const void* v, void* o, float* l
     err = fa::launch_split_merge(m, s);
   }
   return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_forward_strided(const void* q, const int64_t* q_strides, const void* k, const int64_t* k_strides,
+                       const void* v, const int64_t* v_strides, void* o, const int64_t* o_strides, int64_t B,
+                       int64_t H, int64_t H_kv, int64_t N, int64_t D, float scale, int causal, int dtype,
+                       void* stream) {
+  if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (B < 1 || H < 1 || H_kv < 1 || N < 0 || D < 1 || H % H_kv != 0) return FA_ERR_DIM;
+  if (!head_dim_supported(D)) return FA_ERR_UNSUPPORTED_D;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  if (N == 0) return FA_OK;
+  if (!q || !k || !v || !o || !q_strides || !k_strides || !v_strides || !o_strides) return FA_ERR_NULL;
+  const int64_t elem = dtype == FA_F32 ? 4 : 2;
+  const int64_t* st[4] = {q_strides, k_strides, v_strides, o_strides};
+  const int64_t heads[4] = {H, H_kv, H_kv, H};
+  for (int t = 0; t < 4; ++t)
+    for (int i = 0; i < 3; ++i)
+      if (st[t][i] < 0) return FA_ERR_STRIDE;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) return FA_ERR_ALIGN;
+  for (int t = 0; t < 4; ++t)
+    for (int i = 0; i < 3; ++i)
+      if ((st[t][i] * elem) % 16 != 0) return FA_ERR_ALIGN;
+  for (int t = 0; t < 4; ++t)
+    if (st[t][2] < D) return FA_ERR_STRIDE;  // the rows of one head do not overlap
+  if (!rows_disjoint(o_strides, B, H, N, D)) return FA_ERR_STRIDE;
+
+  // Sizes: per-head row offsets and the key/value buffer ranges are 32-bit
+  // (max(N, 64) row strides of bytes below 2^32), the grid as fa_forward.
+  if (N * D >= ((int64_t)1 << 31)) return FA_ERR_TOO_LARGE;
+  for (int t = 0; t < 4; ++t)
+    if ((N > 64 ? N : 64) * st[t][2] * elem >= ((int64_t)1 << 32)) return FA_ERR_TOO_LARGE;
+  if (B > ((int64_t)1 << 31) / H) return FA_ERR_TOO_LARGE;
+  const int64_t BH = B * H;
+  const int64_t block_m = dtype == FA_F32 ? fa::kF32BlockM : fa::kMfmaBlockM;
+  const int64_t qtiles = (N + block_m - 1) / block_m;
+  if (BH > (((int64_t)1 << 31) - 1) / qtiles) return FA_ERR_TOO_LARGE;
+  if (BH > (int64_t)UINT32_MAX / (8 * N + 512)) return FA_ERR_TOO_LARGE;
+  int64_t ext[4];
+  for (int t = 0; t < 4; ++t) {
+    ext[t] = extent_elems(st[t], B, heads[t], N, D);
+    if (ext[t] < 0) return FA_ERR_TOO_LARGE;
+  }
+  const void* ptr[3] = {q, k, v};
+  for (int t = 0; t < 3; ++t)
+    if (ranges_overlap(o, (size_t)(ext[3] * elem), ptr[t], (size_t)(ext[t] * elem))) return FA_ERR_ALIAS;
+
+  const int dev = check_device();
+  if (dev != FA_OK) return dev;
+
+  fa::Problem p = dense_problem(q, k, v, o, H, BH, N, D, scale, causal);
+  p.group = (int)(H / H_kv);
+  fa::Layout* lay[4] = {&p.lq, &p.lk, &p.lv, &p.lo};
+  for (int t = 0; t < 4; ++t) *lay[t] = fa::Layout{st[t][0], st[t][1], (int)st[t][2]};
+  return launch_forward(p, dtype, (hipStream_t)stream);
 }
 
 const char* fa_status_string(int status) {
@@ -348,6 +433,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_DEVICE: return "current HIP device is not a gfx950 (MI355X)";
     case FA_ERR_WORKSPACE: return "workspace NULL, not 256-byte aligned, too small or overlapping a tensor";
     case FA_ERR_SPLITS: return "num_splits out of range (0 for the suggestion, else 1..64)";
+    case FA_ERR_STRIDE: return "invalid strides (negative, rows shorter than D, or overlapping output rows)";
     default: return "unknown status";
   }
 }

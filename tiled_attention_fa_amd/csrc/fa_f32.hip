@@ -39,6 +39,9 @@ struct Args {
   const float* k;
   const float* v;
   float* o;
+  Layout lq, lk, lv, lo;  // element strides of each tensor
+  int H;                  // query heads per batch
+  int group;              // query heads per key/value head
   int N;
   int num_qtiles;
   int total_tiles;  // BH * num_qtiles * splits
@@ -89,11 +92,12 @@ __global__ __launch_bounds__(kBlockM * waves_for<D>()) void fa_forward_f32_kerne
   const int split = rem - qt * a.splits;
   if (CAUSAL) qt = a.num_qtiles - 1 - qt;
   const int N = a.N;
-  const size_t head = (size_t)bh * (size_t)N * D;
-  const float* __restrict__ Q = a.q + head;
-  const float* __restrict__ K = a.k + head;
-  const float* __restrict__ V = a.v + head;
-  float* __restrict__ O = a.o + head;
+  const int b = bh / a.H, h = bh - b * a.H, hk = h / a.group;
+  const float* __restrict__ Q = a.q + b * a.lq.sb + h * a.lq.sh;
+  const float* __restrict__ K = a.k + b * a.lk.sb + hk * a.lk.sh;
+  const float* __restrict__ V = a.v + b * a.lv.sb + hk * a.lv.sh;
+  float* __restrict__ O = a.o + b * a.lo.sb + h * a.lo.sh;
+  const int ldq = a.lq.sn, ldk = a.lk.sn, ldv = a.lv.sn, ldo = a.lo.sn;  // row strides
   const double cd = a.c;
   const int qrow = qt * kBlockM + lane;
 
@@ -101,7 +105,7 @@ __global__ __launch_bounds__(kBlockM * waves_for<D>()) void fa_forward_f32_kerne
 #pragma unroll
   for (int d = 0; d < D; d += 4) {
     f32x4 x = {0.f, 0.f, 0.f, 0.f};
-    if (qrow < N) x = *(const f32x4*)(Q + (size_t)qrow * D + d);
+    if (qrow < N) x = *(const f32x4*)(Q + (size_t)qrow * ldq + d);
     q[d] = x[0] * a.qsign;
     q[d + 1] = x[1] * a.qsign;
     q[d + 2] = x[2] * a.qsign;
@@ -125,8 +129,8 @@ __global__ __launch_bounds__(kBlockM * waves_for<D>()) void fa_forward_f32_kerne
       const int r = idx / (D / 4), c4 = idx - r * (D / 4);
       f32x4 kx = {0.f, 0.f, 0.f, 0.f}, vx = {0.f, 0.f, 0.f, 0.f};
       if (k0 + r < N) {
-        kx = *(const f32x4*)(K + (size_t)(k0 + r) * D + 4 * c4);
-        vx = *(const f32x4*)(V + (size_t)(k0 + r) * D + 4 * c4);
+        kx = *(const f32x4*)(K + (size_t)(k0 + r) * ldk + 4 * c4);
+        vx = *(const f32x4*)(V + (size_t)(k0 + r) * ldv + 4 * c4);
       }
       *(f32x4*)(Ks + r * D + 4 * c4) = kx;
       *(f32x4*)(Vs + r * D + 4 * c4) = vx;
@@ -235,7 +239,7 @@ __global__ __launch_bounds__(kBlockM * waves_for<D>()) void fa_forward_f32_kerne
       if (part)
         *(f32x4*)(dst + (size_t)qrow * D + col) = out * inv;
       else
-        *(f32x4*)(O + (size_t)qrow * D + col) = out * inv;
+        *(f32x4*)(O + (size_t)qrow * ldo + col) = out * inv;
     }
     if (wave == 0) {
       if (part)
@@ -255,6 +259,12 @@ hipError_t launch_f32(const Problem& p, hipStream_t stream) {
   a.k = (const float*)p.k;
   a.v = (const float*)p.v;
   a.o = (float*)p.o;
+  a.lq = p.lq;
+  a.lk = p.lk;
+  a.lv = p.lv;
+  a.lo = p.lo;
+  a.H = p.H;
+  a.group = p.group;
   a.N = p.N;
   a.num_qtiles = (p.N + kBlockM - 1) / kBlockM;
   a.splits = p.splits;

@@ -6,7 +6,19 @@
 
 namespace fa {
 
-// One validated forward problem: [BH, N, D] tensors (B and H folded).
+// Where element (b, h, n, d) of a tensor sits: b*sb + h*sh + n*sn + d
+// elements from its base (d contiguous).
+struct Layout {
+  int64_t sb;
+  int64_t sh;
+  int sn;
+};
+
+// Dense [B, H, N, D].
+inline Layout dense_layout(int64_t H, int64_t N, int64_t D) { return Layout{H * N * D, N * D, (int)D}; }
+
+// One validated forward problem.  Query heads bh = b*H + h, h < H; query
+// head h reads key/value head h / group (group = H / H_kv).
 struct Problem {
   const void* q;
   const void* k;
@@ -17,6 +29,9 @@ struct Problem {
   int D;
   float scale;
   bool causal;
+  int H = 1;
+  int group = 1;
+  Layout lq{}, lk{}, lv{}, lo{};
   // Key-range split (split-KV): with splits > 1 each query block's key
   // tiles are cut into `splits` ranges, one workgroup each, and the kernel
   // writes normalised fp32 partials part_o [splits, BH, N, D] and their

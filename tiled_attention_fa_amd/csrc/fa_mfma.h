@@ -88,6 +88,9 @@ struct Args {
   const uint16_t* k;
   const uint16_t* v;
   uint16_t* o;
+  Layout lq, lk, lv, lo;  // element strides of each tensor
+  int H;                  // query heads per batch
+  int group;              // query heads per key/value head
   int N;
   int num_qtiles;   // ceil(N / BM)
   int total_tiles;  // BH * num_qtiles * splits
@@ -272,11 +275,12 @@ void fa_forward_kernel(Args a) {
   const int split = rem - qt * a.splits;
   if (CAUSAL) qt = a.num_qtiles - 1 - qt;  // longest rows first
   const int N = a.N;
-  const size_t head = (size_t)bh * (size_t)N * D;
-  const uint16_t* __restrict__ Q = a.q + head;
-  [[maybe_unused]] const uint16_t* __restrict__ K = a.k + head;
-  [[maybe_unused]] const uint16_t* __restrict__ V = a.v + head;
-  uint16_t* __restrict__ O = a.o + head;
+  const int b = bh / a.H, h = bh - b * a.H, hk = h / a.group;
+  const uint16_t* __restrict__ Q = a.q + b * a.lq.sb + h * a.lq.sh;
+  [[maybe_unused]] const uint16_t* __restrict__ K = a.k + b * a.lk.sb + hk * a.lk.sh;
+  [[maybe_unused]] const uint16_t* __restrict__ V = a.v + b * a.lv.sb + hk * a.lv.sh;
+  uint16_t* __restrict__ O = a.o + b * a.lo.sb + h * a.lo.sh;
+  const int ldq = a.lq.sn, ldk = a.lk.sn, ldv = a.lv.sn, ldo = a.lo.sn;  // row strides
   const float c = a.c;
 
   const int q0 = qt * BM + wave * 32;  // first query row of this wave
@@ -287,7 +291,7 @@ void fa_forward_kernel(Args a) {
 #pragma unroll
   for (int ch = 0; ch < DC; ++ch) {
     u32x4 x = {0u, 0u, 0u, 0u};
-    if (qrow < N) x = *(const u32x4*)(Q + (size_t)qrow * D + 16 * ch + 8 * hi);
+    if (qrow < N) x = *(const u32x4*)(Q + (size_t)qrow * ldq + 16 * ch + 8 * hi);
     qf[ch] = x ^ a.qxor;
   }
 
@@ -317,21 +321,23 @@ void fa_forward_kernel(Args a) {
   for (int i = 0; i < LOADS; ++i) {
     const int p = i * NT + tid;
     const int row = p / CPR, pc = p % CPR;
-    koff[i] = (row * D + 8 * (pc ^ k_swz<DP>(row))) * 2;
-    voff[i] = (row * D + 8 * (pc ^ v_swz(row))) * 2;
+    koff[i] = (row * ldk + 8 * (pc ^ k_swz<DP>(row))) * 2;
+    voff[i] = (row * ldv + 8 * (pc ^ v_swz(row))) * 2;
     kpred[i] = DP == D || (pc ^ k_swz<DP>(row)) < D / 8;
     vpred[i] = DP == D || (pc ^ v_swz(row)) < D / 8;
   }
   auto tile_load = [&](int t, uint16_t* kdst, uint16_t* vdst) {
 #if defined(__HIP_DEVICE_COMPILE__)  // buffer resources exist in device code only
     const int k0 = t * BN;
-    // bytes from key k0 to the end of the head: below 2^32 (N * D < 2^31),
-    // formed in unsigned arithmetic, passed as the 32-bit record count
-    const int bytes = (int)((uint32_t)(N - k0) * (uint32_t)(2 * D));
+    // bytes from key k0 to key N (max(N, 64) row strides stay below 2^32,
+    // checked by the host), formed in unsigned arithmetic, passed as the
+    // 32-bit record count; rows past N read as zero
+    const int kbytes = (int)((uint32_t)(N - k0) * (uint32_t)(2 * ldk));
+    const int vbytes = (int)((uint32_t)(N - k0) * (uint32_t)(2 * ldv));
     const __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(K + (size_t)k0 * D), 0, bytes, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc((void*)(K + (size_t)k0 * ldk), 0, kbytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rv =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(V + (size_t)k0 * D), 0, bytes, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc((void*)(V + (size_t)k0 * ldv), 0, vbytes, 0x00020000);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const size_t at = (size_t)(i * NT + wave * 64) * 8;
@@ -561,7 +567,7 @@ void fa_forward_kernel(Args a) {
         const int d0 = 32 * db + 8 * g + 4 * hi;
         u32x2 out = {Ops<T>::pack(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
                      Ops<T>::pack(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
-        *(u32x2*)(O + (size_t)qrow * D + d0) = out;
+        *(u32x2*)(O + (size_t)qrow * ldo + d0) = out;
       }
   }
 }
@@ -583,6 +589,12 @@ inline Args make_args(const Problem& p) {
   a.k = (const uint16_t*)p.k;
   a.v = (const uint16_t*)p.v;
   a.o = (uint16_t*)p.o;
+  a.lq = p.lq;
+  a.lk = p.lk;
+  a.lv = p.lv;
+  a.lo = p.lo;
+  a.H = p.H;
+  a.group = p.group;
   a.N = p.N;
   a.num_qtiles = 0;
   a.total_tiles = 0;
