@@ -292,3 +292,45 @@ def test_strided_validation(lib, args, status):
     if status == "FA_ERR_DEVICE" and got == 0:
         pytest.skip("a gfx950 device is present; the no-device path is not reachable")
     assert fa.STATUS_NAMES[got] == status
+
+
+# ------------------------------------------- tile-calibration library
+
+TUNE_HEADER = os.path.join(ROOT, "include", "fa_tune.h")
+
+
+def test_tune_library_exports_its_header():
+    from tiled_attention_fa_amd import tile_sweep
+    lib = tile_sweep.load_tune()
+    text = re.sub(r"/\*.*?\*/", "", open(TUNE_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(fa_\w+)\s*\(", text)))
+    assert names == ["fa_tune_forward", "fa_tune_shapes"]
+    out = subprocess.run(["nm", "-D", "--defined-only", tile_sweep.TUNE_LIB], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (fa_\w+)", out))
+    for n in names + list(EXPORTS):
+        assert n in exported, n
+    assert tile_sweep.shapes(lib, 64) == [(2, 1), (4, 1), (4, 2), (8, 1)]
+    assert tile_sweep.shapes(lib, 96) == [(2, 1), (4, 1), (8, 1)]
+    assert tile_sweep.shapes(lib, 128) == [(2, 1), (4, 1), (8, 1)]
+    assert lib.fa_tune_shapes(80, None, None, 0) == -3
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(dtype=0), "FA_ERR_DTYPE"),
+    (dict(B=0), "FA_ERR_DIM"),
+    (dict(waves=3), "FA_ERR_UNSUPPORTED_D"),
+    (dict(D=128, waves=4, occ=2), "FA_ERR_UNSUPPORTED_D"),
+    (dict(o=A), "FA_ERR_ALIAS"),
+    (dict(), "FA_ERR_DEVICE"),
+])
+def test_tune_forward_validation(args, status):
+    from tiled_attention_fa_amd import tile_sweep
+    lib = tile_sweep.load_tune()
+    kw = dict(q=A, k=B_, v=C, o=O, B=1, H=1, N=64, D=64, dtype=1, waves=4, occ=2)
+    kw.update(args)
+    got = lib.fa_tune_forward(kw["q"], kw["k"], kw["v"], kw["o"], kw["B"], kw["H"], kw["N"], kw["D"],
+                              0.125, 0, kw["dtype"], kw["waves"], kw["occ"], None)
+    if status == "FA_ERR_DEVICE" and got == 0:
+        pytest.skip("a gfx950 device is present; the no-device path is not reachable")
+    assert fa.STATUS_NAMES[got] == status

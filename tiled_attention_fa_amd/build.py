@@ -35,8 +35,12 @@ def common_flags():
             f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
-def _compile(src: str, extra) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+TUNE_LIB = os.path.join(PKG, "libfa_tune.so")
+TUNE_DIR = os.path.join(BUILD_DIR, "tune")
+
+
+def _compile(src: str, extra, out_dir: str = BUILD_DIR) -> str:
+    obj = os.path.join(out_dir, os.path.basename(src) + ".o")
     cmd = [hipcc(), *common_flags(), *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     lines = [ln for ln in (r.stdout + r.stderr).splitlines()
@@ -48,19 +52,34 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(jobs: int = 0, extra=()) -> str:
-    """Compile and link; returns the path of libfa.so.  Always rebuilds."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    jobs = jobs or min(len(srcs), os.cpu_count() or 4, 8)
-    with ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, list(extra)), srcs))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(jobs: int = 0, extra=(), tune: bool = True) -> str:
+    """Compile and link libfa.so and (with tune) the tile-calibration
+    library libfa_tune.so, the same sources with every workgroup shape of
+    the sweep instantiated (-DFA_TILE_SWEEP).  Returns the path of
+    libfa.so.  Always rebuilds."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    os.makedirs(TUNE_DIR, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    work = [(s, list(extra), BUILD_DIR) for s in srcs]
+    if tune:
+        work += [(s, list(extra) + ["-DFA_TILE_SWEEP"], TUNE_DIR) for s in srcs]
+    # the largest translation units first, so the pool ends together
+    work.sort(key=lambda w: -os.path.getsize(w[0]) - (1 << 20) * ("FA_TILE_SWEEP" in w[1] and "mfma" in w[0]))
+    jobs = jobs or min(len(work), os.cpu_count() or 4, 16)
+    with ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(lambda w: _compile(*w), work))
+    _link([o for o, w in zip(objs, work) if w[2] == BUILD_DIR], LIB)
+    if tune:
+        _link([o for o, w in zip(objs, work) if w[2] == TUNE_DIR], TUNE_LIB)
     return LIB
 
 

@@ -418,6 +418,39 @@ int fa_forward_strided(const void* q, const int64_t* q_strides, const void* k, c
   return launch_forward(p, dtype, (hipStream_t)stream);
 }
 
+#ifdef FA_TILE_SWEEP
+int fa_tune_shapes(int64_t D, int* waves, int* occupancy, int capacity) {
+  if (!head_dim_supported(D)) return FA_ERR_UNSUPPORTED_D;
+  const int n = D == 64 ? 4 : 3;
+  for (int i = 0; i < n && i < capacity; ++i) {
+    const int* s = D == 64 ? fa::kTuneShapes64[i] : fa::kTuneShapesWide[i];
+    if (waves) waves[i] = s[0];
+    if (occupancy) occupancy[i] = s[1];
+  }
+  return n;
+}
+
+int fa_tune_forward(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H, int64_t N,
+                    int64_t D, float scale, int causal, int dtype, int waves, int occupancy, void* stream) {
+  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  int64_t BH = 0;
+  const int st = validate(q, k, v, o, B, H, N, D, scale, dtype, 32 * (int64_t)(waves > 0 ? waves : 1), &BH);
+  if (st == 1) return FA_OK;
+  if (st != FA_OK) return st;
+  int sw[4], so[4];
+  const int n = fa_tune_shapes(D, sw, so, 4);
+  bool known = false;
+  for (int i = 0; i < n; ++i) known = known || (sw[i] == waves && so[i] == occupancy);
+  if (!known) return FA_ERR_UNSUPPORTED_D;
+  const int dev = check_device();
+  if (dev != FA_OK) return dev;
+  fa::Problem p = dense_problem(q, k, v, o, H, BH, N, D, scale, causal);
+  const hipError_t err = dtype == FA_F16 ? fa::launch_mfma_shape_f16(p, waves, occupancy, (hipStream_t)stream)
+                                         : fa::launch_mfma_shape_bf16(p, waves, occupancy, (hipStream_t)stream);
+  return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+#endif
+
 const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";

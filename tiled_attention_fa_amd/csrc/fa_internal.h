@@ -58,11 +58,14 @@ struct MergeProblem {
 };
 
 // Workgroup shape of the matrix-core kernel per head dimension and mask:
-// waves per workgroup (32 query rows each) and workgroups resident per CU.
-// Eight waves (256 rows, two waves per SIMD in lockstep) where rows are long
-// and uniform; four waves for causal D = 64, where the finer grain balances
-// the triangle better (two workgroups per CU), and for D = 96 (one wave per
-// SIMD: 128-element LDS rows leave room for one workgroup per CU).
+// waves per workgroup (32 query rows each) and workgroups resident per CU,
+// the fastest of the calibration sweep (tiled_attention_fa_amd/tile_sweep.py,
+// every shape of the tuning build timed on MI355X for each D, storage type
+// and mask).  Eight waves (256 rows, two waves per SIMD in lockstep) where
+// rows are long and uniform; four waves for causal D = 64, where the finer
+// grain balances the triangle better (two workgroups per CU), and for D = 96
+// (one wave per SIMD: 128-element LDS rows leave room for one workgroup per
+// CU).
 constexpr int mfma_waves(int D, bool causal) { return D == 96 || (D == 64 && causal) ? 4 : 8; }
 constexpr int mfma_wgs_per_cu(int D, bool causal) { return D == 64 && causal ? 2 : 1; }
 
@@ -98,6 +101,14 @@ hipError_t launch_mfma_f16(const Problem& p, hipStream_t stream);
 hipError_t launch_mfma_bf16(const Problem& p, hipStream_t stream);
 hipError_t launch_f32(const Problem& p, hipStream_t stream);
 hipError_t launch_split_merge(const MergeProblem& p, hipStream_t stream);
+#ifdef FA_TILE_SWEEP
+// The calibration sweep's shapes (tuning library only): (waves per
+// workgroup, waves_per_eu hint) pairs.
+constexpr int kTuneShapes64[][2] = {{2, 1}, {4, 1}, {4, 2}, {8, 1}};
+constexpr int kTuneShapesWide[][2] = {{2, 1}, {4, 1}, {8, 1}};
+hipError_t launch_mfma_shape_f16(const Problem& p, int waves, int occupancy, hipStream_t stream);
+hipError_t launch_mfma_shape_bf16(const Problem& p, int waves, int occupancy, hipStream_t stream);
+#endif
 hipError_t launch_naive_f16(const NaiveProblem& p, hipStream_t stream);
 hipError_t launch_naive_bf16(const NaiveProblem& p, hipStream_t stream);
 

@@ -630,5 +630,41 @@ hipError_t launch(const Problem& p, hipStream_t stream) {
   }
 }
 
+#ifdef FA_TILE_SWEEP
+// Every workgroup shape of the calibration sweep (the tuning library only):
+// (waves per workgroup, waves_per_eu hint).  Two workgroups per CU need a
+// 64-element LDS row (D = 64) and four waves per workgroup (two waves of
+// two workgroups sit on two SIMDs only); with D = 96 or 128 one workgroup
+// fills the LDS, so those sizes take the one-workgroup shapes only.
+template <typename T, bool SPLIT_P, int D, bool CAUSAL>
+hipError_t launch_shape_d(const Args& a, int64_t BH, int nw, int occ, hipStream_t s) {
+  if (nw == 2 && occ == 1) return launch_one<T, D, CAUSAL, SPLIT_P, 2, 1>(a, BH, s);
+  if (nw == 4 && occ == 1) return launch_one<T, D, CAUSAL, SPLIT_P, 4, 1>(a, BH, s);
+  if (nw == 8 && occ == 1) return launch_one<T, D, CAUSAL, SPLIT_P, 8, 1>(a, BH, s);
+  if constexpr (D == 64) {
+    if (nw == 4 && occ == 2) return launch_one<T, D, CAUSAL, SPLIT_P, 4, 2>(a, BH, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T, bool SPLIT_P>
+hipError_t launch_shape(const Problem& p, int nw, int occ, hipStream_t s) {
+  const Args a = make_args(p);
+  switch (p.D) {
+    case 64:
+      return p.causal ? launch_shape_d<T, SPLIT_P, 64, true>(a, p.BH, nw, occ, s)
+                      : launch_shape_d<T, SPLIT_P, 64, false>(a, p.BH, nw, occ, s);
+    case 96:
+      return p.causal ? launch_shape_d<T, SPLIT_P, 96, true>(a, p.BH, nw, occ, s)
+                      : launch_shape_d<T, SPLIT_P, 96, false>(a, p.BH, nw, occ, s);
+    case 128:
+      return p.causal ? launch_shape_d<T, SPLIT_P, 128, true>(a, p.BH, nw, occ, s)
+                      : launch_shape_d<T, SPLIT_P, 128, false>(a, p.BH, nw, occ, s);
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+#endif
+
 }  // namespace mfma
 }  // namespace fa

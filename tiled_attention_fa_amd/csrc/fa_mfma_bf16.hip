@@ -5,4 +5,9 @@ namespace fa {
 hipError_t launch_mfma_bf16(const Problem& p, hipStream_t stream) {
   return mfma::launch<__bf16, true>(p, stream);
 }
+#ifdef FA_TILE_SWEEP
+hipError_t launch_mfma_shape_bf16(const Problem& p, int waves, int occupancy, hipStream_t stream) {
+  return mfma::launch_shape<__bf16, true>(p, waves, occupancy, stream);
+}
+#endif
 }  // namespace fa

@@ -1,0 +1,187 @@
+"""Tile-size calibration sweep on the current device.
+
+"Flash Attention on Android: tiled SGEMM with RenderScript", section "The
+detail that breaks naive ports: tile calibration", found the best tile size
+to differ between GPUs and asks for it to be measured on each target;
+"Android Transformer Optimization: Attention and Mobile GPU Bottlenecks",
+section "Implementation Recommendations", sizes tiles from the on-chip
+memory.  On MI355X the tile is 32 query rows per wave by 64 keys (the
+32x32 matrix-core tile and the LDS ring); what is left to calibrate is how
+many waves share a workgroup (and so its K/V tiles in LDS) and how many
+workgroups share a CU.  This tool times every shape that the calibration
+library (libfa_tune.so) instantiates, for each head dimension, storage
+type and mask, on synthetic inputs drawn by the workload generator, and
+writes a table:
+
+    python -m tiled_attention_fa_amd.tile_sweep --out profiles/tile_sweep_mi355x
+
+It checks every shape's output against libfa.so's fa_forward on the same
+inputs (the library's own choice), and reports fa_forward's time beside the
+sweep so the table shows whether the shipped choice is the fastest.
+"""
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+TUNE_LIB = os.path.join(PKG, "libfa_tune.so")
+
+# (B, H, N, D, causal): per head dimension one non-causal and one causal
+# shape at the sizes of the workloads, each in fp16 and bf16.
+CASES = [
+    (1, 32, 2048, 64, False), (4, 32, 2048, 64, True),
+    (2, 8, 1000, 96, False), (1, 16, 4096, 96, True),
+    (1, 16, 4096, 128, False), (1, 16, 8192, 128, True),
+]
+DTYPES = ("f16", "bf16")
+
+
+def load_tune():
+    if not os.path.exists(TUNE_LIB):
+        raise ImportError(f"{TUNE_LIB} is not built; run tiled_attention_fa_amd/build.py")
+    lib = ctypes.CDLL(TUNE_LIB)
+    i64, vp, ip = ctypes.c_int64, ctypes.c_void_p, ctypes.POINTER(ctypes.c_int)
+    lib.fa_tune_shapes.argtypes = [i64, ip, ip, ctypes.c_int]
+    lib.fa_tune_shapes.restype = ctypes.c_int
+    lib.fa_tune_forward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float, ctypes.c_int,
+                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
+    lib.fa_tune_forward.restype = ctypes.c_int
+    return lib
+
+
+def shapes(lib, D):
+    w = (ctypes.c_int * 8)()
+    o = (ctypes.c_int * 8)()
+    n = lib.fa_tune_shapes(D, w, o, 8)
+    if n < 0:
+        raise ValueError(f"no shapes for D={D}")
+    return [(w[i], o[i]) for i in range(n)]
+
+
+def tune_forward(lib, q, k, v, o, scale, causal, code, waves, occ, stream):
+    B, H, N, D = q.shape
+    st = lib.fa_tune_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, H, N, D,
+                             float(scale), int(causal), code, waves, occ, stream)
+    if st != 0:
+        raise RuntimeError(f"fa_tune_forward status {st}")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--out", default="", help="write <out>.json and <out>.md")
+    ap.add_argument("--launches", type=int, default=40)
+    ap.add_argument("--rounds", type=int, default=3,
+                    help="interleaved rounds over fa_forward and the shapes; the best round counts")
+    args = ap.parse_args()
+
+    sys.path.insert(0, ROOT)
+    import numpy as np
+    import torch
+
+    import tiled_attention_fa_amd as fa
+    import workloads
+
+    lib = load_tune()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16}
+    codes = {"f16": fa.FA_F16, "bf16": fa.FA_BF16}
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.launches):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.launches * 1e3
+
+    rows = []
+    for B, H, N, D, causal in CASES:
+        for dt in DTYPES:
+            w = workloads.Workload(f"sweep_b{B}h{H}n{N}d{D}_{dt}{'_causal' if causal else ''}", B, H, N, D, dt,
+                                   causal, seed=50_000 + N + D)
+            x = workloads.make_inputs(w)
+            q, k, v = (torch.from_numpy(np.ascontiguousarray(x[n]).view(np.int16)).view(tdt[dt]).to(dev)
+                       for n in "qkv")
+            ref = torch.empty_like(q)
+            out = torch.empty_like(q)
+            # direct C calls with prepared arguments, so that host overhead
+            # does not starve the device between launches
+            base = (q.data_ptr(), k.data_ptr(), v.data_ptr())
+            lib_fa = fa.load_library()
+            fwd_args = base + (ref.data_ptr(), B, H, N, D, float(w.scale), int(causal), codes[dt],
+                               stream.cuda_stream)
+
+            def call():
+                if lib_fa.fa_forward(*fwd_args) != 0:
+                    raise RuntimeError("fa_forward failed")
+
+            # the clock drops while the host prepares the inputs: run
+            # untimed launches until it is back up
+            t0 = time.time()
+            while time.time() - t0 < 0.25:
+                call()
+            torch.cuda.synchronize()
+            flops = workloads.flops(w)
+            variants = shapes(lib, D)
+            best_lib = float("inf")
+            best = {sh: float("inf") for sh in variants}
+            for _ in range(args.rounds):
+                best_lib = min(best_lib, timed(call))
+                for waves, occ in variants:
+                    targs = base + (out.data_ptr(), B, H, N, D, float(w.scale), int(causal), codes[dt], waves,
+                                    occ, stream.cuda_stream)
+                    best[(waves, occ)] = min(best[(waves, occ)], timed(lambda: lib.fa_tune_forward(*targs)))
+            rec = {"case": w.name, "B": B, "H": H, "N": N, "D": D, "dtype": dt, "causal": causal,
+                   "fa_forward_us": round(best_lib, 2), "shapes": []}
+            for waves, occ in variants:
+                tune_forward(lib, q, k, v, out, w.scale, causal, codes[dt], waves, occ, stream.cuda_stream)
+                torch.cuda.synchronize()
+                diff = float((out.float() - ref.float()).abs().max().item())
+                t = best[(waves, occ)]
+                rec["shapes"].append({"waves": waves, "rows": 32 * waves, "waves_per_eu": occ,
+                                      "us": round(t, 2), "tflops": round(flops / (t * 1e-6) / 1e12, 1),
+                                      "max_abs_diff_vs_fa_forward": diff})
+            best = min(rec["shapes"], key=lambda s: s["us"])
+            rec["best"] = {"waves": best["waves"], "waves_per_eu": best["waves_per_eu"], "us": best["us"]}
+            rows.append(rec)
+            print(json.dumps(rec), flush=True)
+            del q, k, v, ref, out
+
+    if args.out:
+        prop = torch.cuda.get_device_properties(dev)
+        meta = {"device": prop.name, "arch": getattr(prop, "gcnArchName", ""), "cus": prop.multi_processor_count,
+                "launches_per_timing": args.launches,
+                "command": "python -m tiled_attention_fa_amd.tile_sweep --out " + args.out}
+        json.dump({"meta": meta, "cases": rows}, open(args.out + ".json", "w"), indent=1)
+        lines = [f"# Tile calibration sweep ({meta['arch']}, {meta['cus']} CUs)", "",
+                 f"Command (repository root): `{meta['command']}`", "",
+                 f"Mean microseconds per launch over {args.launches} back-to-back launches (HIP events), "
+                 f"best of {args.rounds} interleaved rounds, after 0.25 s of untimed launches per case; "
+                 "every workgroup shape of libfa_tune.so: waves x 32 query rows per workgroup, "
+                 "waves_per_eu hint. `fa_forward` is the shipped library's own choice on the same "
+                 "inputs.", "",
+                 "| case | fa_forward | " + " | ".join(["shape / us"] * 4) + " | best |",
+                 "|---|---|" + "---|" * 4 + "---|"]
+        for r in rows:
+            cells = [f"{s['waves']}w occ{s['waves_per_eu']}: {s['us']}" for s in r["shapes"]]
+            cells += [""] * (4 - len(cells))
+            lines.append(f"| {r['case']} | {r['fa_forward_us']} | " + " | ".join(cells) +
+                         f" | {r['best']['waves']}w occ{r['best']['waves_per_eu']} |")
+        worst = max(s["max_abs_diff_vs_fa_forward"] for r in rows for s in r["shapes"])
+        lines += ["", f"Largest difference of any shape's O from fa_forward's: {worst:.3e}."]
+        open(args.out + ".md", "w").write("\n".join(lines) + "\n")
+
+
+if __name__ == "__main__":
+    main()
