@@ -14,7 +14,9 @@ resident in HBM.  Prints one JSON line:
                           current kernel source is committed, else null
   cpu_baseline            the fp64 oracle timed on this host's cores on a
                           bounded sample of the same workload (reported
-                          baseline only)
+                          baseline only); the heads it computes double as a
+                          parity check of the GPU output
+                          (max_abs_err_oracle_heads)
   naive_three_pass        (16-bit storage) the three-pass attention on the
                           same inputs: time per call, the tiled pass's
                           speed-up over it, both byte counts
@@ -23,6 +25,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
 
 import argparse
+import ctypes
 import hashlib
 import glob
 import json
@@ -102,9 +105,11 @@ def torch_inputs(w, x, device):
     return out
 
 
-def cpu_baseline(w, x, budget_s: float = 20.0):
+def cpu_baseline(w, x, o=None, budget_s: float = 20.0):
     """Time the fp64 oracle on a bounded sample of the workload: whole heads,
-    as many as fit the budget (estimated from one head)."""
+    as many as fit the budget (estimated from one head).  With o (the GPU
+    output as a [B, H, N, D] tensor) also the largest difference between it
+    and the oracle on those heads."""
     import oracle
     BH = w.B * w.H
     q = x["q"].reshape(BH, 1, w.N, w.D)
@@ -115,25 +120,17 @@ def cpu_baseline(w, x, budget_s: float = 20.0):
     one = time.perf_counter() - t0
     heads = int(max(1, min(BH, budget_s / max(one, 1e-6))))
     t0 = time.perf_counter()
-    _, _, used = oracle.forward(q[:heads], k[:heads], v[:heads], w.dtype, w.scale, w.causal,
-                                return_rowsum=True)
+    ref, _, used = oracle.forward(q[:heads], k[:heads], v[:heads], w.dtype, w.scale, w.causal,
+                                  return_rowsum=True)
     dt = time.perf_counter() - t0
     flops = workloads.flops(w) * heads / BH
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(used), "kind": "oracle",
-            "sample": f"{heads} of {BH} heads of {w.name} (fp64, S and P rows materialised), "
-                      f"{dt:.2f} s"}
-
-
-def parity_sample(w, x, o):
-    """Max abs error of sampled output rows against the oracle."""
-    import oracle
-    rng = np.random.default_rng(0)
-    BH = w.B * w.H
-    bh = rng.integers(0, BH, 64)
-    ri = rng.integers(0, w.N, 64)
-    ref = oracle.rows(x["q"], x["k"], x["v"], w.dtype, w.scale, w.causal, bh, ri)
-    got = o.float().cpu().numpy().astype(np.float64).reshape(BH, w.N, w.D)[bh, ri]
-    return float(np.abs(got - ref).max())
+    rec = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(used), "kind": "oracle",
+           "sample": f"{heads} of {BH} heads of {w.name} (fp64, S and P rows materialised), "
+                     f"{dt:.2f} s"}
+    if o is not None:
+        got = o.contiguous().float().cpu().numpy().astype(np.float64).reshape(BH, w.N, w.D)[:heads]
+        rec["max_abs_err_vs_gpu"] = float(np.abs(got - ref.reshape(heads, w.N, w.D)).max())
+    return rec
 
 
 def naive_leg(w, q, k, v, o, stream, code, lib, steps, tiled_ms):
@@ -192,7 +189,14 @@ def main():
                     help="seconds of untimed launches before the warm-up steps, so that the "
                          "GPU clock has left its ramp (it takes tens of ms under this load)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--no-check", action="store_true",
+                    help="skip comparing the GPU output with the oracle heads of the CPU baseline")
+    ap.add_argument("--layout", choices=("bhnd", "bnhd"), default="bhnd",
+                    help="memory layout of q, k, v, o: dense [B, H, N, D] (fa_forward) or "
+                         "[B, N, H, D] (fa_forward_strided)")
+    ap.add_argument("--kv-heads", type=int, default=0,
+                    help="key/value heads (grouped-query attention through fa_forward_strided; "
+                         "0: as many as query heads)")
     ap.add_argument("--heads", type=int, default=0,
                     help="run the workload with this many heads instead (same recipe and seed); "
                          "for the few-head cases that split-KV is for")
@@ -235,17 +239,40 @@ def main():
     if args.heads:
         w = w.with_(H=args.heads)
     x = workloads.make_inputs(w)
+    kvh = args.kv_heads or w.H
+    if w.H % kvh:
+        sys.exit(f"--kv-heads {kvh} must divide the {w.H} query heads")
+    if kvh != w.H:  # K and V drawn by the same recipe at kvh heads
+        xkv = workloads.make_inputs(w.with_(H=kvh, seed=w.seed + 1))
+        x = {"q": x["q"], "k": xkv["k"], "v": xkv["v"]}
     input_sha = {n: hashlib.sha256(np.ascontiguousarray(x[n]).tobytes()).hexdigest()[:16]
                  for n in "qkv"}
+    # dense inputs as the oracle takes them: each K/V head repeated for its group
+    x_dense = x if kvh == w.H else {"q": x["q"], "k": np.repeat(x["k"], w.H // kvh, axis=1),
+                                    "v": np.repeat(x["v"], w.H // kvh, axis=1)}
     q, k, v = torch_inputs(w, x, dev)
-    o = torch.empty_like(q)
+    strided = args.layout != "bhnd" or kvh != w.H
+    if args.layout == "bnhd":  # stored [B, N, H, D], viewed as [B, H, N, D]
+        q, k, v = (t.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3) for t in (q, k, v))
+        o = torch.empty((w.B, w.N, w.H, w.D), dtype=q.dtype, device=dev).permute(0, 2, 1, 3)
+    else:
+        o = torch.empty_like(q)
     stream = torch.cuda.current_stream(dev)
 
     # The binding checks the tensors once; the timed loop then calls the C
     # entry point with the same pointers and sizes (inputs stay resident).
-    fa.fa_forward(q, k, v, o, scale=w.scale, causal=w.causal, stream=stream)
     code = {"f16": fa.FA_F16, "bf16": fa.FA_BF16, "f32": fa.FA_F32}[w.dtype]
     lib = fa.load_library()
+    if strided:
+        if args.splits != 1:
+            sys.exit("--splits applies to the dense layout only")
+        fa.fa_forward_strided(q, k, v, o, scale=w.scale, causal=w.causal, stream=stream)
+        strides = [(ctypes.c_int64 * 3)(*t.stride()[:3]) for t in (q, k, v, o)]
+        sargs = (q.data_ptr(), strides[0], k.data_ptr(), strides[1], v.data_ptr(), strides[2],
+                 o.data_ptr(), strides[3], w.B, w.H, kvh, w.N, w.D, float(w.scale), int(w.causal),
+                 code, stream.cuda_stream)
+    else:
+        fa.fa_forward(q, k, v, o, scale=w.scale, causal=w.causal, stream=stream)
     cargs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), w.B, w.H, w.N, w.D,
              float(w.scale), int(w.causal), code, stream.cuda_stream)
 
@@ -261,7 +288,10 @@ def main():
                  stream.cuda_stream)
 
     def step():
-        st = lib.fa_forward(*cargs) if splits == 1 else lib.fa_forward_ex(*xargs)
+        if strided:
+            st = lib.fa_forward_strided(*sargs)
+        else:
+            st = lib.fa_forward(*cargs) if splits == 1 else lib.fa_forward_ex(*xargs)
         if st != 0:
             raise fa.FAError(st)
 
@@ -315,7 +345,7 @@ def main():
     median_single_us = float(np.median(singles))
 
     naive = None
-    if w.dtype != "f32" and not args.no_naive:
+    if w.dtype != "f32" and not args.no_naive and not strided:
         naive = naive_leg(w, q, k, v, o, stream, code, lib, max(10, min(args.steps, 50)), ms_per_step)
 
     rec = {
@@ -333,7 +363,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D,
                    "storage": w.dtype, "causal": w.causal, "parallelism": "none (1 GPU)",
-                   "splits": splits},
+                   "splits": splits, "layout": args.layout, "kv_heads": kvh},
         "pct_peak": round(100 * value / peak, 2),
         "roofline": {
             "bound": "mfma",
@@ -341,9 +371,10 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
-            "traffic": committed_traffic(w.name),
+            # the committed counter profile is of the dense, unsplit workload
+            "traffic": committed_traffic(w.name) if (not strided and splits == 1 and not args.heads) else None,
             "kernel_us_mean": round(kern_us, 3),
-            "min_bytes": workloads.min_bytes(w),
+            "min_bytes": workloads.min_bytes(w) * (w.H + kvh) // (2 * w.H),
         },
         "median_single_launch_us": round(median_single_us, 3),
         "untimed_settle": {"seconds": args.settle_s, "launches": settle_launches},
@@ -355,10 +386,11 @@ def main():
     }
     if naive is not None:
         rec["naive_three_pass"] = naive
-    if not args.no_check:
-        rec["max_abs_err_sampled"] = parity_sample(w, x, o)
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w, x)
+        # the oracle's heads double as a parity check of the GPU output
+        rec["cpu_baseline"] = cpu_baseline(w, x_dense, None if args.no_check else o)
+        if not args.no_check:
+            rec["max_abs_err_oracle_heads"] = rec["cpu_baseline"]["max_abs_err_vs_gpu"]
     print(json.dumps(rec), flush=True)
 
 
