@@ -42,10 +42,12 @@ def np_decode(bits: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "f32":
         return np.asarray(bits, dtype=np.float32).astype(np.float64)
     if dtype == "f16":
-        return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+        with np.errstate(invalid="ignore"):  # NaN patterns stay NaN
+            return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
     if dtype == "bf16":
         u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
-        return u.view(np.float32).astype(np.float64)
+        with np.errstate(invalid="ignore"):  # NaN patterns stay NaN
+            return u.view(np.float32).astype(np.float64)
     raise ValueError(dtype)
 
 
