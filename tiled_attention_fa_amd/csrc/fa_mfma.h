@@ -39,9 +39,12 @@
 //    {4h..4h+3, 8+4h..8+4h+3} of each 16-key chunk, the key order in which
 //    the score accumulator layout holds P.
 //  * Software pipeline inside each wave: the MFMAs that form the scores of
-//    tile t+1 issue among the exponent FMAs and half of the exponentials of
-//    tile t, and the P V MFMAs of tile t among the other exponentials, the
-//    16-bit conversions and the row sums.
+//    tile t+1 issue among the exponentials of tile t, and the P V MFMAs of
+//    tile t among the 16-bit conversions and the row sums.  With D = 64 the
+//    K fragments of the step are read first and the exponent FMAs, the
+//    tile maximum and the lazy check run while those reads are in flight;
+//    with D = 96, 128 (no room for the fragments) the score MFMAs start at
+//    once and the check follows.
 //  * Softmax runs in base 2: p = exp2(s * c - m * c) with c = |scale| *
 //    log2(e) in one FMA; a negative scale flips the sign of Q.  p is formed
 //    with the running maximum as it stands and checked afterwards: only
@@ -309,12 +312,12 @@ void fa_forward_kernel(Args a) {
   const int t_lo = split * ntiles / a.splits;
   const int t_hi = (split + 1) * ntiles / a.splits;
 
-  // Direct global -> LDS loads of tile t, through a buffer resource whose
-  // range starts at the tile's first key and ends at key N, so rows past N
-  // read as zero (the hardware range check).  Load i of this thread fills
-  // chunk p = i * NT + tid of the tile: row p / CPR, physical chunk p % CPR,
-  // which holds logical chunk (p % CPR) ^ swz(row).  Chunks past D (D = 96)
-  // are not loaded.
+  // Direct global -> LDS loads of the next tile, through a buffer resource
+  // whose range starts at the tile's first key and ends at key N, so rows
+  // past N read as zero (the hardware range check).  Load i of this thread
+  // fills chunk p = i * NT + tid of the tile: row p / CPR, physical chunk
+  // p % CPR, which holds logical chunk (p % CPR) ^ swz(row).  Chunks past D
+  // (D = 96) are not loaded.
   uint32_t koff[LOADS], voff[LOADS];
   bool kpred[LOADS], vpred[LOADS];
 #pragma unroll
@@ -326,18 +329,21 @@ void fa_forward_kernel(Args a) {
     kpred[i] = DP == D || (pc ^ k_swz<DP>(row)) < D / 8;
     vpred[i] = DP == D || (pc ^ v_swz(row)) < D / 8;
   }
-  auto tile_load = [&](int t, uint16_t* kdst, uint16_t* vdst) {
+  // Tiles are loaded once each, in increasing order, so the loads follow a
+  // running pointer and byte count (wave-uniform) instead of forming the
+  // tile's address from its index.  The byte counts run from the tile's
+  // first key to key N: max(N, 64) row strides stay below 2^32 (checked by
+  // the host), so the unsigned arithmetic does not wrap.
+  [[maybe_unused]] const char* k_next = (const char*)K + (size_t)t_lo * BN * ldk * 2;
+  [[maybe_unused]] const char* v_next = (const char*)V + (size_t)t_lo * BN * ldv * 2;
+  [[maybe_unused]] uint32_t k_left = (uint32_t)(N - t_lo * BN) * (uint32_t)(2 * ldk);
+  [[maybe_unused]] uint32_t v_left = (uint32_t)(N - t_lo * BN) * (uint32_t)(2 * ldv);
+  auto load_next_tile = [&](uint16_t* kdst, uint16_t* vdst) {
 #if defined(__HIP_DEVICE_COMPILE__)  // buffer resources exist in device code only
-    const int k0 = t * BN;
-    // bytes from key k0 to key N (max(N, 64) row strides stay below 2^32,
-    // checked by the host), formed in unsigned arithmetic, passed as the
-    // 32-bit record count; rows past N read as zero
-    const int kbytes = (int)((uint32_t)(N - k0) * (uint32_t)(2 * ldk));
-    const int vbytes = (int)((uint32_t)(N - k0) * (uint32_t)(2 * ldv));
     const __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(K + (size_t)k0 * ldk), 0, kbytes, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc((void*)k_next, 0, (int)k_left, 0x00020000);
     const __amdgpu_buffer_rsrc_t rv =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(V + (size_t)k0 * ldv), 0, vbytes, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc((void*)v_next, 0, (int)v_left, 0x00020000);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const size_t at = (size_t)(i * NT + wave * 64) * 8;
@@ -348,6 +354,10 @@ void fa_forward_kernel(Args a) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rv, (__attribute__((address_space(3))) void*)(vdst + at), 16, voff[i], 0, 0, 0);
     }
+    k_next += (size_t)BN * ldk * 2;
+    v_next += (size_t)BN * ldv * 2;
+    k_left -= (uint32_t)(BN * 2 * ldk);
+    v_left -= (uint32_t)(BN * 2 * ldv);
 #endif
   };
 
@@ -386,33 +396,69 @@ void fa_forward_kernel(Args a) {
     return (t * BN + BN > N) || (CAUSAL && (t * BN + BN - 1 > q0));
   };
 
-  // The work of one tile.  The exponents x = s*c - m*c are formed with the
-  // running maximum m as it stands, and the next tile's scores (MFMA) issue
-  // among them; p = exp2(x) for the first key block follows.  Only then is
-  // the tile checked: when some x of the wave exceeds kLazy (and always on
-  // the first tile, when m is still -inf) the wave takes the rare path that
-  // raises m to the true row maximum, rescales O and the denominator by
-  // exp(m_old - m_new), and forms x and p again.  Otherwise m stays, p may
-  // reach 2^kLazy, and no rescale is needed; the result is the same softmax
-  // for any m.  Then the second key block's p, the conversion of P to 16
-  // bits, the row sums and P V.  The next tile's scores are computed even
-  // when that tile is not used (past the end, or causally masked for this
-  // wave); masked scores are -inf and c > 0, so their p is exactly 0.
+  // V^T fragment for P V: keys 16*kc .. +15 (in the P key order), head-dim
+  // columns 32*db .. +31.  Rows 16*kc + tr_row and +8 share the swizzle
+  // (row & 3); both addresses are formed from the slot base (derived one
+  // from the other, the second read lost the alias information that lets
+  // the compiler see it does not touch the slot being loaded).
+  auto v_frag = [&](const uint16_t* vt, int kc, int db) -> u32x4 {
+    const int col = 2 * 8 * ((4 * db) ^ tr_chunk_lo) + tr_byte;  // bytes
+    const u32x2 v0 = tr_read((const uint16_t*)((const char*)vt + (16 * kc + tr_row) * DP * 2 + col));
+    const u32x2 v1 = tr_read((const uint16_t*)((const char*)vt + (16 * kc + 8 + tr_row) * DP * 2 + col));
+    return u32x4{v0[0], v0[1], v1[0], v1[1]};
+  };
+
+  // The work of one tile: softmax of the tile whose scores sc were computed
+  // in the previous step, the scores sn of the next tile, and P V.  The
+  // exponents x = s*c - m*c are formed with the running maximum m as it
+  // stands, and the tile is checked: when some x of the wave exceeds kLazy
+  // (and always on the first tile, when m is still -inf) the wave takes the
+  // rare path that raises m to the true row maximum, rescales O and the
+  // denominator by exp(m_old - m_new), and forms x again.  Otherwise m
+  // stays, p = exp2(x) may reach 2^kLazy, and no rescale is needed; the
+  // result is the same softmax for any m.  The next tile's scores are
+  // computed even when that tile is not used (past the end, or causally
+  // masked for this wave); masked scores are -inf and c > 0, so their p is
+  // exactly 0.
+  //
+  // Two orders, the same arithmetic.  With D = 64 (check_first) the wave
+  // issues its K fragment reads, forms x, the maximum and the check while
+  // they are in flight, then issues the V fragment reads and the next
+  // tile's MFMAs with all exponentials beside them, then the 16-bit P, the
+  // row sums and P V.
+  // With D = 96, 128 the fragments would not fit in registers beside the
+  // larger accumulators: the next tile's MFMAs issue among the exponent
+  // FMAs and the first key block's exponentials (reading K as they go),
+  // the check follows, and V is read during P V.
+  constexpr bool check_first = D == 64;
   auto tile_body = [&](const uint16_t* kt_next, const uint16_t* vt, f32x16 (&sc)[2],
                        f32x16 (&sn)[2], bool first) {
+    [[maybe_unused]] u32x4 kf[DC][2], vf[4][DB];
+    if constexpr (check_first) {
+#pragma unroll
+      for (int ch = 0; ch < DC; ++ch)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int row = 32 * kb + l32;
+          const int pc = (2 * ch + hi) ^ k_swz<DP>(row);
+          kf[ch][kb] = *(const u32x4*)(kt_next + row * DP + 8 * pc);
+        }
+    }
     float x[2][16];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) x[kb][e] = __builtin_fmaf(sc[kb][e], c, -mc);
-    qk(kt_next, sn);
+    if constexpr (!check_first) qk(kt_next, sn);
     const float xmax = max32(x);
     float p[2][16];
+    if constexpr (!check_first) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      p[0][e] = __builtin_amdgcn_exp2f(x[0][e]);
-      // issue these beside the MFMAs above, not after the check below
-      asm volatile("" ::"v"(p[0][e]));
+      for (int e = 0; e < 16; ++e) {
+        p[0][e] = __builtin_amdgcn_exp2f(x[0][e]);
+        // issue these beside the MFMAs above, not after the check below
+        asm volatile("" ::"v"(p[0][e]));
+      }
     }
     if (__builtin_amdgcn_ballot_w64(first || xmax > kLazy)) {
       // keeps the compiler from turning this rare path into selects that
@@ -436,6 +482,22 @@ void fa_forward_kernel(Args a) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) x[kb][e] = __builtin_fmaf(sc[kb][e], c, -mc);
+      if constexpr (!check_first) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) p[0][e] = __builtin_amdgcn_exp2f(x[0][e]);
+      }
+    }
+    if constexpr (check_first) {
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) vf[kc][db] = v_frag(vt, kc, db);
+      sn[0] = f32x16{};
+      sn[1] = f32x16{};
+#pragma unroll
+      for (int ch = 0; ch < DC; ++ch)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) sn[kb] = Ops<T>::mma(kf[ch][kb], qf[ch], sn[kb]);
 #pragma unroll
       for (int e = 0; e < 16; ++e) p[0][e] = __builtin_amdgcn_exp2f(x[0][e]);
     }
@@ -462,16 +524,9 @@ void fa_forward_kernel(Args a) {
       }
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        // rows 16*kc + tr_row and +8 share the swizzle (row & 3); both
-        // addresses are formed from the slot base (derived one from the
-        // other, the second read lost the alias information that lets the
-        // compiler see it does not touch the slot being loaded)
-        const int col = 2 * 8 * ((4 * db) ^ tr_chunk_lo) + tr_byte;  // bytes
-        const u32x2 v0 = tr_read((const uint16_t*)((const char*)vt + (16 * kc + tr_row) * DP * 2 + col));
-        const u32x2 v1 = tr_read((const uint16_t*)((const char*)vt + (16 * kc + 8 + tr_row) * DP * 2 + col));
-        const u32x4 vf = {v0[0], v0[1], v1[0], v1[1]};
-        oacc[db] = Ops<T>::mma(vf, pf, oacc[db]);
-        if constexpr (SPLIT_P) oacc[db] = Ops<T>::mma(vf, pfl, oacc[db]);
+        const u32x4 v = check_first ? vf[kc][db] : v_frag(vt, kc, db);
+        oacc[db] = Ops<T>::mma(v, pf, oacc[db]);
+        if constexpr (SPLIT_P) oacc[db] = Ops<T>::mma(v, pfl, oacc[db]);
       }
     }
   };
@@ -483,8 +538,8 @@ void fa_forward_kernel(Args a) {
   using I3 = std::integral_constant<int, 3>;
   f32x16 sA[2], sB[2];
   if (t_lo < t_hi) {
-    tile_load(t_lo, kbuf(I0{}), vbuf(I0{}));
-    if (t_lo + 1 < t_hi) tile_load(t_lo + 1, kbuf(I1{}), vbuf(I1{}));
+    load_next_tile(kbuf(I0{}), vbuf(I0{}));
+    if (t_lo + 1 < t_hi) load_next_tile(kbuf(I1{}), vbuf(I1{}));
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
     // the first tile of the range holds the first key that any row of the
@@ -505,7 +560,7 @@ void fa_forward_kernel(Args a) {
     // transpose reads below passes a wait for the loads of step t-1
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile t+1 has landed
     __syncthreads();
-    if (t + 2 < t_hi) tile_load(t + 2, kbuf(Pre2{}), vbuf(Pre2{}));
+    if (t + 2 < t_hi) load_next_tile(kbuf(Pre2{}), vbuf(Pre2{}));
     if (live(t)) {
       if (is_edge(t)) {  // ragged / causal masks
         const int k0 = t * BN;
