@@ -365,18 +365,21 @@ void fa_forward_kernel(Args a) {
   // the score of key k0 + 32*kb + 8*(e/4) + 4*hi + (e%4) against query
   // qrow.  The two key blocks form independent MFMA chains, issued
   // alternately.
+  // Byte offset of this lane's K operand chunk ch within a tile (key block
+  // 0; key block 1 is 32 rows further, with the same swizzle).
+  uint32_t k_off[DC];
+#pragma unroll
+  for (int ch = 0; ch < DC; ++ch) k_off[ch] = (l32 * DP + 8 * ((2 * ch + hi) ^ k_swz<DP>(l32))) * 2;
+  auto k_frag = [&](const uint16_t* kt, int ch, int kb) -> u32x4 {
+    return *(const u32x4*)((const char*)kt + k_off[ch] + kb * (32 * DP * 2));
+  };
   auto qk = [&](const uint16_t* kt, f32x16 (&s)[2]) {
     s[0] = f32x16{};
     s[1] = f32x16{};
 #pragma unroll
     for (int ch = 0; ch < DC; ++ch)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int row = 32 * kb + l32;
-        const int pc = (2 * ch + hi) ^ k_swz<DP>(row);
-        const u32x4 kf = *(const u32x4*)(kt + row * DP + 8 * pc);
-        s[kb] = Ops<T>::mma(kf, qf[ch], s[kb]);
-      }
+      for (int kb = 0; kb < 2; ++kb) s[kb] = Ops<T>::mma(k_frag(kt, ch, kb), qf[ch], s[kb]);
   };
 
   // V^T transpose-read source of this lane: within each 16-lane group g,
@@ -401,11 +404,23 @@ void fa_forward_kernel(Args a) {
   // (row & 3); both addresses are formed from the slot base (derived one
   // from the other, the second read lost the alias information that lets
   // the compiler see it does not touch the slot being loaded).
+  uint32_t v_off[DB];  // bytes: row tr_row, the lane's columns of block db
+#pragma unroll
+  for (int db = 0; db < DB; ++db) v_off[db] = tr_row * DP * 2 + 2 * 8 * ((4 * db) ^ tr_chunk_lo) + tr_byte;
   auto v_frag = [&](const uint16_t* vt, int kc, int db) -> u32x4 {
-    const int col = 2 * 8 * ((4 * db) ^ tr_chunk_lo) + tr_byte;  // bytes
-    const u32x2 v0 = tr_read((const uint16_t*)((const char*)vt + (16 * kc + tr_row) * DP * 2 + col));
-    const u32x2 v1 = tr_read((const uint16_t*)((const char*)vt + (16 * kc + 8 + tr_row) * DP * 2 + col));
+    const u32x2 v0 = tr_read((const uint16_t*)((const char*)vt + v_off[db] + 16 * kc * DP * 2));
+    const u32x2 v1 = tr_read((const uint16_t*)((const char*)vt + v_off[db] + (16 * kc + 8) * DP * 2));
     return u32x4{v0[0], v0[1], v1[0], v1[1]};
+  };
+  // Marks the lane offsets as redefined: otherwise the compiler forms the
+  // address of every (ring slot, chunk) pair once before the loop and keeps
+  // them all in registers (48 at D = 128, which spills), instead of adding
+  // the slot base as the instruction's immediate offset.
+  auto refresh_offsets = [&]() {
+#pragma unroll
+    for (int ch = 0; ch < DC; ++ch) asm volatile("" : "+v"(k_off[ch]));
+#pragma unroll
+    for (int db = 0; db < DB; ++db) asm volatile("" : "+v"(v_off[db]));
   };
 
   // The work of one tile: softmax of the tile whose scores sc were computed
@@ -433,16 +448,13 @@ void fa_forward_kernel(Args a) {
   constexpr bool check_first = D == 64;
   auto tile_body = [&](const uint16_t* kt_next, const uint16_t* vt, f32x16 (&sc)[2],
                        f32x16 (&sn)[2], bool first) {
+    refresh_offsets();
     [[maybe_unused]] u32x4 kf[DC][2], vf[4][DB];
     if constexpr (check_first) {
 #pragma unroll
       for (int ch = 0; ch < DC; ++ch)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const int row = 32 * kb + l32;
-          const int pc = (2 * ch + hi) ^ k_swz<DP>(row);
-          kf[ch][kb] = *(const u32x4*)(kt_next + row * DP + 8 * pc);
-        }
+        for (int kb = 0; kb < 2; ++kb) kf[ch][kb] = k_frag(kt_next, ch, kb);
     }
     float x[2][16];
 #pragma unroll
