@@ -82,13 +82,17 @@ def kernel_source_hash(dtype: str, sources=None) -> str:
 
 def committed_traffic(name: str, sources=None):
     """HBM bytes per call from a committed counter profile (traffic_<name>.json,
-    name = a workload, or "naive_" + a workload) of the current kernel
-    source, or None."""
+    name = a workload, or "naive_" / "cold_" + a workload) of the current
+    kernel source, or None."""
     path = os.path.join(PROFILE_DIR, f"traffic_{name}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    dtype = workloads.get(name[len("naive_"):] if name.startswith("naive_") else name).dtype
+    base = name
+    for prefix in ("naive_", "cold_"):
+        if base.startswith(prefix):
+            base = base[len(prefix):]
+    dtype = workloads.get(base).dtype
     if rec.get("kernel_source_hash") != kernel_source_hash(dtype, sources):
         return None
     return rec.get("hbm_bytes_per_launch")
@@ -205,6 +209,10 @@ def main():
                          "suggestion for this device); 1 times fa_forward itself")
     ap.add_argument("--no-naive", action="store_true",
                     help="skip the three-pass comparison leg (16-bit storage only)")
+    ap.add_argument("--cold-flush-mib", type=int, default=0,
+                    help="cold-cache run: before every launch, write a buffer of this many MiB "
+                         "(512 evicts L2 and the 256 MB Infinity Cache); each launch is timed on its own "
+                         "and value is from their median")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of attention, time a plain device copy of this many MiB "
                          "(reference kernel for scaling HBM byte counters)")
@@ -287,13 +295,25 @@ def main():
                  float(w.scale), int(w.causal), code, splits, ws.data_ptr(), ws.numel(),
                  stream.cuda_stream)
 
-    def step():
+    def launch():
         if strided:
             st = lib.fa_forward_strided(*sargs)
         else:
             st = lib.fa_forward(*cargs) if splits == 1 else lib.fa_forward_ex(*xargs)
         if st != 0:
             raise fa.FAError(st)
+
+    # Cold-cache mode: every launch follows a write of the flush buffer, so
+    # no input is left in L2 or the Infinity Cache.
+    cold = args.cold_flush_mib > 0
+    flush_buf = torch.empty(args.cold_flush_mib * 2 ** 20, dtype=torch.uint8, device=dev) if cold else None
+    flushes = [0]
+
+    def step():
+        if cold:
+            flushes[0] += 1
+            flush_buf.fill_(flushes[0] & 0xFF)
+        launch()
 
     # Clock settle, then the W warm-up steps; neither is timed.
     settle_launches = 0
@@ -308,17 +328,33 @@ def main():
     torch.cuda.synchronize()
 
     # Timed region: K back-to-back launches between two events recorded on
-    # the stream the kernel runs on.
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    total_ms = ev0.elapsed_time(ev1)
-    ms_per_step = total_ms / args.steps
+    # the stream the kernel runs on.  Cold: K launches, each after a flush
+    # and between its own pair of events (the flush is not timed); the
+    # median launch stands for the step.
+    if cold:
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for e0, e1 in pairs:
+            flushes[0] += 1
+            flush_buf.fill_(flushes[0] & 0xFF)
+            e0.record(stream)
+            launch()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        cold_us = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in pairs)
+        ms_per_step = float(np.median(cold_us)) * 1e-3
+    else:
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            step()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        total_ms = ev0.elapsed_time(ev1)
+        ms_per_step = total_ms / args.steps
     flops = workloads.flops(w)
     value = flops / (ms_per_step * 1e-3) / 1e12
     # Per-launch duration of the forward kernel: the launches are
@@ -329,23 +365,27 @@ def main():
     kern_us = ms_per_step * 1e3
     achieved = flops / (kern_us * 1e-6) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    log(f"mean launch {kern_us:.2f} us over {args.steps} back-to-back launches")
+    if cold:
+        log(f"cold: median launch {kern_us:.2f} us over {args.steps} launches, each after a "
+            f"{args.cold_flush_mib} MiB flush")
+    else:
+        log(f"mean launch {kern_us:.2f} us over {args.steps} back-to-back launches")
 
     # Median of individually bracketed launches (each with its own event
     # pair, so it includes the event overhead; reported beside the mean).
-    singles = []
-    for _ in range(max(20, min(args.steps, 50))):
+    singles = cold_us if cold else []
+    for _ in range(0 if cold else max(20, min(args.steps, 50))):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        step()
+        launch()
         e1.record(stream)
         e1.synchronize()
         singles.append(e0.elapsed_time(e1) * 1e3)
     median_single_us = float(np.median(singles))
 
     naive = None
-    if w.dtype != "f32" and not args.no_naive and not strided:
+    if w.dtype != "f32" and not args.no_naive and not strided and not cold:
         naive = naive_leg(w, q, k, v, o, stream, code, lib, max(10, min(args.steps, 50)), ms_per_step)
 
     rec = {
@@ -363,7 +403,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D,
                    "storage": w.dtype, "causal": w.causal, "parallelism": "none (1 GPU)",
-                   "splits": splits, "layout": args.layout, "kv_heads": kvh},
+                   "splits": splits, "layout": args.layout, "kv_heads": kvh,
+                   "cache": f"cold ({args.cold_flush_mib} MiB written before each launch)" if cold
+                   else "warm (back-to-back launches)"},
         "pct_peak": round(100 * value / peak, 2),
         "roofline": {
             "bound": "mfma",
@@ -372,7 +414,8 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
             # the committed counter profile is of the dense, unsplit workload
-            "traffic": committed_traffic(w.name) if (not strided and splits == 1 and not args.heads) else None,
+            "traffic": committed_traffic(("cold_" if cold else "") + w.name)
+            if (not strided and splits == 1 and not args.heads) else None,
             "kernel_us_mean": round(kern_us, 3),
             "min_bytes": workloads.min_bytes(w) * (w.H + kvh) // (2 * w.H),
         },
