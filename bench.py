@@ -422,7 +422,7 @@ def main():
         "median_single_launch_us": round(median_single_us, 3),
         "untimed_settle": {"seconds": args.settle_s, "launches": settle_launches},
         "device": {"name": prop.name, "arch": getattr(prop, "gcnArchName", ""),
-                   "cus": prop.multi_processor_count,
+                   "cus": prop.multi_processor_count, "max_clock_mhz": round(fa.fa_device_info()[1] / 1000),
                    "peak_used": f"dense {w.dtype} matrix-core peak {peak} TFLOP/s (published)"},
         "inputs_sha256_16": input_sha,
         "kernel_source_hash": kernel_source_hash(w.dtype),

@@ -253,6 +253,13 @@ int fa_naive_forward(const void* q, const void* k, const void* v, void* o, int64
                      int64_t N, int64_t D, float scale, int causal, int dtype, void* workspace,
                      int64_t workspace_bytes, void* stream);
 
+/* Properties of the current HIP device that a measurement reports beside its
+ * figures: *cus = compute units, *max_clock_khz = peak shader clock (kHz),
+ * both from the HIP runtime.  Either pointer may be NULL.  Returns FA_OK, or
+ * FA_ERR_DEVICE when no device is current or the runtime refuses the query
+ * (outputs untouched).  Synchronous; enqueues nothing. */
+int fa_device_info(int* cus, int* max_clock_khz);
+
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* fa_status_string(int status);
 

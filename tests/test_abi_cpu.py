@@ -87,6 +87,16 @@ def test_validation(lib, args, status):
     assert fa.STATUS_NAMES[got] == status
 
 
+def test_device_info_without_device(lib):
+    import ctypes
+    cus, clk = ctypes.c_int(-7), ctypes.c_int(-7)
+    got = lib.fa_device_info(ctypes.byref(cus), ctypes.byref(clk))
+    if got == 0:
+        pytest.skip("a device is present; the no-device path is not reachable")
+    assert fa.STATUS_NAMES[got] == "FA_ERR_DEVICE"
+    assert (cus.value, clk.value) == (-7, -7)  # outputs untouched on error
+
+
 # ------------------------------------------------- three-pass entry points
 
 def _ws(B, H, N, dt):

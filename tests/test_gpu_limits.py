@@ -86,3 +86,11 @@ def test_long_bf16_d128_bnhd_mqa():
     vx = np.ascontiguousarray(np.repeat(xkv["v"], w.H, axis=1))
     ref = oracle.rows(xq["q"], kx, vx, "bf16", w.scale, True, bh, ri)
     parity(to_numpy64(o.contiguous()).reshape(w.H, w.N, w.D)[bh, ri], ref, "bf16", "bnhd mqa long")
+
+
+def test_device_info():
+    cus, clk = fa.fa_device_info()
+    prop = torch.cuda.get_device_properties(torch.cuda.current_device())
+    assert cus == prop.multi_processor_count
+    assert 500_000 <= clk <= 5_000_000  # kHz
+    assert fa.load_library().fa_device_info(None, None) == 0

@@ -27,9 +27,9 @@ STATUS_NAMES = {
 }
 
 # Every symbol include/fa.h declares.
-EXPORTS = ("fa_forward", "fa_forward_ex", "fa_forward_ex_workspace_bytes", "fa_forward_strided",
-           "fa_naive_forward", "fa_naive_workspace_bytes", "fa_splitkv_suggest", "fa_status_string",
-           "fa_version")
+EXPORTS = ("fa_device_info", "fa_forward", "fa_forward_ex", "fa_forward_ex_workspace_bytes",
+           "fa_forward_strided", "fa_naive_forward", "fa_naive_workspace_bytes", "fa_splitkv_suggest",
+           "fa_status_string", "fa_version")
 
 _lib = None
 
@@ -74,6 +74,8 @@ def load_library():
     lib.fa_naive_forward.restype = ctypes.c_int
     lib.fa_naive_workspace_bytes.argtypes = [i64, i64, i64, ctypes.c_int]
     lib.fa_naive_workspace_bytes.restype = i64
+    lib.fa_device_info.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
+    lib.fa_device_info.restype = ctypes.c_int
     lib.fa_status_string.argtypes = [ctypes.c_int]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
@@ -88,6 +90,15 @@ def fa_status_string(status: int) -> str:
 
 def fa_version() -> str:
     return load_library().fa_version().decode()
+
+
+def fa_device_info():
+    """(compute units, peak shader clock in kHz) of the current device."""
+    cus, clk = ctypes.c_int(0), ctypes.c_int(0)
+    st = load_library().fa_device_info(ctypes.byref(cus), ctypes.byref(clk))
+    if st != 0:
+        raise FAError(st)
+    return cus.value, clk.value
 
 
 def fa_forward_raw(q: int, k: int, v: int, o: int, B: int, H: int, N: int, D: int, scale: float,

@@ -471,6 +471,17 @@ const char* fa_status_string(int status) {
   }
 }
 
+int fa_device_info(int* cus, int* max_clock_khz) {
+  int dev = -1, n = 0, clk = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FA_ERR_DEVICE;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipDeviceGetAttribute(&clk, hipDeviceAttributeClockRate, dev) != hipSuccess)
+    return FA_ERR_DEVICE;
+  if (cus != nullptr) *cus = n;
+  if (max_clock_khz != nullptr) *max_clock_khz = clk;
+  return FA_OK;
+}
+
 const char* fa_version(void) { return "fa-mi355x 0.1.0 gfx950"; }
 
 }  // extern "C"
