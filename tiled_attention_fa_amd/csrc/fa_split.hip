@@ -12,7 +12,8 @@
 //   lse = M + ln sum_r exp(lse_r - M),   M = max_r lse_r
 //   O   = sum_r exp(lse_r - lse) O_r
 //
-// A range that held no visible key of the row has lse_r = -inf and weight 0.
+// A range that held no visible key of the row has lse_r = -inf, O_r = 0 and
+// weight 0.
 // One thread per 4 consecutive columns of a row; the partials are fp32,
 // [splits, rows, D] and [splits, rows].
 #include <hip/hip_runtime.h>
@@ -54,15 +55,19 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeProblem p) {
     const int64_t row = idx / G;
     const int g = (int)(idx - row * G);
     float M = -INFINITY;
+#pragma unroll 4
     for (int s = 0; s < p.splits; ++s) M = fmaxf(M, p.part_lse[s * p.rows + row]);
     float L = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // unrolled so that the loads of several ranges are in flight at once; a
+    // range with no visible key (lse_r = -inf, O_r = 0) gets weight 0
+#pragma unroll 4
     for (int s = 0; s < p.splits; ++s) {
       const float ls = p.part_lse[s * p.rows + row];
-      if (ls == -INFINITY) continue;  // no visible key in this range
-      const float w = expf(ls - M);
+      const f32x4 o = *(const f32x4*)(p.part_o + ((size_t)s * p.rows + row) * p.D + 4 * g);
+      const float w = ls == -INFINITY ? 0.f : expf(ls - M);
       L += w;
-      acc += w * *(const f32x4*)(p.part_o + ((size_t)s * p.rows + row) * p.D + 4 * g);
+      acc += w * o;
     }
     store4<OutT>(p.o, (size_t)row * p.D + 4 * g, acc * (1.f / L));
     if (p.lse != nullptr && g == 0) p.lse[row] = M + logf(L);
