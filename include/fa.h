@@ -83,7 +83,12 @@ typedef enum fa_status {
  * The call is asynchronous: it validates its arguments on the host,
  * enqueues one kernel on `stream` and returns.  The caller owns all buffers
  * and synchronises.  The library holds no state between calls apart from a
- * per-device cache of the device check, and allocates nothing.
+ * per-device cache of the device check and CU count, and allocates nothing.
+ * When B*H times the 16-bit kernel's query blocks fill at most half of the
+ * device's workgroup slots (few heads, short rows), each workgroup's waves
+ * split its key tiles in two groups whose partial results are merged in
+ * LDS by the rescaling rule of the online softmax; the arithmetic order
+ * changes, the result agrees to the same tolerance.
  * Pointers must be device memory of the current HIP device.
  * Returns FA_OK or a negative fa_status.
  */
@@ -187,6 +192,23 @@ int64_t fa_forward_ex_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D
  * FA_ERR_DEVICE when no device is current).
  */
 int fa_splitkv_suggest(int64_t B, int64_t H, int64_t N, int64_t D, int dtype, int causal);
+
+/*
+ * fa_key_groups_suggest -- how many key groups the workgroups of fa_forward,
+ * fa_forward_strided and fa_forward_ex (with one key range) use on the
+ * current device for these sizes: 2 when dtype is FA_F16 or FA_BF16, N > 64
+ * and B*H times the one-group kernel's query blocks (256 rows; 128 for
+ * causal D = 64 and for D = 96) fill at most half of the device's workgroup
+ * slots (one per CU; two for causal D = 64), else 1.  With 2 the waves of a
+ * workgroup (64 query rows) form two groups that take alternate key tiles,
+ * and their running maxima, denominators and accumulators are merged in
+ * LDS by the rescaling rule of the online softmax ("Android Transformer
+ * Optimization: Attention and Mobile GPU Bottlenecks", section "A Complete
+ * Tile Loop").  Host only; returns 1, 2 or a negative fa_status
+ * (FA_ERR_DTYPE, FA_ERR_DIM, FA_ERR_UNSUPPORTED_D, FA_ERR_TOO_LARGE,
+ * FA_ERR_DEVICE when no device is current).
+ */
+int fa_key_groups_suggest(int64_t B, int64_t H, int64_t N, int64_t D, int dtype, int causal);
 
 /*
  * The three-pass ("naive") attention that tiling is measured against:

@@ -15,6 +15,7 @@ import numpy as np
 import torch
 
 import tiled_attention_fa_amd as fa
+from workloads import make_inputs
 
 TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 ABS_TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-3}
@@ -66,3 +67,44 @@ def parity(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = "") -> dict
     else:
         assert max_abs <= ABS_TOL[dtype], f"{what}: max abs error {max_abs:.3e} > {ABS_TOL[dtype]}"
     return {"max_abs": max_abs}
+
+
+# ---- strided layouts and grouped key/value heads
+
+def bits_to(t_bits, dtype, layout, device="cuda:0", pad=0):
+    """Dense [B, Hx, N, D] storage bits -> a device tensor viewed as
+    [B, Hx, N, D] in the given memory layout: "bhnd" dense, "bnhd" with
+    heads inside rows, "pad" with each row padded by `pad` elements."""
+    a = np.ascontiguousarray(t_bits)
+    host = torch.from_numpy(a if dtype == "f32" else a.view(np.int16)).view(TORCH_DTYPES[dtype])
+    B, Hx, N, D = host.shape
+    if layout == "bhnd":
+        return host.to(device)
+    if layout == "bnhd":
+        return host.permute(0, 2, 1, 3).contiguous().to(device).permute(0, 2, 1, 3)
+    if layout == "pad":
+        buf = torch.zeros((B, Hx, N, D + pad), dtype=host.dtype)
+        buf[..., :D] = host
+        return buf.to(device)[..., :D]
+    raise ValueError(layout)
+
+
+def empty_out(B, H, N, D, dtype, layout, pad=0, device="cuda:0"):
+    t = TORCH_DTYPES[dtype]
+    if layout == "bhnd":
+        return torch.empty((B, H, N, D), dtype=t, device=device)
+    if layout == "bnhd":
+        return torch.empty((B, N, H, D), dtype=t, device=device).permute(0, 2, 1, 3)
+    return torch.empty((B, H, N, D + pad), dtype=t, device=device)[..., :D]
+
+
+def make_gqa_inputs(w, H_kv):
+    """Q with H heads, K and V with H_kv heads (the workload recipe drawn at
+    H_kv heads for K and V)."""
+    xq = make_inputs(w)
+    xkv = make_inputs(w.with_(H=H_kv, seed=w.seed + 1))
+    return xq["q"], xkv["k"], xkv["v"]
+
+
+def expand(bits, group):
+    return np.ascontiguousarray(np.repeat(bits, group, axis=1))

@@ -257,6 +257,16 @@ def test_splitkv_suggest_without_device(lib):
     assert fa.STATUS_NAMES[fa.fa_splitkv_suggest(1, 32, 2048, 80, 1, False)] == "FA_ERR_UNSUPPORTED_D"
 
 
+def test_key_groups_suggest_without_device(lib):
+    got = fa.fa_key_groups_suggest(1, 8, 1000, 96, 1, False)
+    if got >= 1:
+        pytest.skip("a device is present")
+    assert fa.STATUS_NAMES[got] == "FA_ERR_DEVICE"
+    assert fa.STATUS_NAMES[fa.fa_key_groups_suggest(1, 8, 1000, 80, 1, False)] == "FA_ERR_UNSUPPORTED_D"
+    assert fa.STATUS_NAMES[fa.fa_key_groups_suggest(1, 8, 1000, 64, 7, False)] == "FA_ERR_DTYPE"
+    assert fa.STATUS_NAMES[fa.fa_key_groups_suggest(0, 8, 1000, 64, 1, False)] == "FA_ERR_DIM"
+
+
 # ------------------------------------------------------ fa_forward_strided
 
 DENSE = (4 * 64 * 64, 64 * 64, 64)          # [B, H=4, N=64, D=64]
@@ -320,10 +330,12 @@ def test_tune_library_exports_its_header():
     exported = set(re.findall(r"\bT (fa_\w+)", out))
     for n in names + list(EXPORTS):
         assert n in exported, n
-    assert tile_sweep.shapes(lib, 64) == [(2, 1), (4, 1), (4, 2), (8, 1)]
-    assert tile_sweep.shapes(lib, 96) == [(2, 1), (4, 1), (8, 1)]
-    assert tile_sweep.shapes(lib, 128) == [(2, 1), (4, 1), (8, 1)]
-    assert lib.fa_tune_shapes(80, None, None, 0) == -3
+    assert tile_sweep.shapes(lib, 64) == [(2, 1, 1), (4, 1, 1), (4, 2, 1), (8, 1, 1), (4, 1, 2), (4, 2, 2),
+                                          (8, 1, 2)]
+    wide = [(2, 1, 1), (4, 1, 1), (8, 1, 1), (4, 1, 2), (8, 1, 2)]
+    assert tile_sweep.shapes(lib, 96) == wide
+    assert tile_sweep.shapes(lib, 128) == wide
+    assert lib.fa_tune_shapes(80, None, None, None, 0) == -3
 
 
 @pytest.mark.parametrize("args,status", [
@@ -331,16 +343,19 @@ def test_tune_library_exports_its_header():
     (dict(B=0), "FA_ERR_DIM"),
     (dict(waves=3), "FA_ERR_UNSUPPORTED_D"),
     (dict(D=128, waves=4, occ=2), "FA_ERR_UNSUPPORTED_D"),
+    (dict(D=128, waves=4, occ=2, ks=2), "FA_ERR_UNSUPPORTED_D"),
+    (dict(waves=2, occ=1, ks=2), "FA_ERR_UNSUPPORTED_D"),
+    (dict(ks=3), "FA_ERR_UNSUPPORTED_D"),
     (dict(o=A), "FA_ERR_ALIAS"),
     (dict(), "FA_ERR_DEVICE"),
 ])
 def test_tune_forward_validation(args, status):
     from tiled_attention_fa_amd import tile_sweep
     lib = tile_sweep.load_tune()
-    kw = dict(q=A, k=B_, v=C, o=O, B=1, H=1, N=64, D=64, dtype=1, waves=4, occ=2)
+    kw = dict(q=A, k=B_, v=C, o=O, B=1, H=1, N=64, D=64, dtype=1, waves=4, occ=2, ks=1)
     kw.update(args)
     got = lib.fa_tune_forward(kw["q"], kw["k"], kw["v"], kw["o"], kw["B"], kw["H"], kw["N"], kw["D"],
-                              0.125, 0, kw["dtype"], kw["waves"], kw["occ"], None)
+                              0.125, 0, kw["dtype"], kw["waves"], kw["occ"], kw["ks"], None)
     if status == "FA_ERR_DEVICE" and got == 0:
         pytest.skip("a gfx950 device is present; the no-device path is not reachable")
     assert fa.STATUS_NAMES[got] == status

@@ -1,0 +1,153 @@
+"""GPU parity of the two key groups of the matrix-core kernel, and of the one
+group on the same problems, against the fp64 oracle, through the C ABI.
+
+When B*H times the query blocks leave most of the device idle (few heads,
+short rows), fa_forward, fa_forward_strided and fa_forward_ex (one key range)
+run workgroups whose waves form two groups over the same query rows, taking
+alternate key tiles; each group keeps its own running maximum, denominator
+and accumulator, and the two are merged in LDS by the rescaling rule of the
+online softmax ("Android Transformer Optimization: Attention and Mobile GPU
+Bottlenecks", sections "The Essence of FlashAttention: Reordering the
+Computation" and "A Complete Tile Loop").  fa_key_groups_suggest names the
+choice, so every case here asserts which path it runs:
+
+  * small grids: two groups (ragged N, both masks, every head dimension,
+    fp16 and bf16; rows whose second group sees no key at all);
+  * the same heads repeated until the grid fills the device: one group, on
+    the same feature matrix (log-sum-exp output, strided layouts, grouped
+    key/value heads), so that both kernels keep that coverage.
+
+Tolerances as for fa_forward (gpu_helpers) and the log-sum-exp bound of the
+split-KV tests (1e-3 for 16-bit storage).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tiled_attention_fa_amd as fa
+from gpu_helpers import bits_to, empty_out, expand, make_gqa_inputs, parity, to_device, to_numpy64
+from workloads import Workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+CODES = {"f16": 1, "bf16": 2}
+LSE_TOL = 1e-3
+CASES = [(65, (1, 2)), (129, (2, 1)), (200, (1, 3)), (1000, (2, 2))]
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def groups(B, H, N, D, dtype, causal):
+    g = fa.fa_key_groups_suggest(B, H, N, D, CODES[dtype], causal)
+    assert g in (1, 2), f"fa_key_groups_suggest returned {g}"
+    return g
+
+
+def heads_for_one_group(N, D, dtype, causal):
+    """Fewest heads (a power of two) at which B = 1 runs one key group."""
+    H = 1
+    while groups(1, H, N, D, dtype, causal) == 2:
+        H *= 2
+    return H
+
+
+def tile_heads(bits, H):
+    """[B, h, N, D] -> [B, H, N, D], head j a copy of head j % h."""
+    h = bits.shape[1]
+    reps = -(-H // h)
+    return np.ascontiguousarray(np.tile(bits, (1, reps, 1, 1))[:, :H])
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("D", [64, 96, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_two_groups_small_grid(dtype, D, causal):
+    for N, (B, H) in CASES:
+        assert groups(B, H, N, D, dtype, causal) == 2, f"N={N} B={B} H={H}: expected two key groups"
+        w = Workload(f"kg2_{dtype}_d{D}_n{N}", B, H, N, D, dtype, causal,
+                     seed=70_000 + 17 * N + D + (1 if causal else 0))
+        _say(f"[key groups 2] {w.name} causal={causal} B={B} H={H}")
+        x = make_inputs(w)
+        ref, ref_lse = oracle.forward(x["q"], x["k"], x["v"], dtype, w.scale, causal, return_lse=True)
+        q, k, v = (to_device(x[n], dtype) for n in "qkv")
+        o = fa.forward(q, k, v, scale=w.scale, causal=causal)
+        torch.cuda.synchronize()
+        parity(to_numpy64(o), ref, dtype, f"{w.name} causal={causal} fa_forward")
+        o2, lse = fa.forward_ex(q, k, v, scale=w.scale, causal=causal, num_splits=1, lse=True)
+        torch.cuda.synchronize()
+        parity(to_numpy64(o2), ref, dtype, f"{w.name} causal={causal} fa_forward_ex")
+        err = float(np.abs(lse.double().cpu().numpy() - ref_lse).max())
+        assert err <= LSE_TOL, f"{w.name} causal={causal}: lse error {err:.3e}"
+
+
+def test_one_tile_rows_take_one_group():
+    """N <= 64: a single key tile, nothing to split."""
+    for N in (1, 17, 64):
+        assert groups(1, 1, N, 64, "f16", False) == 1
+        assert groups(1, 1, N, 128, "bf16", True) == 1
+    assert groups(1, 1, 65, 64, "f16", False) == 2
+
+
+def test_full_grids_take_one_group():
+    """The benchmark workloads fill the device: one group."""
+    assert groups(1, 32, 2048, 64, "f16", False) == 1
+    assert groups(4, 32, 2048, 64, "bf16", True) == 1
+    assert groups(1, 16, 8192, 128, "f16", True) == 1
+    cus, _ = fa.fa_device_info()
+    # the ragged workload: 16 heads x 8 blocks of 128 rows, one workgroup per CU
+    assert groups(2, 8, 1000, 96, "f16", False) == (2 if 2 * 128 <= cus else 1)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("D", [64, 96, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_one_group_same_problems(dtype, D, causal):
+    """The small cases with their heads repeated until the grid takes one
+    group; every head checked against the oracle of the head it copies."""
+    for N, (B, h) in CASES[:3]:
+        H = heads_for_one_group(N, D, dtype, causal)
+        assert groups(B, H, N, D, dtype, causal) == 1
+        w = Workload(f"kg1_{dtype}_d{D}_n{N}", B, h, N, D, dtype, causal,
+                     seed=71_000 + 17 * N + D + (1 if causal else 0))
+        _say(f"[key groups 1] {w.name} causal={causal} B={B} H={H} (copies of {h} heads)")
+        x = make_inputs(w)
+        ref, ref_lse = oracle.forward(x["q"], x["k"], x["v"], dtype, w.scale, causal, return_lse=True)
+        q, k, v = (to_device(tile_heads(x[n], H), dtype) for n in "qkv")
+        o, lse = fa.forward_ex(q, k, v, scale=w.scale, causal=causal, num_splits=1, lse=True)
+        torch.cuda.synchronize()
+        parity(to_numpy64(o), tile_heads(ref, H), dtype, f"{w.name} causal={causal} one group")
+        err = float(np.abs(lse.double().cpu().numpy() - tile_heads(ref_lse[..., None], H)[..., 0]).max())
+        assert err <= LSE_TOL, f"{w.name} causal={causal}: lse error {err:.3e}"
+
+
+LAYOUTS = [("bnhd", "bnhd", "bnhd", "bnhd"), ("pad", "bhnd", "pad", "bnhd")]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_strided_gqa_both_paths(dtype, D, causal):
+    """Strided layouts with grouped key/value heads: on a small grid (two
+    groups) and with the query heads repeated to fill the device (one group;
+    the key/value heads repeated alike keep each query head's pairing)."""
+    N, H, Hkv = 200, 4, 2
+    w = Workload(f"kgs_{dtype}_d{D}", 1, H, N, D, dtype, causal, seed=72_000 + D + (1 if causal else 0))
+    q, k, v = make_gqa_inputs(w, Hkv)
+    ref = oracle.forward(q, expand(k, H // Hkv), expand(v, H // Hkv), dtype, w.scale, causal)
+    H1 = max(heads_for_one_group(N, D, dtype, causal), H)
+    for Hq, want in ((H, 2), (H1, 1)):
+        assert groups(1, Hq, N, D, dtype, causal) == want
+        rep = Hq // H
+        qb, kb, vb = tile_heads(q, Hq), tile_heads(k, Hkv * rep), tile_heads(v, Hkv * rep)
+        for layouts in LAYOUTS:
+            _say(f"[key groups {want}] {w.name} causal={causal} H={Hq} H_kv={Hkv * rep} {layouts}")
+            lq, lk, lv, lo = layouts
+            o = empty_out(1, Hq, N, D, dtype, lo, pad=8)
+            fa.fa_forward_strided(bits_to(qb, dtype, lq, pad=8), bits_to(kb, dtype, lk, pad=8),
+                                  bits_to(vb, dtype, lv, pad=8), o, scale=w.scale, causal=causal)
+            torch.cuda.synchronize()
+            parity(to_numpy64(o), tile_heads(ref, Hq), dtype, f"{w.name} causal={causal} H={Hq} {layouts}")

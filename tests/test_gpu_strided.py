@@ -16,7 +16,7 @@ import torch
 import oracle
 import tiled_attention_fa_amd as fa
 import workloads
-from gpu_helpers import TORCH_DTYPES, parity, to_numpy64
+from gpu_helpers import bits_to, empty_out, expand, make_gqa_inputs, parity, to_numpy64
 from workloads import Workload, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -24,45 +24,6 @@ pytestmark = pytest.mark.gpu
 
 def _say(msg):
     print(msg, flush=True)
-
-
-def bits_to(t_bits, dtype, layout, device="cuda:0", pad=0):
-    """Dense [B, Hx, N, D] storage bits -> a device tensor viewed as
-    [B, Hx, N, D] in the given memory layout: "bhnd" dense, "bnhd" with
-    heads inside rows, "pad" with each row padded by `pad` elements."""
-    a = np.ascontiguousarray(t_bits)
-    host = torch.from_numpy(a if dtype == "f32" else a.view(np.int16)).view(TORCH_DTYPES[dtype])
-    B, Hx, N, D = host.shape
-    if layout == "bhnd":
-        return host.to(device)
-    if layout == "bnhd":
-        return host.permute(0, 2, 1, 3).contiguous().to(device).permute(0, 2, 1, 3)
-    if layout == "pad":
-        buf = torch.zeros((B, Hx, N, D + pad), dtype=host.dtype)
-        buf[..., :D] = host
-        return buf.to(device)[..., :D]
-    raise ValueError(layout)
-
-
-def empty_out(B, H, N, D, dtype, layout, pad=0, device="cuda:0"):
-    t = TORCH_DTYPES[dtype]
-    if layout == "bhnd":
-        return torch.empty((B, H, N, D), dtype=t, device=device)
-    if layout == "bnhd":
-        return torch.empty((B, N, H, D), dtype=t, device=device).permute(0, 2, 1, 3)
-    return torch.empty((B, H, N, D + pad), dtype=t, device=device)[..., :D]
-
-
-def make_gqa_inputs(w, H_kv):
-    """Q with H heads, K and V with H_kv heads (the workload recipe drawn at
-    H_kv heads for K and V)."""
-    xq = make_inputs(w)
-    xkv = make_inputs(w.with_(H=H_kv, seed=w.seed + 1))
-    return xq["q"], xkv["k"], xkv["v"]
-
-
-def expand(bits, group):
-    return np.ascontiguousarray(np.repeat(bits, group, axis=1))
 
 
 def run_strided(q_bits, k_bits, v_bits, dtype, scale, causal, layouts, H, pad=8):

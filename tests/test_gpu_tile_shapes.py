@@ -31,9 +31,9 @@ def test_every_shape_matches_oracle(tune, dtype, D, causal):
         x = make_inputs(w)
         ref = oracle.forward(x["q"], x["k"], x["v"], dtype, w.scale, causal)
         q, k, v = (to_device(x[n], dtype) for n in "qkv")
-        for waves, occ in tile_sweep.shapes(tune, D):
-            print(f"[shape] {w.name} causal={causal} waves={waves} occ={occ}", flush=True)
+        for waves, occ, ks in tile_sweep.shapes(tune, D):
+            print(f"[shape] {w.name} causal={causal} waves={waves} occ={occ} key_groups={ks}", flush=True)
             o = torch.empty_like(q)
-            tile_sweep.tune_forward(tune, q, k, v, o, w.scale, causal, code, waves, occ, 0)
+            tile_sweep.tune_forward(tune, q, k, v, o, w.scale, causal, code, waves, occ, ks, 0)
             torch.cuda.synchronize()
-            parity(to_numpy64(o), ref, dtype, f"{w.name} causal={causal} shape {waves}x{occ}")
+            parity(to_numpy64(o), ref, dtype, f"{w.name} causal={causal} shape {waves}x{occ}x{ks}")

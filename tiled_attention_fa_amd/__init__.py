@@ -24,6 +24,7 @@ from ._lib import (  # noqa: F401
     fa_naive_forward_raw,
     fa_naive_workspace_bytes,
     fa_device_info,
+    fa_key_groups_suggest,
     fa_splitkv_suggest,
     fa_status_string,
     fa_version,

@@ -28,8 +28,8 @@ STATUS_NAMES = {
 
 # Every symbol include/fa.h declares.
 EXPORTS = ("fa_device_info", "fa_forward", "fa_forward_ex", "fa_forward_ex_workspace_bytes",
-           "fa_forward_strided", "fa_naive_forward", "fa_naive_workspace_bytes", "fa_splitkv_suggest",
-           "fa_status_string", "fa_version")
+           "fa_forward_strided", "fa_key_groups_suggest", "fa_naive_forward", "fa_naive_workspace_bytes",
+           "fa_splitkv_suggest", "fa_status_string", "fa_version")
 
 _lib = None
 
@@ -69,6 +69,8 @@ def load_library():
     lib.fa_forward_ex_workspace_bytes.restype = i64
     lib.fa_splitkv_suggest.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
     lib.fa_splitkv_suggest.restype = ctypes.c_int
+    lib.fa_key_groups_suggest.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
+    lib.fa_key_groups_suggest.restype = ctypes.c_int
     lib.fa_naive_forward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float, ctypes.c_int,
                                      ctypes.c_int, vp, i64, vp]
     lib.fa_naive_forward.restype = ctypes.c_int
@@ -143,6 +145,13 @@ def fa_forward_ex_workspace_bytes(B: int, H: int, N: int, D: int, dtype: int, ca
 def fa_splitkv_suggest(B: int, H: int, N: int, D: int, dtype: int, causal: bool) -> int:
     return int(load_library().fa_splitkv_suggest(int(B), int(H), int(N), int(D), int(dtype),
                                                  int(bool(causal))))
+
+
+def fa_key_groups_suggest(B: int, H: int, N: int, D: int, dtype: int, causal: bool) -> int:
+    """Key groups (1 or 2) the forward kernel uses for these sizes on the
+    current device, or a negative status."""
+    return int(load_library().fa_key_groups_suggest(int(B), int(H), int(N), int(D), int(dtype),
+                                                    int(bool(causal))))
 
 
 def fa_naive_workspace_bytes(B: int, H: int, N: int, dtype: int) -> int:

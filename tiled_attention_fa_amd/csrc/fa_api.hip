@@ -188,6 +188,20 @@ int suggest_splits(int64_t BH, int64_t N, int64_t D, int dtype, bool causal, int
   return s < 1 ? 1 : (int)s;
 }
 
+// Key groups per workgroup (1 or 2) for the matrix-core kernel: two when the
+// one-group grid fills at most half of the device's workgroup slots and the
+// rows span more than one key tile.  The two groups halve each workgroup's
+// chain of key tiles and, with 64-row workgroups, spread the rows over
+// four times as many workgroups (measured on MI355X: 24-47% faster on such
+// grids, slower on full ones).
+int suggest_key_groups(int64_t BH, int64_t N, int64_t D, int dtype, bool causal, int cus) {
+  if (dtype == FA_F32 || N <= 64) return 1;
+  const int64_t block_m = 32 * fa::mfma_waves((int)D, causal);
+  const int64_t total = BH * ((N + block_m - 1) / block_m);
+  const int64_t slots = (int64_t)cus * fa::mfma_wgs_per_cu((int)D, causal);
+  return 2 * total <= slots ? 2 : 1;
+}
+
 // Workspace of split-KV: the fp32 partials [splits, BH, N, D], then their
 // log-sum-exp [splits, BH, N], each on a 256-byte boundary.  -1 when the
 // size does not fit in int64.
@@ -215,8 +229,11 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, int64_t B, 
 
   const int dev = check_device();
   if (dev != FA_OK) return dev;
+  const int cus = current_cus();
+  if (cus < 0) return cus;
 
   fa::Problem p = dense_problem(q, k, v, o, H, BH, N, D, scale, causal);
+  p.key_groups = suggest_key_groups(BH, N, D, dtype, causal != 0, cus);
   return launch_forward(p, dtype, (hipStream_t)stream);
 }
 
@@ -277,6 +294,16 @@ int fa_splitkv_suggest(int64_t B, int64_t H, int64_t N, int64_t D, int dtype, in
   const int cus = current_cus();
   if (cus < 0) return cus;
   return suggest_splits(B * H, N, D, dtype, causal != 0, cus);
+}
+
+int fa_key_groups_suggest(int64_t B, int64_t H, int64_t N, int64_t D, int dtype, int causal) {
+  if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (B < 1 || H < 1 || N < 0 || D < 1) return FA_ERR_DIM;
+  if (!head_dim_supported(D)) return FA_ERR_UNSUPPORTED_D;
+  if (B > ((int64_t)1 << 31) / H) return FA_ERR_TOO_LARGE;
+  const int cus = current_cus();
+  if (cus < 0) return cus;
+  return suggest_key_groups(B * H, N, D, dtype, causal != 0, cus);
 }
 
 int64_t fa_forward_ex_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int dtype, int causal,
@@ -343,6 +370,11 @@ int fa_forward_ex(const void* q, const void* k, const void* v, void* o, float* l
   fa::Problem p = dense_problem(q, k, v, o, H, BH, N, D, scale, causal);
   p.splits = splits;
   p.lse = splits == 1 ? lse : nullptr;
+  if (splits == 1) {
+    const int cus = current_cus();
+    if (cus < 0) return cus;
+    p.key_groups = suggest_key_groups(BH, N, D, dtype, causal != 0, cus);
+  }
   if (splits > 1) {
     p.part_o = (float*)workspace;
     p.part_lse = (float*)((char*)workspace + lse_off);
@@ -410,43 +442,53 @@ int fa_forward_strided(const void* q, const int64_t* q_strides, const void* k, c
 
   const int dev = check_device();
   if (dev != FA_OK) return dev;
+  const int cus = current_cus();
+  if (cus < 0) return cus;
 
   fa::Problem p = dense_problem(q, k, v, o, H, BH, N, D, scale, causal);
   p.group = (int)(H / H_kv);
+  p.key_groups = suggest_key_groups(BH, N, D, dtype, causal != 0, cus);
   fa::Layout* lay[4] = {&p.lq, &p.lk, &p.lv, &p.lo};
   for (int t = 0; t < 4; ++t) *lay[t] = fa::Layout{st[t][0], st[t][1], (int)st[t][2]};
   return launch_forward(p, dtype, (hipStream_t)stream);
 }
 
 #ifdef FA_TILE_SWEEP
-int fa_tune_shapes(int64_t D, int* waves, int* occupancy, int capacity) {
+int fa_tune_shapes(int64_t D, int* waves, int* occupancy, int* key_groups, int capacity) {
   if (!head_dim_supported(D)) return FA_ERR_UNSUPPORTED_D;
-  const int n = D == 64 ? 4 : 3;
+  const int n = D == 64 ? fa::kTuneShapes64Count : fa::kTuneShapesWideCount;
   for (int i = 0; i < n && i < capacity; ++i) {
     const int* s = D == 64 ? fa::kTuneShapes64[i] : fa::kTuneShapesWide[i];
     if (waves) waves[i] = s[0];
     if (occupancy) occupancy[i] = s[1];
+    if (key_groups) key_groups[i] = s[2];
   }
   return n;
 }
 
 int fa_tune_forward(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H, int64_t N,
-                    int64_t D, float scale, int causal, int dtype, int waves, int occupancy, void* stream) {
+                    int64_t D, float scale, int causal, int dtype, int waves, int occupancy, int key_groups,
+                    void* stream) {
   if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  int sw[8], so[8], sk[8];
+  const int n = fa_tune_shapes(D, sw, so, sk, 8);
+  bool known = false;
+  for (int i = 0; i < n; ++i) known = known || (sw[i] == waves && so[i] == occupancy && sk[i] == key_groups);
   int64_t BH = 0;
-  const int st = validate(q, k, v, o, B, H, N, D, scale, dtype, 32 * (int64_t)(waves > 0 ? waves : 1), &BH);
+  // rows per workgroup bound the grid (any positive block is safe to check
+  // before the shape itself is; an unknown shape is rejected below)
+  const int64_t block_m = known ? 32 * (int64_t)waves / key_groups : 32;
+  const int st = validate(q, k, v, o, B, H, N, D, scale, dtype, block_m, &BH);
   if (st == 1) return FA_OK;
   if (st != FA_OK) return st;
-  int sw[4], so[4];
-  const int n = fa_tune_shapes(D, sw, so, 4);
-  bool known = false;
-  for (int i = 0; i < n; ++i) known = known || (sw[i] == waves && so[i] == occupancy);
   if (!known) return FA_ERR_UNSUPPORTED_D;
   const int dev = check_device();
   if (dev != FA_OK) return dev;
   fa::Problem p = dense_problem(q, k, v, o, H, BH, N, D, scale, causal);
-  const hipError_t err = dtype == FA_F16 ? fa::launch_mfma_shape_f16(p, waves, occupancy, (hipStream_t)stream)
-                                         : fa::launch_mfma_shape_bf16(p, waves, occupancy, (hipStream_t)stream);
+  p.key_groups = key_groups;
+  const hipError_t err =
+      dtype == FA_F16 ? fa::launch_mfma_shape_f16(p, waves, occupancy, key_groups, (hipStream_t)stream)
+                      : fa::launch_mfma_shape_bf16(p, waves, occupancy, key_groups, (hipStream_t)stream);
   return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 #endif

@@ -42,6 +42,10 @@ struct Problem {
   // Optional [BH, N] log-sum-exp of each row's scaled scores (splits == 1;
   // with splits > 1 the merge kernel writes it).
   float* lse = nullptr;
+  // Key groups per workgroup of the matrix-core kernel (1 or 2; 2 only with
+  // splits == 1): two wave groups share the query rows of a workgroup and
+  // take alternate key tiles, merged in LDS at the end.
+  int key_groups = 1;
 };
 
 // Merge of split-KV partials: O = sum_s exp(lse_s - lse) O_s with
@@ -68,6 +72,10 @@ struct MergeProblem {
 // CU).
 constexpr int mfma_waves(int D, bool causal) { return D == 96 || (D == 64 && causal) ? 4 : 8; }
 constexpr int mfma_wgs_per_cu(int D, bool causal) { return D == 64 && causal ? 2 : 1; }
+// With two key groups: 4 waves (2 row blocks of 32 x 2 groups, 64 rows per
+// workgroup); two workgroups per CU where the LDS allows it (D = 64).
+constexpr int mfma_ks_waves = 4;
+constexpr int mfma_ks_occupancy(int D) { return D == 64 ? 2 : 1; }
 
 // One validated three-pass problem: the forward problem plus the caller's
 // workspace, cut into the fp32 score matrix S [BH, N, N] and the
@@ -89,9 +97,11 @@ struct NaiveProblem {
   bool causal;
 };
 
-// Smallest number of query rows per workgroup of each kernel family: the
-// host bounds grid sizes with these (larger blocks only mean fewer
-// workgroups).
+// Query rows per workgroup of each kernel family that the host bounds grid
+// sizes with (larger blocks only mean fewer workgroups).  The matrix-core
+// kernel's smallest block with one key group is 128 rows; its two-key-group
+// shape (64 rows) is chosen only for grids smaller than the device's
+// workgroup slots, far below these bounds.
 constexpr int kMfmaBlockM = 128;
 constexpr int kF32BlockM = 64;
 
@@ -103,11 +113,12 @@ hipError_t launch_f32(const Problem& p, hipStream_t stream);
 hipError_t launch_split_merge(const MergeProblem& p, hipStream_t stream);
 #ifdef FA_TILE_SWEEP
 // The calibration sweep's shapes (tuning library only): (waves per
-// workgroup, waves_per_eu hint) pairs.
-constexpr int kTuneShapes64[][2] = {{2, 1}, {4, 1}, {4, 2}, {8, 1}};
-constexpr int kTuneShapesWide[][2] = {{2, 1}, {4, 1}, {8, 1}};
-hipError_t launch_mfma_shape_f16(const Problem& p, int waves, int occupancy, hipStream_t stream);
-hipError_t launch_mfma_shape_bf16(const Problem& p, int waves, int occupancy, hipStream_t stream);
+// workgroup, waves_per_eu hint, key groups).
+constexpr int kTuneShapes64[][3] = {{2, 1, 1}, {4, 1, 1}, {4, 2, 1}, {8, 1, 1}, {4, 1, 2}, {4, 2, 2}, {8, 1, 2}};
+constexpr int kTuneShapesWide[][3] = {{2, 1, 1}, {4, 1, 1}, {8, 1, 1}, {4, 1, 2}, {8, 1, 2}};
+constexpr int kTuneShapes64Count = 7, kTuneShapesWideCount = 5;
+hipError_t launch_mfma_shape_f16(const Problem& p, int waves, int occupancy, int key_groups, hipStream_t stream);
+hipError_t launch_mfma_shape_bf16(const Problem& p, int waves, int occupancy, int key_groups, hipStream_t stream);
 #endif
 hipError_t launch_naive_f16(const NaiveProblem& p, hipStream_t stream);
 hipError_t launch_naive_bf16(const NaiveProblem& p, hipStream_t stream);

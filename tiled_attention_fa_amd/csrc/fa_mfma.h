@@ -207,7 +207,6 @@ __device__ __forceinline__ u32x2 tr_read(const uint16_t* p) {
 template <int D, int NW>
 struct Shape {
   static constexpr int BN = kBlockN;     // keys per tile
-  static constexpr int BM = 32 * NW;     // query rows per workgroup, 32 per wave
   static constexpr int NT = 64 * NW;     // threads per workgroup
   static constexpr int DP = D <= 64 ? 64 : 128;  // LDS row length (elements)
   static constexpr int CPR = DP / 8;     // 16-byte chunks per LDS row
@@ -236,11 +235,16 @@ __device__ __forceinline__ int k_swz(int row) {
 }
 __device__ __forceinline__ int v_swz(int row) { return 2 * (row & 3); }
 
-template <typename T, int D, bool CAUSAL, bool SPLIT_P, int NW, int OCC>
+template <typename T, int D, bool CAUSAL, bool SPLIT_P, int NW, int OCC, int KS>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC)))
 void fa_forward_kernel(Args a) {
   using S = Shape<D, NW>;
-  constexpr int BN = S::BN, BM = S::BM, NT = S::NT, DP = S::DP, CPR = S::CPR;
+  // KS key groups: with KS = 2 the waves form two groups over the same query
+  // rows, group g taking key tiles g, g+2, g+4, ... of the range, and their
+  // results are merged at the end (for grids that leave CUs idle).
+  static_assert(KS == 1 || (KS == 2 && NW % 2 == 0), "key groups");
+  constexpr int NWR = NW / KS;  // waves per key group = 32-row blocks per workgroup
+  constexpr int BN = S::BN, BM = 32 * NWR, NT = S::NT, DP = S::DP, CPR = S::CPR;
   constexpr int DC = S::DC, DB = S::DB, TILE = S::TILE, LOADS = S::LOADS;
   // A ring of four LDS slots per operand (tile t in slot t % 4), each slot
   // an array of its own, and the step loop unrolled over the ring: the
@@ -269,6 +273,8 @@ void fa_forward_kernel(Args a) {
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
+  const int kgrp = KS == 1 ? 0 : wave / NWR;  // key group
+  const int rb = wave - kgrp * NWR;            // 32-row block
 
   const int logical = xcd_remap(blockIdx.x, a.total_tiles);
   const int per_head = a.num_qtiles * a.splits;
@@ -286,7 +292,7 @@ void fa_forward_kernel(Args a) {
   const int ldq = a.lq.sn, ldk = a.lk.sn, ldv = a.lv.sn, ldo = a.lo.sn;  // row strides
   const float c = a.c;
 
-  const int q0 = qt * BM + wave * 32;  // first query row of this wave
+  const int q0 = qt * BM + rb * 32;  // first query row of this wave
   const int qrow = q0 + l32;           // this lane's query row
 
   // Q fragment: row qrow, columns 16*ch + 8*hi .. +7 (B operand layout).
@@ -357,6 +363,36 @@ void fa_forward_kernel(Args a) {
     k_next += (size_t)BN * ldk * 2;
     v_next += (size_t)BN * ldv * 2;
     k_left -= (uint32_t)(BN * 2 * ldk);
+    v_left -= (uint32_t)(BN * 2 * ldv);
+#endif
+  };
+  // KS == 2: K runs a pair of tiles ahead of V, so each operand follows its
+  // own running pointer.
+  auto load_k_tile = [&](uint16_t* dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void*)k_next, 0, (int)k_left, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i)
+      if (kpred[i])
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rk, (__attribute__((address_space(3))) void*)(dst + (size_t)(i * NT + wave * 64) * 8), 16, koff[i], 0,
+            0, 0);
+    k_next += (size_t)BN * ldk * 2;
+    k_left -= (uint32_t)(BN * 2 * ldk);
+#endif
+  };
+  auto load_v_tile = [&](uint16_t* dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc((void*)v_next, 0, (int)v_left, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i)
+      if (vpred[i])
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rv, (__attribute__((address_space(3))) void*)(dst + (size_t)(i * NT + wave * 64) * 8), 16, voff[i], 0,
+            0, 0);
+    v_next += (size_t)BN * ldv * 2;
     v_left -= (uint32_t)(BN * 2 * ldv);
 #endif
   };
@@ -543,63 +579,170 @@ void fa_forward_kernel(Args a) {
     }
   };
 
-  // Software pipeline over the ring.
+  // Ragged / causal masks of the scores of tile t.
+  auto mask_scores = [&](int t, f32x16 (&sc)[2]) {
+    if (is_edge(t)) {
+      const int k0 = t * BN;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = k0 + 32 * kb + 8 * (e >> 2) + 4 * hi + (e & 3);
+          if (key >= N || (CAUSAL && key > qrow)) sc[kb][e] = -INFINITY;
+        }
+    }
+  };
+
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
   f32x16 sA[2], sB[2];
-  if (t_lo < t_hi) {
-    load_next_tile(kbuf(I0{}), vbuf(I0{}));
-    if (t_lo + 1 < t_hi) load_next_tile(kbuf(I1{}), vbuf(I1{}));
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    __syncthreads();
-    // the first tile of the range holds the first key that any row of the
-    // range sees (a causal row sees a prefix of the keys)
-    qk(kbuf(I0{}), sA);
-  }
-  // Step t (t % 4 == J): pass the barrier (tile t+1, whose loads went out
-  // in step t-1, is then visible, and every wave is done with step t-1);
-  // issue the loads of tile t+2 into slot (t+2) % 4, last read in step
-  // t-2; then the tile body: softmax of tile t, whose scores were computed
-  // in step t-1, while the scores of tile t+1 are computed, and P V of
-  // tile t.
-  auto step = [&](int t, auto J, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
-    constexpr int j = decltype(J)::value;
-    using Next = std::integral_constant<int, (j + 1) & 3>;
-    using Pre2 = std::integral_constant<int, (j + 2) & 3>;
-    // unconditional (redundant at t = 0), so that every path into the
-    // transpose reads below passes a wait for the loads of step t-1
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile t+1 has landed
-    __syncthreads();
-    if (t + 2 < t_hi) load_next_tile(kbuf(Pre2{}), vbuf(Pre2{}));
-    if (live(t)) {
-      if (is_edge(t)) {  // ragged / causal masks
-        const int k0 = t * BN;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int key = k0 + 32 * kb + 8 * (e >> 2) + 4 * hi + (e & 3);
-            if (key >= N || (CAUSAL && key > qrow)) sc[kb][e] = -INFINITY;
-          }
-      }
-      tile_body(kbuf(Next{}), vbuf(J), sc, sn, t == t_lo);
+  if constexpr (KS == 1) {
+    // Software pipeline over the ring.
+    if (t_lo < t_hi) {
+      load_next_tile(kbuf(I0{}), vbuf(I0{}));
+      if (t_lo + 1 < t_hi) load_next_tile(kbuf(I1{}), vbuf(I1{}));
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      __syncthreads();
+      // the first tile of the range holds the first key that any row of the
+      // range sees (a causal row sees a prefix of the keys)
+      qk(kbuf(I0{}), sA);
     }
-  };
-  // The guards nest so that step t+2 is only reached through step t+1 (and
-  // its wait for the loads of step t); with flat guards the compiler sees a
-  // path that skips it and makes the transpose reads of step t+2 wait for
-  // those loads.
-  for (int t = t_lo; t < t_hi; t += 4) {
-    step(t, I0{}, sA, sB);
-    if (t + 1 < t_hi) {
-      step(t + 1, I1{}, sB, sA);
-      if (t + 2 < t_hi) {
-        step(t + 2, I2{}, sA, sB);
-        if (t + 3 < t_hi) step(t + 3, I3{}, sB, sA);
+    // Step t (t % 4 == J): pass the barrier (tile t+1, whose loads went out
+    // in step t-1, is then visible, and every wave is done with step t-1);
+    // issue the loads of tile t+2 into slot (t+2) % 4, last read in step
+    // t-2; then the tile body: softmax of tile t, whose scores were computed
+    // in step t-1, while the scores of tile t+1 are computed, and P V of
+    // tile t.
+    auto step = [&](int t, auto J, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+      constexpr int j = decltype(J)::value;
+      using Next = std::integral_constant<int, (j + 1) & 3>;
+      using Pre2 = std::integral_constant<int, (j + 2) & 3>;
+      // unconditional (redundant at t = 0), so that every path into the
+      // transpose reads below passes a wait for the loads of step t-1
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile t+1 has landed
+      __syncthreads();
+      if (t + 2 < t_hi) load_next_tile(kbuf(Pre2{}), vbuf(Pre2{}));
+      if (live(t)) {
+        mask_scores(t, sc);
+        tile_body(kbuf(Next{}), vbuf(J), sc, sn, t == t_lo);
+      }
+    };
+    // The guards nest so that step t+2 is only reached through step t+1 (and
+    // its wait for the loads of step t); with flat guards the compiler sees a
+    // path that skips it and makes the transpose reads of step t+2 wait for
+    // those loads.
+    for (int t = t_lo; t < t_hi; t += 4) {
+      step(t, I0{}, sA, sB);
+      if (t + 1 < t_hi) {
+        step(t + 1, I1{}, sB, sA);
+        if (t + 2 < t_hi) {
+          step(t + 2, I2{}, sA, sB);
+          if (t + 3 < t_hi) step(t + 3, I3{}, sB, sA);
+        }
       }
     }
+  } else {
+    // Two key groups over pairs of tiles.  K slot j holds K tiles 2p, 2p+1
+    // of pair p in arrays k(2j), k(2j+1), V slot j likewise in v(2j),
+    // v(2j+1); the K pairs run one ahead of the V pairs.  Step s (j = s % 2)
+    // passes the barrier (K pair s+1 and V pair s, loaded in step s-1, have
+    // landed; every wave is done with step s-1), loads K pair s+2 into K
+    // slot j (it held pair s, last read in step s-1) and V pair s+1 into V
+    // slot j+1 (it held pair s-1), then runs the tile body on the wave's
+    // tile t_lo + 2s + kgrp: its softmax, the scores of its tile two ahead
+    // (K pair s+1), P V with V pair s.  Tile indices are relative to t_lo.
+    auto load_k_pair = [&](int u0, auto J) {  // tiles t_lo+u0, t_lo+u0+1
+      constexpr int j = decltype(J)::value;
+      if (t_lo + u0 < t_hi) load_k_tile(kbuf(std::integral_constant<int, 2 * j>{}));
+      if (t_lo + u0 + 1 < t_hi) load_k_tile(kbuf(std::integral_constant<int, 2 * j + 1>{}));
+    };
+    auto load_v_pair = [&](int u0, auto J) {
+      constexpr int j = decltype(J)::value;
+      if (t_lo + u0 < t_hi) load_v_tile(vbuf(std::integral_constant<int, 2 * j>{}));
+      if (t_lo + u0 + 1 < t_hi) load_v_tile(vbuf(std::integral_constant<int, 2 * j + 1>{}));
+    };
+    // this wave's tile of the pair in slot J
+    auto my_k = [&](auto J) -> uint16_t* {
+      constexpr int j = decltype(J)::value;
+      return kgrp ? kbuf(std::integral_constant<int, 2 * j + 1>{}) : kbuf(std::integral_constant<int, 2 * j>{});
+    };
+    auto my_v = [&](auto J) -> uint16_t* {
+      constexpr int j = decltype(J)::value;
+      return kgrp ? vbuf(std::integral_constant<int, 2 * j + 1>{}) : vbuf(std::integral_constant<int, 2 * j>{});
+    };
+    const int nsteps = (t_hi - t_lo + 1) / 2;
+    if (nsteps > 0) {
+      load_k_pair(0, I0{});
+      load_k_pair(2, I1{});
+      load_v_pair(0, I0{});
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      __syncthreads();
+      qk(my_k(I0{}), sA);
+    }
+    auto pstep = [&](int st, auto J, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+      constexpr int j = decltype(J)::value;
+      using Nx = std::integral_constant<int, (j + 1) & 1>;
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      __syncthreads();
+      load_k_pair(2 * st + 4, J);
+      load_v_pair(2 * st + 2, Nx{});
+      const int t = t_lo + 2 * st + kgrp;
+      if (live(t)) {
+        mask_scores(t, sc);
+        tile_body(my_k(Nx{}), my_v(J), sc, sn, st == 0);
+      }
+    };
+    for (int st = 0; st < nsteps; st += 2) {
+      pstep(st, I0{}, sA, sB);
+      if (st + 1 < nsteps) pstep(st + 1, I1{}, sB, sA);
+    }
+
+    // Merge of the two groups by the rescaling rule of the online softmax:
+    // with a_g = exp2((m_g - M) c), M = max(m_0, m_1), O = a_0 O_0 + a_1 O_1
+    // and l = a_0 l_0 + a_1 l_1 (a group that saw no key has m = -inf,
+    // O = 0, l = 0 and weight 0).  Both waves of a row block hold the same
+    // rows in the same lanes, so group 1 leaves its accumulators, its
+    // denominator shares and m in LDS lane by lane and group 0 combines
+    // them.  Accumulator block (db, rb) takes 4 KiB of the K arrays (DP/32
+    // blocks per array); m and the shares sit in v(0).
+    __syncthreads();  // every wave is done with the ring
+    constexpr int per_array = DP / 32;
+    auto acc_block = [&](int q) -> float* {
+      const int arr = q / per_array, off = (q - arr * per_array) * 1024;
+      float* base = arr == 0 ? (float*)kbuf(I0{}) : arr == 1 ? (float*)kbuf(I1{})
+                  : arr == 2 ? (float*)kbuf(I2{}) : (float*)kbuf(I3{});
+      return base + off;
+    };
+    float* const ml = (float*)vbuf(I0{}) + rb * 5 * 64 + lane;
+    if (kgrp == 1) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        float* blk = acc_block(db * NWR + rb) + lane;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) blk[e * 64] = oacc[db][e];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ml[i * 64] = lp[i];
+      ml[4 * 64] = m_run;
+    }
+    __syncthreads();
+    if (kgrp == 1) return;
+    const float m1 = ml[4 * 64];
+    const float M = fmaxf(m_run, m1);
+    const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run - M) * c);
+    const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m1 - M) * c);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const float* blk = acc_block(db * NWR + rb) + lane;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[db][e] = oacc[db][e] * a0 + blk[e * 64] * a1;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lp[i] = lp[i] * a0 + ml[i * 64] * a1;
+    m_run = M;
+    mc = M == -INFINITY ? 0.f : M * c;
   }
 
   // Epilogue: divide by the row's denominator once, round, store.
@@ -639,14 +782,15 @@ void fa_forward_kernel(Args a) {
   }
 }
 
-template <typename T, int D, bool CAUSAL, bool SPLIT_P, int NW, int OCC>
+template <typename T, int D, bool CAUSAL, bool SPLIT_P, int NW, int OCC, int KS = 1>
 hipError_t launch_one(const Args& base, int64_t BH, hipStream_t stream) {
   using S = Shape<D, NW>;
+  constexpr int BM = 32 * NW / KS;
   Args a = base;
-  a.num_qtiles = (a.N + S::BM - 1) / S::BM;
+  a.num_qtiles = (a.N + BM - 1) / BM;
   a.total_tiles = (int)(BH * a.num_qtiles * a.splits);
   void* args[] = {&a};
-  return hipLaunchKernel((const void*)fa_forward_kernel<T, D, CAUSAL, SPLIT_P, NW, OCC>,
+  return hipLaunchKernel((const void*)fa_forward_kernel<T, D, CAUSAL, SPLIT_P, NW, OCC, KS>,
                          dim3(a.total_tiles), dim3(S::NT), args, 0, stream);
 }
 
@@ -678,10 +822,28 @@ inline Args make_args(const Problem& p) {
 }
 
 // Workgroup shape per head dimension and mask: mfma_waves (measured on
-// MI355X).  D = 64 causal runs two workgroups per CU (waves_per_eu 2).
+// MI355X).  D = 64 causal runs two workgroups per CU (waves_per_eu 2).  With
+// two key groups (p.key_groups == 2, chosen by the host for grids that leave
+// CUs idle) the workgroup is 4 waves: 2 row blocks x 2 key groups.
 template <typename T, bool SPLIT_P>
 hipError_t launch(const Problem& p, hipStream_t stream) {
   const Args a = make_args(p);
+  if (p.key_groups == 2) {
+    constexpr int W = mfma_ks_waves;
+    switch (p.D) {
+      case 64:
+        return p.causal ? launch_one<T, 64, true, SPLIT_P, W, mfma_ks_occupancy(64), 2>(a, p.BH, stream)
+                        : launch_one<T, 64, false, SPLIT_P, W, mfma_ks_occupancy(64), 2>(a, p.BH, stream);
+      case 96:
+        return p.causal ? launch_one<T, 96, true, SPLIT_P, W, mfma_ks_occupancy(96), 2>(a, p.BH, stream)
+                        : launch_one<T, 96, false, SPLIT_P, W, mfma_ks_occupancy(96), 2>(a, p.BH, stream);
+      case 128:
+        return p.causal ? launch_one<T, 128, true, SPLIT_P, W, mfma_ks_occupancy(128), 2>(a, p.BH, stream)
+                        : launch_one<T, 128, false, SPLIT_P, W, mfma_ks_occupancy(128), 2>(a, p.BH, stream);
+      default:
+        return hipErrorInvalidValue;
+    }
+  }
   switch (p.D) {
     case 64:
       return p.causal ? launch_one<T, 64, true, SPLIT_P, mfma_waves(64, true), 2>(a, p.BH, stream)
@@ -699,34 +861,42 @@ hipError_t launch(const Problem& p, hipStream_t stream) {
 
 #ifdef FA_TILE_SWEEP
 // Every workgroup shape of the calibration sweep (the tuning library only):
-// (waves per workgroup, waves_per_eu hint).  Two workgroups per CU need a
-// 64-element LDS row (D = 64) and four waves per workgroup (two waves of
-// two workgroups sit on two SIMDs only); with D = 96 or 128 one workgroup
-// fills the LDS, so those sizes take the one-workgroup shapes only.
+// (waves per workgroup, waves_per_eu hint, key groups).  Two workgroups per
+// CU need a 64-element LDS row (D = 64) and four waves per workgroup (two
+// waves of two workgroups sit on two SIMDs only); with D = 96 or 128 one
+// workgroup fills the LDS, so those sizes take the one-workgroup shapes only.
 template <typename T, bool SPLIT_P, int D, bool CAUSAL>
-hipError_t launch_shape_d(const Args& a, int64_t BH, int nw, int occ, hipStream_t s) {
-  if (nw == 2 && occ == 1) return launch_one<T, D, CAUSAL, SPLIT_P, 2, 1>(a, BH, s);
-  if (nw == 4 && occ == 1) return launch_one<T, D, CAUSAL, SPLIT_P, 4, 1>(a, BH, s);
-  if (nw == 8 && occ == 1) return launch_one<T, D, CAUSAL, SPLIT_P, 8, 1>(a, BH, s);
-  if constexpr (D == 64) {
-    if (nw == 4 && occ == 2) return launch_one<T, D, CAUSAL, SPLIT_P, 4, 2>(a, BH, s);
+hipError_t launch_shape_d(const Args& a, int64_t BH, int nw, int occ, int ks, hipStream_t s) {
+  if (ks == 1) {
+    if (nw == 2 && occ == 1) return launch_one<T, D, CAUSAL, SPLIT_P, 2, 1>(a, BH, s);
+    if (nw == 4 && occ == 1) return launch_one<T, D, CAUSAL, SPLIT_P, 4, 1>(a, BH, s);
+    if (nw == 8 && occ == 1) return launch_one<T, D, CAUSAL, SPLIT_P, 8, 1>(a, BH, s);
+    if constexpr (D == 64) {
+      if (nw == 4 && occ == 2) return launch_one<T, D, CAUSAL, SPLIT_P, 4, 2>(a, BH, s);
+    }
+  } else if (ks == 2) {
+    if (nw == 4 && occ == 1) return launch_one<T, D, CAUSAL, SPLIT_P, 4, 1, 2>(a, BH, s);
+    if (nw == 8 && occ == 1) return launch_one<T, D, CAUSAL, SPLIT_P, 8, 1, 2>(a, BH, s);
+    if constexpr (D == 64) {
+      if (nw == 4 && occ == 2) return launch_one<T, D, CAUSAL, SPLIT_P, 4, 2, 2>(a, BH, s);
+    }
   }
   return hipErrorInvalidValue;
 }
 
 template <typename T, bool SPLIT_P>
-hipError_t launch_shape(const Problem& p, int nw, int occ, hipStream_t s) {
+hipError_t launch_shape(const Problem& p, int nw, int occ, int ks, hipStream_t s) {
   const Args a = make_args(p);
   switch (p.D) {
     case 64:
-      return p.causal ? launch_shape_d<T, SPLIT_P, 64, true>(a, p.BH, nw, occ, s)
-                      : launch_shape_d<T, SPLIT_P, 64, false>(a, p.BH, nw, occ, s);
+      return p.causal ? launch_shape_d<T, SPLIT_P, 64, true>(a, p.BH, nw, occ, ks, s)
+                      : launch_shape_d<T, SPLIT_P, 64, false>(a, p.BH, nw, occ, ks, s);
     case 96:
-      return p.causal ? launch_shape_d<T, SPLIT_P, 96, true>(a, p.BH, nw, occ, s)
-                      : launch_shape_d<T, SPLIT_P, 96, false>(a, p.BH, nw, occ, s);
+      return p.causal ? launch_shape_d<T, SPLIT_P, 96, true>(a, p.BH, nw, occ, ks, s)
+                      : launch_shape_d<T, SPLIT_P, 96, false>(a, p.BH, nw, occ, ks, s);
     case 128:
-      return p.causal ? launch_shape_d<T, SPLIT_P, 128, true>(a, p.BH, nw, occ, s)
-                      : launch_shape_d<T, SPLIT_P, 128, false>(a, p.BH, nw, occ, s);
+      return p.causal ? launch_shape_d<T, SPLIT_P, 128, true>(a, p.BH, nw, occ, ks, s)
+                      : launch_shape_d<T, SPLIT_P, 128, false>(a, p.BH, nw, occ, ks, s);
     default:
       return hipErrorInvalidValue;
   }

@@ -7,8 +7,9 @@ to differ between GPUs and asks for it to be measured on each target;
 section "Implementation Recommendations", sizes tiles from the on-chip
 memory.  On MI355X the tile is 32 query rows per wave by 64 keys (the
 32x32 matrix-core tile and the LDS ring); what is left to calibrate is how
-many waves share a workgroup (and so its K/V tiles in LDS) and how many
-workgroups share a CU.  This tool times every shape that the calibration
+many waves share a workgroup (and so its K/V tiles in LDS), how many
+workgroups share a CU, and whether the waves split the key tiles in two
+groups (for grids that leave CUs idle).  This tool times every shape that the calibration
 library (libfa_tune.so) instantiates, for each head dimension, storage
 type and mask, on synthetic inputs drawn by the workload generator, and
 writes a table:
@@ -32,11 +33,17 @@ ROOT = os.path.dirname(PKG)
 TUNE_LIB = os.path.join(PKG, "libfa_tune.so")
 
 # (B, H, N, D, causal): per head dimension one non-causal and one causal
-# shape at the sizes of the workloads, each in fp16 and bf16.
+# shape at the sizes of the workloads, each in fp16 and bf16, then grids
+# that fill a quarter, half and three quarters of the device with the
+# one-group shapes (where the key groups may pay).
 CASES = [
     (1, 32, 2048, 64, False), (4, 32, 2048, 64, True),
     (2, 8, 1000, 96, False), (1, 16, 4096, 96, True),
     (1, 16, 4096, 128, False), (1, 16, 8192, 128, True),
+    (1, 8, 2048, 64, False), (1, 16, 2048, 64, False), (1, 24, 2048, 64, False),
+    (1, 8, 2048, 64, True), (1, 16, 2048, 64, True),
+    (1, 4, 2048, 96, False), (2, 12, 1000, 96, False),
+    (1, 8, 2048, 128, False), (1, 4, 4096, 128, True), (1, 12, 4096, 128, True),
 ]
 DTYPES = ("f16", "bf16")
 
@@ -46,27 +53,29 @@ def load_tune():
         raise ImportError(f"{TUNE_LIB} is not built; run tiled_attention_fa_amd/build.py")
     lib = ctypes.CDLL(TUNE_LIB)
     i64, vp, ip = ctypes.c_int64, ctypes.c_void_p, ctypes.POINTER(ctypes.c_int)
-    lib.fa_tune_shapes.argtypes = [i64, ip, ip, ctypes.c_int]
+    lib.fa_tune_shapes.argtypes = [i64, ip, ip, ip, ctypes.c_int]
     lib.fa_tune_shapes.restype = ctypes.c_int
     lib.fa_tune_forward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float, ctypes.c_int,
-                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
+                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
     lib.fa_tune_forward.restype = ctypes.c_int
     return lib
 
 
 def shapes(lib, D):
+    """(waves, waves_per_eu, key_groups) of every shape the library has for D."""
     w = (ctypes.c_int * 8)()
     o = (ctypes.c_int * 8)()
-    n = lib.fa_tune_shapes(D, w, o, 8)
+    g = (ctypes.c_int * 8)()
+    n = lib.fa_tune_shapes(D, w, o, g, 8)
     if n < 0:
         raise ValueError(f"no shapes for D={D}")
-    return [(w[i], o[i]) for i in range(n)]
+    return [(w[i], o[i], g[i]) for i in range(n)]
 
 
-def tune_forward(lib, q, k, v, o, scale, causal, code, waves, occ, stream):
+def tune_forward(lib, q, k, v, o, scale, causal, code, waves, occ, key_groups, stream):
     B, H, N, D = q.shape
     st = lib.fa_tune_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, H, N, D,
-                             float(scale), int(causal), code, waves, occ, stream)
+                             float(scale), int(causal), code, waves, occ, key_groups, stream)
     if st != 0:
         raise RuntimeError(f"fa_tune_forward status {st}")
 
@@ -138,22 +147,24 @@ def main():
             best = {sh: float("inf") for sh in variants}
             for _ in range(args.rounds):
                 best_lib = min(best_lib, timed(call))
-                for waves, occ in variants:
-                    targs = base + (out.data_ptr(), B, H, N, D, float(w.scale), int(causal), codes[dt], waves,
-                                    occ, stream.cuda_stream)
-                    best[(waves, occ)] = min(best[(waves, occ)], timed(lambda: lib.fa_tune_forward(*targs)))
+                for sh in variants:
+                    targs = base + (out.data_ptr(), B, H, N, D, float(w.scale), int(causal), codes[dt]) + sh + (
+                        stream.cuda_stream,)
+                    best[sh] = min(best[sh], timed(lambda: lib.fa_tune_forward(*targs)))
             rec = {"case": w.name, "B": B, "H": H, "N": N, "D": D, "dtype": dt, "causal": causal,
                    "fa_forward_us": round(best_lib, 2), "shapes": []}
-            for waves, occ in variants:
-                tune_forward(lib, q, k, v, out, w.scale, causal, codes[dt], waves, occ, stream.cuda_stream)
+            for waves, occ, ks in variants:
+                tune_forward(lib, q, k, v, out, w.scale, causal, codes[dt], waves, occ, ks, stream.cuda_stream)
                 torch.cuda.synchronize()
                 diff = float((out.float() - ref.float()).abs().max().item())
-                t = best[(waves, occ)]
-                rec["shapes"].append({"waves": waves, "rows": 32 * waves, "waves_per_eu": occ,
-                                      "us": round(t, 2), "tflops": round(flops / (t * 1e-6) / 1e12, 1),
+                t = best[(waves, occ, ks)]
+                rec["shapes"].append({"waves": waves, "rows": 32 * waves // ks, "waves_per_eu": occ,
+                                      "key_groups": ks, "us": round(t, 2),
+                                      "tflops": round(flops / (t * 1e-6) / 1e12, 1),
                                       "max_abs_diff_vs_fa_forward": diff})
             best = min(rec["shapes"], key=lambda s: s["us"])
-            rec["best"] = {"waves": best["waves"], "waves_per_eu": best["waves_per_eu"], "us": best["us"]}
+            rec["best"] = {"waves": best["waves"], "waves_per_eu": best["waves_per_eu"],
+                           "key_groups": best["key_groups"], "us": best["us"]}
             rows.append(rec)
             print(json.dumps(rec), flush=True)
             del q, k, v, ref, out
@@ -168,16 +179,21 @@ def main():
                  f"Command (repository root): `{meta['command']}`", "",
                  f"Mean microseconds per launch over {args.launches} back-to-back launches (HIP events), "
                  f"best of {args.rounds} interleaved rounds, after 0.25 s of untimed launches per case; "
-                 "every workgroup shape of libfa_tune.so: waves x 32 query rows per workgroup, "
-                 "waves_per_eu hint. `fa_forward` is the shipped library's own choice on the same "
-                 "inputs.", "",
-                 "| case | fa_forward | " + " | ".join(["shape / us"] * 4) + " | best |",
-                 "|---|---|" + "---|" * 4 + "---|"]
+                 "every workgroup shape of libfa_tune.so: `Nw` = N waves per workgroup (32 query rows "
+                 "each), `occK` = waves_per_eu hint K, `ks2` = the waves in two key groups over half as many "
+                 "rows, alternate key tiles each. `fa_forward` is the shipped library's own choice on the "
+                 "same inputs.", "",
+                 "| case | fa_forward | " + " | ".join(["shape / us"] * 7) + " | best |",
+                 "|---|---|" + "---|" * 7 + "---|"]
+
+        def label(s):
+            return f"{s['waves']}w occ{s['waves_per_eu']}" + (" ks2" if s["key_groups"] == 2 else "")
+
         for r in rows:
-            cells = [f"{s['waves']}w occ{s['waves_per_eu']}: {s['us']}" for s in r["shapes"]]
-            cells += [""] * (4 - len(cells))
+            cells = [f"{label(s)}: {s['us']}" for s in r["shapes"]]
+            cells += [""] * (7 - len(cells))
             lines.append(f"| {r['case']} | {r['fa_forward_us']} | " + " | ".join(cells) +
-                         f" | {r['best']['waves']}w occ{r['best']['waves_per_eu']} |")
+                         f" | {label(r['best'])} |")
         worst = max(s["max_abs_diff_vs_fa_forward"] for r in rows for s in r["shapes"])
         lines += ["", f"Largest difference of any shape's O from fa_forward's: {worst:.3e}."]
         open(args.out + ".md", "w").write("\n".join(lines) + "\n")
