@@ -124,6 +124,33 @@ def test_one_group_same_problems(dtype, D, causal):
         assert err <= LSE_TOL, f"{w.name} causal={causal}: lse error {err:.3e}"
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("D", [64, 96, 128])
+def test_two_groups_causal_partial_grids(dtype, D):
+    """Causal grids between half and three quarters of the slots run two
+    groups (8-wave workgroups at D = 96 and 128); non-causal ones of the same
+    size run one.  Three heads of each are checked against the oracle."""
+    cus, _ = fa.fa_device_info()
+    block, per_cu = {64: (128, 2), 96: (128, 1), 128: (256, 1)}[D]
+    N = 2048
+    blocks = N // block
+    slots = cus * per_cu
+    H = (5 * slots // 8) // blocks  # ~5/8 of the slots
+    assert 2 * H * blocks > slots and 4 * H * blocks <= 3 * slots
+    assert groups(1, H, N, D, dtype, True) == 2
+    assert groups(1, H, N, D, dtype, False) == 1
+    w = Workload(f"kgp_{dtype}_d{D}", 1, H, N, D, dtype, True, seed=73_000 + D)
+    _say(f"[key groups 2, partial causal grid] {w.name} H={H}")
+    x = make_inputs(w)
+    q, k, v = (to_device(x[n], dtype) for n in "qkv")
+    o = fa.forward(q, k, v, scale=w.scale, causal=True)
+    torch.cuda.synchronize()
+    got = to_numpy64(o)
+    for h in (0, H // 2, H - 1):
+        ref = oracle.forward(x["q"][:, h:h + 1], x["k"][:, h:h + 1], x["v"][:, h:h + 1], dtype, w.scale, True)
+        parity(got[:, h:h + 1], ref, dtype, f"{w.name} head {h}")
+
+
 LAYOUTS = [("bnhd", "bnhd", "bnhd", "bnhd"), ("pad", "bhnd", "pad", "bnhd")]
 
 

@@ -188,18 +188,28 @@ int suggest_splits(int64_t BH, int64_t N, int64_t D, int dtype, bool causal, int
   return s < 1 ? 1 : (int)s;
 }
 
-// Key groups per workgroup (1 or 2) for the matrix-core kernel: two when the
-// one-group grid fills at most half of the device's workgroup slots and the
-// rows span more than one key tile.  The two groups halve each workgroup's
-// chain of key tiles and, with 64-row workgroups, spread the rows over
-// four times as many workgroups (measured on MI355X: 24-47% faster on such
-// grids, slower on full ones).
-int suggest_key_groups(int64_t BH, int64_t N, int64_t D, int dtype, bool causal, int cus) {
+// Key groups per workgroup (1 or 2) for the matrix-core kernel, and the
+// waves of the two-group workgroup (*ks_waves, 4 or 8), measured on MI355X:
+//  * the one-group grid fills at most half of the device's workgroup slots:
+//    two groups in 4-wave workgroups of 64 rows, which halve each chain of
+//    key tiles and spread the rows over more workgroups (24-47% faster);
+//  * causal grids up to three quarters full: the rows that see every key
+//    set the time, and two groups halve their chain (2-29% faster; 8 waves
+//    of 128 rows at D = 96 and 128); non-causal grids there, and fuller
+//    ones, run faster with one group.
+// Rows within one key tile have nothing to split.
+int suggest_key_groups(int64_t BH, int64_t N, int64_t D, int dtype, bool causal, int cus, int* ks_waves) {
+  *ks_waves = fa::mfma_ks_waves;
   if (dtype == FA_F32 || N <= 64) return 1;
   const int64_t block_m = 32 * fa::mfma_waves((int)D, causal);
   const int64_t total = BH * ((N + block_m - 1) / block_m);
   const int64_t slots = (int64_t)cus * fa::mfma_wgs_per_cu((int)D, causal);
-  return 2 * total <= slots ? 2 : 1;
+  if (2 * total <= slots) return 2;
+  if (causal && 4 * total <= 3 * slots) {
+    if (D != 64) *ks_waves = 8;
+    return 2;
+  }
+  return 1;
 }
 
 // Workspace of split-KV: the fp32 partials [splits, BH, N, D], then their
@@ -233,7 +243,7 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, int64_t B, 
   if (cus < 0) return cus;
 
   fa::Problem p = dense_problem(q, k, v, o, H, BH, N, D, scale, causal);
-  p.key_groups = suggest_key_groups(BH, N, D, dtype, causal != 0, cus);
+  p.key_groups = suggest_key_groups(BH, N, D, dtype, causal != 0, cus, &p.ks_waves);
   return launch_forward(p, dtype, (hipStream_t)stream);
 }
 
@@ -303,7 +313,8 @@ int fa_key_groups_suggest(int64_t B, int64_t H, int64_t N, int64_t D, int dtype,
   if (B > ((int64_t)1 << 31) / H) return FA_ERR_TOO_LARGE;
   const int cus = current_cus();
   if (cus < 0) return cus;
-  return suggest_key_groups(B * H, N, D, dtype, causal != 0, cus);
+  int waves = 0;
+  return suggest_key_groups(B * H, N, D, dtype, causal != 0, cus, &waves);
 }
 
 int64_t fa_forward_ex_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int dtype, int causal,
@@ -373,7 +384,7 @@ int fa_forward_ex(const void* q, const void* k, const void* v, void* o, float* l
   if (splits == 1) {
     const int cus = current_cus();
     if (cus < 0) return cus;
-    p.key_groups = suggest_key_groups(BH, N, D, dtype, causal != 0, cus);
+    p.key_groups = suggest_key_groups(BH, N, D, dtype, causal != 0, cus, &p.ks_waves);
   }
   if (splits > 1) {
     p.part_o = (float*)workspace;
@@ -447,7 +458,7 @@ int fa_forward_strided(const void* q, const int64_t* q_strides, const void* k, c
 
   fa::Problem p = dense_problem(q, k, v, o, H, BH, N, D, scale, causal);
   p.group = (int)(H / H_kv);
-  p.key_groups = suggest_key_groups(BH, N, D, dtype, causal != 0, cus);
+  p.key_groups = suggest_key_groups(BH, N, D, dtype, causal != 0, cus, &p.ks_waves);
   fa::Layout* lay[4] = {&p.lq, &p.lk, &p.lv, &p.lo};
   for (int t = 0; t < 4; ++t) *lay[t] = fa::Layout{st[t][0], st[t][1], (int)st[t][2]};
   return launch_forward(p, dtype, (hipStream_t)stream);

@@ -44,8 +44,10 @@ struct Problem {
   float* lse = nullptr;
   // Key groups per workgroup of the matrix-core kernel (1 or 2; 2 only with
   // splits == 1): two wave groups share the query rows of a workgroup and
-  // take alternate key tiles, merged in LDS at the end.
+  // take alternate key tiles, merged in LDS at the end; ks_waves is that
+  // workgroup's wave count (4, or 8 for D = 96 and 128).
   int key_groups = 1;
+  int ks_waves = 4;
 };
 
 // Merge of split-KV partials: O = sum_s exp(lse_s - lse) O_s with
@@ -73,7 +75,9 @@ struct MergeProblem {
 constexpr int mfma_waves(int D, bool causal) { return D == 96 || (D == 64 && causal) ? 4 : 8; }
 constexpr int mfma_wgs_per_cu(int D, bool causal) { return D == 64 && causal ? 2 : 1; }
 // With two key groups: 4 waves (2 row blocks of 32 x 2 groups, 64 rows per
-// workgroup); two workgroups per CU where the LDS allows it (D = 64).
+// workgroup), two workgroups per CU where the LDS allows it (D = 64); or, for
+// causal D = 96 and 128 grids between half and three quarters of the slots,
+// 8 waves (128 rows).
 constexpr int mfma_ks_waves = 4;
 constexpr int mfma_ks_occupancy(int D) { return D == 64 ? 2 : 1; }
 

@@ -824,7 +824,8 @@ inline Args make_args(const Problem& p) {
 // Workgroup shape per head dimension and mask: mfma_waves (measured on
 // MI355X).  D = 64 causal runs two workgroups per CU (waves_per_eu 2).  With
 // two key groups (p.key_groups == 2, chosen by the host for grids that leave
-// CUs idle) the workgroup is 4 waves: 2 row blocks x 2 key groups.
+// CUs idle) the workgroup is p.ks_waves waves: 2 or 4 row blocks x 2 key
+// groups.
 template <typename T, bool SPLIT_P>
 hipError_t launch(const Problem& p, hipStream_t stream) {
   const Args a = make_args(p);
@@ -835,9 +836,11 @@ hipError_t launch(const Problem& p, hipStream_t stream) {
         return p.causal ? launch_one<T, 64, true, SPLIT_P, W, mfma_ks_occupancy(64), 2>(a, p.BH, stream)
                         : launch_one<T, 64, false, SPLIT_P, W, mfma_ks_occupancy(64), 2>(a, p.BH, stream);
       case 96:
+        if (p.causal && p.ks_waves == 8) return launch_one<T, 96, true, SPLIT_P, 8, 1, 2>(a, p.BH, stream);
         return p.causal ? launch_one<T, 96, true, SPLIT_P, W, mfma_ks_occupancy(96), 2>(a, p.BH, stream)
                         : launch_one<T, 96, false, SPLIT_P, W, mfma_ks_occupancy(96), 2>(a, p.BH, stream);
       case 128:
+        if (p.causal && p.ks_waves == 8) return launch_one<T, 128, true, SPLIT_P, 8, 1, 2>(a, p.BH, stream);
         return p.causal ? launch_one<T, 128, true, SPLIT_P, W, mfma_ks_occupancy(128), 2>(a, p.BH, stream)
                         : launch_one<T, 128, false, SPLIT_P, W, mfma_ks_occupancy(128), 2>(a, p.BH, stream);
       default:

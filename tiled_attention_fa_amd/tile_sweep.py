@@ -35,7 +35,8 @@ TUNE_LIB = os.path.join(PKG, "libfa_tune.so")
 # (B, H, N, D, causal): per head dimension one non-causal and one causal
 # shape at the sizes of the workloads, each in fp16 and bf16, then grids
 # that fill a quarter, half and three quarters of the device with the
-# one-group shapes (where the key groups may pay).
+# one-group shapes (where the key groups may pay), and causal grids between
+# half and seven eighths.
 CASES = [
     (1, 32, 2048, 64, False), (4, 32, 2048, 64, True),
     (2, 8, 1000, 96, False), (1, 16, 4096, 96, True),
@@ -44,6 +45,8 @@ CASES = [
     (1, 8, 2048, 64, True), (1, 16, 2048, 64, True),
     (1, 4, 2048, 96, False), (2, 12, 1000, 96, False),
     (1, 8, 2048, 128, False), (1, 4, 4096, 128, True), (1, 12, 4096, 128, True),
+    (1, 24, 2048, 64, True), (1, 28, 2048, 64, True), (1, 12, 2048, 96, True), (1, 6, 8192, 128, True),
+    (1, 14, 4096, 128, True),
 ]
 DTYPES = ("f16", "bf16")
 
