@@ -17,6 +17,11 @@
 //    the two waves that share a SIMD belong to one workgroup and advance in
 //    lockstep (one barrier per tile); waves of different workgroups on one
 //    SIMD would not: the older one wins issue and the younger ends alone.
+//  * Grids that leave CUs idle (the host's choice, key_groups == 2): the
+//    waves of a workgroup form two groups over the same query rows, group g
+//    taking key tiles g, g+2, ...; K and V then run in separate two-slot
+//    rings of tile pairs (the same eight LDS arrays), and after the loop the
+//    two groups' (m, l, O) are merged in LDS by the rescaling rule above.
 //  * Key/value tiles of 64 keys go straight from global memory to LDS
 //    (buffer_load ... lds, 16 bytes per lane) through a buffer resource that
 //    ends at key N, so rows past N read as zero.  A ring of four LDS slots
