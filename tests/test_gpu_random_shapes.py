@@ -1,0 +1,92 @@
+"""GPU parity on seeded random problems, against the fp64 oracle, through the
+C ABI: storage type, head dimension, mask, B, H, key/value heads, N (ragged
+lengths included), entry point (fa_forward, fa_forward_ex with a log-sum-exp
+and a random key-range count, fa_forward_strided with a random layout) and
+scale are drawn from one fixed generator, so the cases are the same on every
+run.  Small head counts land on the two-key-group kernel, larger ones on the
+one-group kernel; the test reports how many cases took each path and asserts
+that both were taken.
+
+Tolerances as for fa_forward (gpu_helpers); the log-sum-exp bound of the
+split-KV tests.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tiled_attention_fa_amd as fa
+from gpu_helpers import bits_to, empty_out, expand, make_gqa_inputs, parity, to_device, to_numpy64
+from workloads import Workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+CODES = {"f32": 0, "f16": 1, "bf16": 2}
+LSE_TOL = {"f32": 2e-5, "f16": 1e-3, "bf16": 1e-3}
+CASES = 200
+LAYOUTS = ["bhnd", "bnhd", "pad"]
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def draw(rng):
+    dtype = ["f16", "bf16", "f32"][rng.choice(3, p=[0.45, 0.45, 0.1])]
+    D = int(rng.choice([64, 96, 128]))
+    causal = bool(rng.integers(2))
+    B = int(rng.integers(1, 3))
+    Hkv = int(rng.integers(1, 5))
+    H = Hkv * int(rng.choice([1, 2, 4]))
+    if rng.random() < 0.3:  # enough heads for the one-group kernel
+        H = Hkv * int(rng.choice([16, 32]))
+    N = int(rng.choice([int(rng.integers(1, 130)), int(rng.integers(130, 700))]))
+    if H >= 16:  # keeps the oracle's share of the run to seconds
+        N = min(N, 400)
+    scale = float(rng.choice([1.0 / np.sqrt(D), 0.05, 0.4]))
+    entry = str(rng.choice(["forward", "ex", "strided"]))
+    return dtype, D, causal, B, H, Hkv, N, scale, entry
+
+
+def test_random_problems():
+    rng = np.random.default_rng(20261202)
+    paths = {1: 0, 2: 0}
+    for i in range(CASES):
+        dtype, D, causal, B, H, Hkv, N, scale, entry = draw(rng)
+        if entry != "strided":
+            Hkv = H
+        w = Workload(f"rand{i}_{dtype}_d{D}", B, H, N, D, dtype, causal, seed=90_000 + i)
+        g = fa.fa_key_groups_suggest(B, H, N, D, CODES[dtype], causal)
+        assert g in (1, 2)
+        if dtype != "f32":
+            paths[g] += 1
+        _say(f"[random {i}] {entry} {dtype} B={B} H={H} H_kv={Hkv} N={N} D={D} causal={causal} "
+             f"scale={scale:.3g} key_groups={g}")
+        if entry == "strided":
+            q, k, v = make_gqa_inputs(w, Hkv)
+            layouts = [LAYOUTS[int(rng.integers(3))] for _ in range(4)]
+            o = empty_out(B, H, N, D, dtype, layouts[3], pad=8)
+            fa.fa_forward_strided(bits_to(q, dtype, layouts[0], pad=8), bits_to(k, dtype, layouts[1], pad=8),
+                                  bits_to(v, dtype, layouts[2], pad=8), o, scale=scale, causal=causal)
+            torch.cuda.synchronize()
+            ref = oracle.forward(q, expand(k, H // Hkv), expand(v, H // Hkv), dtype, scale, causal)
+            parity(to_numpy64(o), ref, dtype, f"case {i} strided {layouts}")
+            continue
+        x = make_inputs(w)
+        q, k, v = (to_device(x[n], dtype) for n in "qkv")
+        if entry == "forward":
+            o = fa.forward(q, k, v, scale=scale, causal=causal)
+            torch.cuda.synchronize()
+            ref = oracle.forward(x["q"], x["k"], x["v"], dtype, scale, causal)
+            parity(to_numpy64(o), ref, dtype, f"case {i} fa_forward")
+        else:
+            splits = int(rng.choice([0, 1, 2, 3]))
+            o, lse = fa.forward_ex(q, k, v, scale=scale, causal=causal, num_splits=splits, lse=True)
+            torch.cuda.synchronize()
+            ref, ref_lse = oracle.forward(x["q"], x["k"], x["v"], dtype, scale, causal, return_lse=True)
+            parity(to_numpy64(o), ref, dtype, f"case {i} fa_forward_ex splits={splits}")
+            err = float(np.abs(lse.double().cpu().numpy() - ref_lse).max())
+            assert err <= LSE_TOL[dtype], f"case {i}: lse error {err:.3e}"
+    _say(f"[random] 16-bit cases by key groups: {paths}")
+    assert paths[1] > 0 and paths[2] > 0, paths
