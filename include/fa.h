@@ -84,11 +84,10 @@ typedef enum fa_status {
  * enqueues one kernel on `stream` and returns.  The caller owns all buffers
  * and synchronises.  The library holds no state between calls apart from a
  * per-device cache of the device check and CU count, and allocates nothing.
- * When B*H times the 16-bit kernel's query blocks fill at most half of the
- * device's workgroup slots (few heads, short rows), or at most three
- * quarters with the causal mask, each workgroup's waves split its key tiles
- * in two groups whose partial results are merged in LDS by the rescaling
- * rule of the online softmax (fa_key_groups_suggest); the arithmetic order
+ * When B*H times the 16-bit kernel's query blocks leave much of the device
+ * idle (few heads, short rows; fa_key_groups_suggest), each workgroup's
+ * waves split its key tiles in two groups whose partial results are merged
+ * in LDS by the rescaling rule of the online softmax; the arithmetic order
  * changes, the result agrees to the same tolerance.
  * Pointers must be device memory of the current HIP device.
  * Returns FA_OK or a negative fa_status.
@@ -198,12 +197,14 @@ int fa_splitkv_suggest(int64_t B, int64_t H, int64_t N, int64_t D, int dtype, in
  * fa_key_groups_suggest -- how many key groups the workgroups of fa_forward,
  * fa_forward_strided and fa_forward_ex (with one key range) use on the
  * current device for these sizes: 2 when dtype is FA_F16 or FA_BF16, N > 64
- * and B*H times the one-group kernel's query blocks (256 rows; 128 for
- * causal D = 64 and for D = 96) fill at most half of the device's workgroup
- * slots (one per CU; two for causal D = 64), or at most three quarters with
- * causal != 0, else 1.  With 2 the waves of a workgroup (64 query rows; 128
- * for causal D = 96 and 128 beyond half the slots) form two groups that take
- * alternate key tiles,
+ * and either
+ *   - non-causal: B*H times the blocks of 256 rows is at most a quarter of
+ *     the CU count, or at most half of it for D = 64 and 128; or
+ *   - causal: B*H times the one-group kernel's query blocks (256 rows; 128
+ *     for D = 64 and 96) fill at most three quarters of the device's
+ *     workgroup slots (one per CU; two for D = 64);
+ * else 1.  With 2 the waves of a workgroup (64 query rows, or 128 on the
+ * fuller of those grids) form two groups that take alternate key tiles,
  * and their running maxima, denominators and accumulators are merged in
  * LDS by the rescaling rule of the online softmax ("Android Transformer
  * Optimization: Attention and Mobile GPU Bottlenecks", section "A Complete

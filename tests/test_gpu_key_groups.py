@@ -151,6 +151,30 @@ def test_two_groups_causal_partial_grids(dtype, D):
         parity(got[:, h:h + 1], ref, dtype, f"{w.name} head {h}")
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("D", [64, 96, 128])
+def test_noncausal_quarter_to_half_grids(dtype, D):
+    """Non-causal grids whose 256-row blocks cover between a quarter and half
+    of the CUs: two groups in 8-wave workgroups at D = 64 and 128, one group
+    at D = 96.  Three heads checked against the oracle."""
+    cus, _ = fa.fa_device_info()
+    N = 2048
+    H = (3 * cus // 8) // (N // 256)  # ~3/8 of the CUs
+    assert 4 * H * (N // 256) > cus and 2 * H * (N // 256) <= cus
+    want = 1 if D == 96 else 2
+    assert groups(1, H, N, D, dtype, False) == want
+    w = Workload(f"kgq_{dtype}_d{D}", 1, H, N, D, dtype, False, seed=74_000 + D)
+    _say(f"[key groups {want}, quarter-to-half grid] {w.name} H={H}")
+    x = make_inputs(w)
+    q, k, v = (to_device(x[n], dtype) for n in "qkv")
+    o = fa.forward(q, k, v, scale=w.scale, causal=False)
+    torch.cuda.synchronize()
+    got = to_numpy64(o)
+    for h in (0, H // 2, H - 1):
+        ref = oracle.forward(x["q"][:, h:h + 1], x["k"][:, h:h + 1], x["v"][:, h:h + 1], dtype, w.scale, False)
+        parity(got[:, h:h + 1], ref, dtype, f"{w.name} head {h}")
+
+
 LAYOUTS = [("bnhd", "bnhd", "bnhd", "bnhd"), ("pad", "bhnd", "pad", "bnhd")]
 
 

@@ -189,23 +189,36 @@ int suggest_splits(int64_t BH, int64_t N, int64_t D, int dtype, bool causal, int
 }
 
 // Key groups per workgroup (1 or 2) for the matrix-core kernel, and the
-// waves of the two-group workgroup (*ks_waves, 4 or 8), measured on MI355X:
-//  * the one-group grid fills at most half of the device's workgroup slots:
-//    two groups in 4-wave workgroups of 64 rows, which halve each chain of
-//    key tiles and spread the rows over more workgroups (24-47% faster);
-//  * causal grids up to three quarters full: the rows that see every key
-//    set the time, and two groups halve their chain (2-29% faster; 8 waves
-//    of 128 rows at D = 96 and 128); non-causal grids there, and fuller
-//    ones, run faster with one group.
-// Rows within one key tile have nothing to split.
+// waves of the two-group workgroup (*ks_waves, 4 or 8), measured on MI355X.
+// Two groups halve each workgroup's chain of key tiles; the workgroup shape
+// decides how many rounds of workgroups the grid needs.  Rows within one key
+// tile have nothing to split.
+//  * Non-causal, with w = B*H times the blocks of 256 rows: w <= CUs / 4
+//    takes 4-wave workgroups of 64 rows (all CUs busy in one round; 24-47%
+//    faster); w <= CUs / 2 at D = 64 and 128 takes 8-wave workgroups of 128
+//    rows (one round, two waves per SIMD; 4-30% faster); fuller grids, and
+//    D = 96 beyond a quarter, run faster with one group.
+//  * Causal, with the one-group grid's fill of the device's workgroup
+//    slots: up to one half, 4-wave workgroups; up to three quarters, where
+//    the rows that see every key set the time, 4 waves at D = 64 and 8 at
+//    D = 96 and 128 (2-29% faster); fuller grids run one group.
 int suggest_key_groups(int64_t BH, int64_t N, int64_t D, int dtype, bool causal, int cus, int* ks_waves) {
   *ks_waves = fa::mfma_ks_waves;
   if (dtype == FA_F32 || N <= 64) return 1;
+  if (!causal) {
+    const int64_t w = BH * ((N + 255) / 256);
+    if (4 * w <= cus) return 2;
+    if (D != 96 && 2 * w <= cus) {
+      *ks_waves = 8;
+      return 2;
+    }
+    return 1;
+  }
   const int64_t block_m = 32 * fa::mfma_waves((int)D, causal);
   const int64_t total = BH * ((N + block_m - 1) / block_m);
   const int64_t slots = (int64_t)cus * fa::mfma_wgs_per_cu((int)D, causal);
   if (2 * total <= slots) return 2;
-  if (causal && 4 * total <= 3 * slots) {
+  if (4 * total <= 3 * slots) {
     if (D != 64) *ks_waves = 8;
     return 2;
   }

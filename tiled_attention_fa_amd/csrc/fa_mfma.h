@@ -835,19 +835,25 @@ template <typename T, bool SPLIT_P>
 hipError_t launch(const Problem& p, hipStream_t stream) {
   const Args a = make_args(p);
   if (p.key_groups == 2) {
+    // the 8-wave shapes the host may choose: non-causal D = 64 and 128,
+    // causal D = 96 and 128
     constexpr int W = mfma_ks_waves;
+    const bool w8 = p.ks_waves == 8;
     switch (p.D) {
       case 64:
-        return p.causal ? launch_one<T, 64, true, SPLIT_P, W, mfma_ks_occupancy(64), 2>(a, p.BH, stream)
-                        : launch_one<T, 64, false, SPLIT_P, W, mfma_ks_occupancy(64), 2>(a, p.BH, stream);
+        if (p.causal) return launch_one<T, 64, true, SPLIT_P, W, mfma_ks_occupancy(64), 2>(a, p.BH, stream);
+        return w8 ? launch_one<T, 64, false, SPLIT_P, 8, 1, 2>(a, p.BH, stream)
+                  : launch_one<T, 64, false, SPLIT_P, W, mfma_ks_occupancy(64), 2>(a, p.BH, stream);
       case 96:
-        if (p.causal && p.ks_waves == 8) return launch_one<T, 96, true, SPLIT_P, 8, 1, 2>(a, p.BH, stream);
-        return p.causal ? launch_one<T, 96, true, SPLIT_P, W, mfma_ks_occupancy(96), 2>(a, p.BH, stream)
-                        : launch_one<T, 96, false, SPLIT_P, W, mfma_ks_occupancy(96), 2>(a, p.BH, stream);
+        if (!p.causal) return launch_one<T, 96, false, SPLIT_P, W, mfma_ks_occupancy(96), 2>(a, p.BH, stream);
+        return w8 ? launch_one<T, 96, true, SPLIT_P, 8, 1, 2>(a, p.BH, stream)
+                  : launch_one<T, 96, true, SPLIT_P, W, mfma_ks_occupancy(96), 2>(a, p.BH, stream);
       case 128:
-        if (p.causal && p.ks_waves == 8) return launch_one<T, 128, true, SPLIT_P, 8, 1, 2>(a, p.BH, stream);
-        return p.causal ? launch_one<T, 128, true, SPLIT_P, W, mfma_ks_occupancy(128), 2>(a, p.BH, stream)
-                        : launch_one<T, 128, false, SPLIT_P, W, mfma_ks_occupancy(128), 2>(a, p.BH, stream);
+        if (p.causal)
+          return w8 ? launch_one<T, 128, true, SPLIT_P, 8, 1, 2>(a, p.BH, stream)
+                    : launch_one<T, 128, true, SPLIT_P, W, mfma_ks_occupancy(128), 2>(a, p.BH, stream);
+        return w8 ? launch_one<T, 128, false, SPLIT_P, 8, 1, 2>(a, p.BH, stream)
+                  : launch_one<T, 128, false, SPLIT_P, W, mfma_ks_occupancy(128), 2>(a, p.BH, stream);
       default:
         return hipErrorInvalidValue;
     }
