@@ -1,6 +1,7 @@
 """GPU parity at the largest sizes that run in seconds: one 65,536-token
 head (row offsets of millions of elements; causal, non-causal and split
-into four key ranges), a 4,096-head grid (B=32, H=128), and a bf16
+into four key ranges), 16,384-token rows on the two-key-group kernel, a
+4,096-head grid (B=32, H=128), and a bf16
 D=128 long head in the [B, N, H, D] layout with multi-query K/V.  Sampled
 rows, including the first and last rows and rows at block edges, are checked
 against the fp64 oracle one by one."""
@@ -50,6 +51,29 @@ def test_one_long_head(causal):
     err_lse = float(np.abs(lse.double().cpu().numpy()[0, 0][ri] - ref_lse).max())
     assert err_lse <= 1e-3, err_lse
     _say(f"[limits] N=65536 causal={causal}: max abs err {e['max_abs']:.3e}, lse {err_lse:.3e}")
+
+
+@pytest.mark.parametrize("dtype,D,H,causal", [("f16", 64, 1, False), ("bf16", 128, 2, True), ("f16", 96, 1, True)])
+def test_long_rows_two_key_groups(dtype, D, H, causal):
+    """16,384-token rows on grids small enough for two key groups: chains of
+    128 key tiles per group, merged at the end.  Sampled rows against the
+    oracle, with fa_forward_ex's log-sum-exp."""
+    N = 16384
+    assert fa.fa_key_groups_suggest(1, H, N, D, {"f16": fa.FA_F16, "bf16": fa.FA_BF16}[dtype], causal) == 2
+    w = Workload(f"limit_kg2_{dtype}_d{D}", 1, H, N, D, dtype, causal, seed=9010 + D)
+    _say(f"[limits] {w.name} H={H} causal={causal}")
+    x = make_inputs(w)
+    q, k, v = (to_device(x[n], dtype) for n in "qkv")
+    o, lse = fa.forward_ex(q, k, v, causal=causal, num_splits=1, lse=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(D)
+    bh, ri = sample_rows(N, H, rng)
+    ref, ref_lse = oracle.rows(x["q"], x["k"], x["v"], dtype, w.scale, causal, bh, ri, return_lse=True)
+    got = to_numpy64(o).reshape(H, N, D)[bh, ri]
+    e = parity(got, ref, dtype, w.name)
+    err_lse = float(np.abs(lse.double().cpu().numpy().reshape(H, N)[bh, ri] - ref_lse).max())
+    assert err_lse <= 1e-3, err_lse
+    _say(f"[limits] {w.name}: max abs err {e['max_abs']:.3e}, lse {err_lse:.3e}")
 
 
 def test_many_heads_grid():
