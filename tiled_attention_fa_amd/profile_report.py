@@ -1,0 +1,281 @@
+"""Summaries of the rocprofv3 runs behind `bench.py`'s roofline figures.
+
+`bench.py` reports `roofline.traffic` from `profiles/traffic_<workload>.json` (and,
+with `--cold-flush-mib`, from `traffic_cold_<workload>.json`) when the file's
+kernel source hash matches the current sources.  This module writes those files
+and the Markdown summaries beside them from the CSV output of the rocprofv3
+runs that each summary lists, so every committed figure can be rebuilt:
+
+python -m tiled_attention_fa_amd.profile_report warm --workload W --dir D
+python -m tiled_attention_fa_amd.profile_report cold --workload W --dir D
+
+D is the directory the rocprofv3 runs wrote to (their `-d` arguments are
+D/prof_FETCH_SIZE_W, D/prof_WRITE_SIZE_W, D/prof_FETCH_SIZE_copy256,
+D/prof_WRITE_SIZE_copy256 and D/prof_trace_W, whose bench output is
+D/prof_trace_W.log; for "cold", D/prof_FETCH_SIZE_cold_W,
+D/prof_WRITE_SIZE_cold_W and the cold bench's output D/cold_bench_W.log).
+The counters are scaled by what the same counters read for a plain 256 MiB
+device copy, so FETCH_SIZE and WRITE_SIZE become bytes.
+"""
+
+import argparse
+import collections
+import csv
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def agg(path, filt="fa_forward_kernel"):
+    per = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        if filt in r["Kernel_Name"]:
+            per[r["Counter_Name"]].append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in per.items()}, {k: len(v) for k, v in per.items()}
+
+
+def warm(W, G):
+    import workloads
+    import bench
+    fk, nk = agg(f'{G}/prof_FETCH_SIZE_{W}/run_counter_collection.csv', 'fa_forward_kernel')
+    wk, _ = agg(f'{G}/prof_WRITE_SIZE_{W}/run_counter_collection.csv', 'fa_forward_kernel')
+    fc, _ = agg(f'{G}/prof_FETCH_SIZE_copy256/run_counter_collection.csv', 'copyBuffer')
+    wc, _ = agg(f'{G}/prof_WRITE_SIZE_copy256/run_counter_collection.csv', 'copyBuffer')
+    copy_kib = 256 * 1024
+    ffac = fc['FETCH_SIZE'] / copy_kib
+    wfac = wc['WRITE_SIZE'] / copy_kib
+    fetch_b = fk['FETCH_SIZE'] * 1024 / ffac
+    write_b = wk['WRITE_SIZE'] * 1024 / wfac
+    log = open(f'{G}/prof_trace_{W}.log').read().splitlines()
+    rec = json.loads([l for l in log if l.startswith('{')][-1])
+    src_hash = rec['kernel_source_hash']
+    w = workloads.get(W)
+    minb = workloads.min_bytes(w)
+    stats = list(csv.DictReader(open(f'{G}/prof_trace_{W}/run_kernel_stats.csv')))
+    kname = [r for r in stats if 'fa_forward_kernel' in r['Name']][0]
+    out = {
+        "workload": W, "kernel": kname['Name'], "kernel_source_hash": src_hash,
+        "fetch_size_kib_per_dispatch": round(fk['FETCH_SIZE'], 2), "write_size_kib_per_dispatch": round(wk['WRITE_SIZE'], 2),
+        "copy_calibration": {"bytes_read": copy_kib * 1024, "bytes_written": copy_kib * 1024,
+                              "fetch_size_kib": round(fc['FETCH_SIZE'], 2), "write_size_kib": round(wc['WRITE_SIZE'], 2),
+                              "fetch_factor": round(ffac, 5), "write_factor": round(wfac, 5)},
+        "hbm_bytes_per_launch": int(round(fetch_b + write_b)),
+        "hbm_read_bytes_per_launch": int(round(fetch_b)), "hbm_write_bytes_per_launch": int(round(write_b)),
+        "min_bytes": minb, "ratio_to_min": round((fetch_b + write_b) / minb, 4),
+    }
+    P = os.path.join(ROOT, 'profiles')
+    os.makedirs(P, exist_ok=True)
+    json.dump(out, open(f'{P}/traffic_{W}.json', 'w'), indent=1)
+    cmd_pmc = f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {G}/prof_FETCH_SIZE_{W} -o run -- python -u bench.py --workload {W} --steps 20 --warmup 5 --no-cpu-baseline --no-check"
+    md = f"""# HBM bytes of the forward kernel: {W}
+
+Kernel `{kname['Name']}` (kernel source hash `{src_hash}` over the fp16 kernel's source files with comments removed, as `bench.py` computes it).
+
+Commands (run from the repository root on one MI355X, each pass its own process):
+
+    {cmd_pmc}
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d {G}/prof_WRITE_SIZE_{W} -o run -- python -u bench.py --workload {W} --steps 20 --warmup 5 --no-cpu-baseline --no-check
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d {G}/prof_FETCH_SIZE_copy256 -o run -- python -u bench.py --copy-calibration-mib 256 --steps 10 --warmup 2
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d {G}/prof_WRITE_SIZE_copy256 -o run -- python -u bench.py --copy-calibration-mib 256 --steps 10 --warmup 2
+
+| quantity | value |
+|---|---|
+| FETCH_SIZE per dispatch (mean of {nk['FETCH_SIZE']}) | {fk['FETCH_SIZE']:.1f} KiB |
+| WRITE_SIZE per dispatch | {wk['WRITE_SIZE']:.1f} KiB |
+| plain 256 MiB device copy (`__amd_rocclr_copyBuffer`): FETCH_SIZE | {fc['FETCH_SIZE']:.1f} KiB (factor {ffac:.4f} of the bytes read) |
+| same copy: WRITE_SIZE | {wc['WRITE_SIZE']:.1f} KiB (factor {wfac:.4f} of the bytes written) |
+| HBM read per launch (FETCH_SIZE / factor) | {fetch_b/1e6:.2f} MB |
+| HBM write per launch (WRITE_SIZE / factor) | {write_b/1e6:.2f} MB |
+| total | {(fetch_b+write_b)/1e6:.2f} MB |
+| minimum Q+K+V+O | {minb/1e6:.2f} MB |
+| ratio | {(fetch_b+write_b)/minb:.3f} |
+
+The counters measure L2-to-memory traffic, an upper bound on HBM bytes (reads served by the
+Infinity Cache count too).  K and V are re-read by every 128-query workgroup of a head; those
+re-reads are served from the XCD's L2, so the kernel moves about the minimum.
+"""
+    by = f"\nSummary written by `python -m tiled_attention_fa_amd.profile_report warm --workload {W} --dir {G}`.\n"
+    open(f'{P}/fa_forward_{W}_hbm_bytes.md', 'w').write(md + by)
+    cmd_tr = f"rocprofv3 --kernel-trace --stats --output-format csv -d {G}/prof_trace_{W} -o run -- python -u bench.py --workload {W} --steps 100 --warmup 20 --no-cpu-baseline"
+    rows = '\n'.join(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs'])/1e3:.2f} | {float(r['MinNs'])/1e3:.2f} | {float(r['MaxNs'])/1e3:.2f} | {r['Percentage']} |" for r in stats)
+    md2 = f"""# Kernel trace of the benchmark: {W}
+
+Command (repository root, one MI355X):
+
+    {cmd_tr}
+
+`run_kernel_stats.csv` (durations in microseconds; the calls include the clock-settle and warm-up launches and the
+one launch the binding makes before the timed loop):
+
+| kernel | calls | average | min | max | % time |
+|---|---|---|---|---|---|
+{rows}
+
+The JSON line `bench.py` printed in the same run: value {rec['value']} TFLOP/s, mean launch
+{rec['roofline']['kernel_us_mean']} us (HIP events around {rec['steps']} back-to-back launches),
+against the trace's average of {float(kname['AverageNs'])/1e3:.2f} us for the forward kernel.
+"""
+    open(f'{P}/fa_forward_{W}_kernel_trace.md', 'w').write(md2 + by)
+    print(json.dumps(out, indent=1))
+
+    # ---- three-pass comparison path: sum of its three kernels per call
+    if w.dtype != 'f32':
+        names = ['naive13scores_kernel', 'naive14softmax_kernel', 'naive9pv_kernel', 'naive19softmax_long_kernel']
+        def agg_sum(path, counter):
+            per = collections.defaultdict(list)
+            for r in csv.DictReader(open(path)):
+                kn = r['Kernel_Name']
+                if 'naive' in kn and r['Counter_Name'] == counter:
+                    per[kn].append(float(r['Counter_Value']))
+            return {k: (sum(v) / len(v), len(v)) for k, v in per.items()}
+        nf = agg_sum(f'{G}/prof_FETCH_SIZE_{W}/run_counter_collection.csv', 'FETCH_SIZE')
+        nw = agg_sum(f'{G}/prof_WRITE_SIZE_{W}/run_counter_collection.csv', 'WRITE_SIZE')
+        if nf:
+            kinds = sorted(nf)
+            f_b = sum(nf[k][0] for k in kinds) * 1024 / ffac
+            w_b = sum(nw[k][0] for k in kinds) * 1024 / wfac
+            nb = workloads.naive_bytes(w)
+            nhash = bench.kernel_source_hash(w.dtype, bench.NAIVE_SOURCES[w.dtype])
+            nout = {"workload": W, "path": "three-pass (fa_naive_forward)", "kernels": kinds,
+                    "kernel_source_hash": nhash,
+                    "per_kernel_kib": {k: {"fetch": round(nf[k][0], 1), "write": round(nw[k][0], 1), "dispatches": nf[k][1]} for k in kinds},
+                    "hbm_bytes_per_launch": int(round(f_b + w_b)),
+                    "hbm_read_bytes_per_launch": int(round(f_b)), "hbm_write_bytes_per_launch": int(round(w_b)),
+                    "algorithmic_bytes": nb, "ratio_to_algorithmic": round((f_b + w_b) / nb, 4),
+                    "ratio_to_tiled_measured": round((f_b + w_b) / (fetch_b + write_b), 2)}
+            json.dump(nout, open(f'{P}/traffic_naive_{W}.json', 'w'), indent=1)
+            krows = '\n'.join(f"| `{k[:80]}` | {nf[k][0]:.1f} | {nw[k][0]:.1f} | {nf[k][0]*1024/ffac/1e6:.1f} | {nw[k][0]*1024/wfac/1e6:.1f} |" for k in kinds)
+            md3 = f"""# HBM bytes of the three-pass path: {W}
+
+The three kernels of `fa_naive_forward` (scores, softmax, P V), per call, from the same two counter runs as
+`fa_forward_{W}_hbm_bytes.md` (the bench runs the three-pass path after the tiled one) and the same copy calibration.
+Kernel source hash `{nhash}` over the three-pass sources with comments removed, as `bench.py` computes it.
+
+Commands (repository root, one MI355X, each pass its own process):
+
+    {cmd_pmc}
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d {G}/prof_WRITE_SIZE_{W} -o run -- python -u bench.py --workload {W} --steps 20 --warmup 5 --no-cpu-baseline --no-check
+
+| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | read MB | written MB |
+|---|---|---|---|---|
+{krows}
+
+| quantity | value |
+|---|---|
+| HBM bytes per call (read + written) | {(f_b+w_b)/1e6:.1f} MB |
+| algorithmic bytes (`workloads.naive_bytes`) | {nb/1e6:.1f} MB |
+| ratio | {(f_b+w_b)/nb:.3f} |
+| tiled pass, measured | {(fetch_b+write_b)/1e6:.2f} MB |
+| three-pass / tiled, measured | {(f_b+w_b)/(fetch_b+write_b):.1f} |
+"""
+            open(f'{P}/fa_naive_{W}_hbm_bytes.md', 'w').write(md3 + by)
+            print(json.dumps(nout, indent=1))
+
+
+
+def cold(W, G):
+    import bench
+    import workloads
+    f, nf = agg(f'{G}/prof_FETCH_SIZE_cold_{W}/run_counter_collection.csv')
+    wr, nw = agg(f'{G}/prof_WRITE_SIZE_cold_{W}/run_counter_collection.csv')
+    P = os.path.join(ROOT, 'profiles')
+    warm = json.load(open(f'{P}/traffic_{W}.json'))
+    cal = warm['copy_calibration']
+    fb = f['FETCH_SIZE'] * 1024 / cal['fetch_factor']
+    wb = wr['WRITE_SIZE'] * 1024 / cal['write_factor']
+    w = workloads.get(W)
+    rec = json.loads([l for l in open(f'{G}/cold_bench_{W}.log') if l.startswith('{')][-1])
+    out = {"workload": W, "cache": "cold: 512 MiB written before every launch (L2 and the 256 MB Infinity Cache evicted)",
+           "kernel": warm['kernel'], "kernel_source_hash": bench.kernel_source_hash(w.dtype),
+           "fetch_size_kib_per_dispatch": round(f['FETCH_SIZE'], 2), "write_size_kib_per_dispatch": round(wr['WRITE_SIZE'], 2),
+           "dispatches": {"fetch": nf['FETCH_SIZE'], "write": nw['WRITE_SIZE']},
+           "copy_calibration": cal, "hbm_bytes_per_launch": int(round(fb + wb)),
+           "hbm_read_bytes_per_launch": int(round(fb)), "hbm_write_bytes_per_launch": int(round(wb)),
+           "min_bytes": workloads.min_bytes(w), "ratio_to_min": round((fb + wb) / workloads.min_bytes(w), 4),
+           "cold_median_launch_us": round(rec['ms_per_step'] * 1e3, 3), "cold_tflops": rec['value']}
+    json.dump(out, open(f'{P}/traffic_cold_{W}.json', 'w'), indent=1)
+    B = f"python -u bench.py --workload {W} --cold-flush-mib 512 --steps 20 --warmup 5 --settle-s 0.05 --no-cpu-baseline --no-check"
+    md = f"""# HBM bytes of the forward kernel with cold caches: {W}
+
+Kernel `{warm['kernel']}` (kernel source hash `{out['kernel_source_hash']}`).  In cold mode `bench.py` writes a
+512 MiB buffer before every launch of the forward kernel (settle, warm-up and timed launches alike), which evicts L2
+and the 256 MB Infinity Cache, and times each launch between its own pair of events.
+
+Commands (repository root, one MI355X, each pass its own process):
+
+    python -u bench.py --workload {W} --cold-flush-mib 512 --steps 100 --warmup 10 --no-cpu-baseline
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d {G}/prof_FETCH_SIZE_cold_{W} -o run -- {B}
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d {G}/prof_WRITE_SIZE_cold_{W} -o run -- {B}
+
+| | cold | warm (back-to-back launches) |
+|---|---|---|
+| `FETCH_SIZE` per dispatch (KiB) | {f['FETCH_SIZE']:,.1f} (over {nf['FETCH_SIZE']} dispatches) | {warm['fetch_size_kib_per_dispatch']:,.1f} |
+| `WRITE_SIZE` per dispatch (KiB) | {wr['WRITE_SIZE']:,.1f} | {warm['write_size_kib_per_dispatch']:,.1f} |
+| HBM bytes per launch (copy-calibrated: fetch x {1 / cal['fetch_factor']:.3f}, write x {1 / cal['write_factor']:.3f}) | {fb + wb:,.0f} | {warm['hbm_bytes_per_launch']:,} |
+| ratio to the Q+K+V+O minimum ({workloads.min_bytes(w):,} B) | {(fb + wb) / workloads.min_bytes(w):.4f} | {warm['ratio_to_min']} |
+| launch time | {rec['ms_per_step'] * 1e3:.2f} us (median of 100) | ~41 us (mean of back-to-back launches) |
+
+The counters measure L2 egress (requests to the Infinity Fabric, whether the Infinity Cache or DRAM serves them), and
+they read the same with cold and warm caches: the 24 MiB of inputs do not survive in L2 from one launch to the next
+even when warm.  The difference is where the misses are served: with cold caches every byte comes from DRAM, and the
+launch takes ~15% longer.
+"""
+    by = f"\nSummary written by `python -m tiled_attention_fa_amd.profile_report cold --workload {W} --dir {G}`.\n"
+    open(f'{P}/fa_forward_{W}_hbm_bytes_cold.md', 'w').write(md + by)
+    print(md)
+
+
+
+def trace(W, G, run, suffix):
+    """Kernel-trace summary of one `bench.py --workload W` run under
+    `rocprofv3 --kernel-trace --stats -d G/run`, its output in G/run.log."""
+    stats = list(csv.DictReader(open(f"{G}/{run}/run_kernel_stats.csv")))
+    rec = json.loads([l for l in open(f"{G}/{run}.log") if l.startswith("{")][-1])
+    fwd = [r for r in stats if "fa_forward_kernel" in r["Name"]][0]
+    cmd = (f"rocprofv3 --kernel-trace --stats --output-format csv -d {G}/{run} -o run -- python -u bench.py "
+           f"--workload {W} --steps {rec['steps']} --warmup {rec['warmup']} --no-cpu-baseline")
+    rows = "\n".join(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.4g} |"
+                     for r in stats[:6])
+    md = f"""# Kernel trace of the benchmark: {W}
+
+Command (repository root, one MI355X):
+
+    {cmd}
+
+`run_kernel_stats.csv` (durations in microseconds; the calls include the clock-settle and warm-up launches). The
+forward kernel's template arguments end with the waves per workgroup, the waves_per_eu hint and the key groups.
+
+| kernel | calls | average | min | max | % time |
+|---|---|---|---|---|---|
+{rows}
+
+The JSON line `bench.py` printed in the same run: value {rec['value']} TFLOP/s, mean launch
+{rec['ms_per_step'] * 1e3:.3f} us (HIP events around {rec['steps']} back-to-back launches), against the trace's average of
+{float(fwd['AverageNs']) / 1e3:.2f} us for the forward kernel.
+
+Summary written by `python -m tiled_attention_fa_amd.profile_report trace --workload {W} --dir {G} --run {run} --suffix "{suffix}"`.
+"""
+    open(os.path.join(ROOT, "profiles", f"fa_forward_{W}{suffix}_kernel_trace.md"), "w").write(md)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("kind", choices=["warm", "cold", "trace"])
+    ap.add_argument("--workload", default="prefill_b1h32n2048d64_f16")
+    ap.add_argument("--dir", required=True, help="the directory the rocprofv3 runs wrote to")
+    ap.add_argument("--run", default="", help="trace: the run's rocprofv3 -d name under --dir")
+    ap.add_argument("--suffix", default="", help="trace: text appended to the workload in the file name")
+    args = ap.parse_args()
+    sys.path.insert(0, ROOT)
+    G = args.dir.rstrip("/")
+    if args.kind == "trace":
+        trace(args.workload, G, args.run or f"prof_trace_{args.workload}", args.suffix)
+    else:
+        (warm if args.kind == "warm" else cold)(args.workload, G)
+
+
+if __name__ == "__main__":
+    main()
