@@ -228,19 +228,21 @@ launch takes ~15% longer.
 
 
 
-def trace(W, G, run, suffix):
+def trace(W, G, run, suffix, out="", note="", title="", bench_args=""):
     """Kernel-trace summary of one `bench.py --workload W` run under
     `rocprofv3 --kernel-trace --stats -d G/run`, its output in G/run.log."""
     stats = list(csv.DictReader(open(f"{G}/{run}/run_kernel_stats.csv")))
     rec = json.loads([l for l in open(f"{G}/{run}.log") if l.startswith("{")][-1])
     fwd = [r for r in stats if "fa_forward_kernel" in r["Name"]][0]
-    cmd = (f"rocprofv3 --kernel-trace --stats --output-format csv -d {G}/{run} -o run -- python -u bench.py "
-           f"--workload {W} --steps {rec['steps']} --warmup {rec['warmup']} --no-cpu-baseline")
+    args = bench_args or f"--workload {W} --steps {rec['steps']} --warmup {rec['warmup']} --no-cpu-baseline"
+    cmd = f"rocprofv3 --kernel-trace --stats --output-format csv -d {G}/{run} -o run -- python -u bench.py {args}"
     rows = "\n".join(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.4g} |"
                      for r in stats[:6])
-    md = f"""# Kernel trace of the benchmark: {W}
-
+    head = f"# {title}" if title else f"# Kernel trace of the benchmark: {W}"
+    note_md = f"\n{note}\n" if note else ""
+    md = f"""{head}
+{note_md}
 Command (repository root, one MI355X):
 
     {cmd}
@@ -256,23 +258,100 @@ The JSON line `bench.py` printed in the same run: value {rec['value']} TFLOP/s, 
 {rec['ms_per_step'] * 1e3:.3f} us (HIP events around {rec['steps']} back-to-back launches), against the trace's average of
 {float(fwd['AverageNs']) / 1e3:.2f} us for the forward kernel.
 
-Summary written by `python -m tiled_attention_fa_amd.profile_report trace --workload {W} --dir {G} --run {run} --suffix "{suffix}"`.
+Summary written by `python -m tiled_attention_fa_amd.profile_report trace --workload {W} --dir {G} --run {run}` with
+the title, note and file name given.
 """
-    open(os.path.join(ROOT, "profiles", f"fa_forward_{W}{suffix}_kernel_trace.md"), "w").write(md)
+    name = out or f"fa_forward_{W}{suffix}_kernel_trace.md"
+    open(os.path.join(ROOT, "profiles", name), "w").write(md)
+
+
+def sq(W, G, pre):
+    """SQ counters of the forward kernel from the four counter passes
+    G/<pre>_A .. G/<pre>_D (each its own rocprofv3 --pmc run of the bench)."""
+    import glob
+    vals = collections.defaultdict(list)
+    kname = ""
+    for f in sorted(glob.glob(f"{G}/{pre}_*/run_counter_collection.csv")):
+        for r in csv.DictReader(open(f)):
+            if "fa_forward_kernel" in r["Kernel_Name"]:
+                vals[r["Counter_Name"]].append(float(r["Counter_Value"]))
+                kname = r["Kernel_Name"]
+    m = {k: sum(v) / len(v) for k, v in vals.items()}
+    B = f"python -u bench.py --workload {W} --steps 20 --warmup 5 --no-cpu-baseline --no-check --no-naive"
+    passes = {
+        "A": "SQ_WAVES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS "
+             "SQ_WAIT_INST_LDS SQ_WAIT_ANY",
+        "B": "SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_VALU_TRANS_F32 "
+             "SQ_VALU_MFMA_COEXEC_CYCLES SQ_INSTS_SALU",
+        "C": "GRBM_GUI_ACTIVE SQ_CYCLES SQ_INST_LEVEL_LDS SQ_ACTIVE_INST_ANY SQ_THREAD_CYCLES_VALU SQ_LDS_DATA_FIFO_FULL "
+             "SQ_WAIT_INST_ANY SQ_ACTIVE_INST_MISC",
+        "D": "SQ_ACTIVE_INST_SCA SQ_LDS_ADDR_CONFLICT SQ_LDS_UNALIGNED_STALL SQ_LDS_CMD_FIFO_FULL SQ_INST_CYCLES_SALU "
+             "SQ_ACTIVE_INST_FLAT SQ_INSTS_BRANCH SQ_ACTIVE_INST_VMEM",
+    }
+    waves = m["SQ_WAVES"]
+    simds, tiles = 1024, 32
+    life = m["SQ_WAVE_CYCLES"] * 4 / waves
+    mfma = m["SQ_VALU_MFMA_BUSY_CYCLES"] / simds
+    valu = m["SQ_ACTIVE_INST_VALU"] * 4 / simds
+    coex = m["SQ_VALU_MFMA_COEXEC_CYCLES"] / simds
+
+    def per_wave_tile(k):
+        return m[k] / waves / tiles
+
+    lines = [f"# SQ counters of the forward kernel: {W}", "",
+             f"Kernel `{kname}` (8 waves x 32 query rows per workgroup, 256 workgroups, 2048 waves).  Four counter",
+             "passes, each its own process (repository root, one MI355X):", ""]
+    for k, c in passes.items():
+        lines.append(f"    rocprofv3 --pmc {c} --output-format csv -d {G}/{pre}_{k} -o run -- {B}")
+    lines += ["", "Mean per dispatch over the ~2000 dispatches of each pass:", "", "| counter | value |", "|---|---|"]
+    for k in sorted(m):
+        lines.append(f"| `{k}` | {m[k]:,.0f} |")
+    lines += ["", "Derived (MI355X: 256 CUs x 4 SIMDs = 1024 SIMDs, two waves per SIMD; SQ cycle counters in units of 4 "
+              "cycles; one", "MFMA 32x32x16 counts 32 busy cycles):", "", "| quantity | value |", "|---|---|",
+              f"| wave lifetime (SQ_WAVE_CYCLES x 4 / waves) | {life:,.0f} cycles (~{life / 2.0e3:.1f} us at 2.0 GHz) |",
+              f"| matrix-core busy per SIMD (SQ_VALU_MFMA_BUSY_CYCLES / 1024) | {mfma:,.0f} cycles = "
+              f"{100 * mfma / life:.0f}% |",
+              f"| VALU issue per SIMD, MFMA included (SQ_ACTIVE_INST_VALU x 4 / 1024) | {valu:,.0f} cycles = "
+              f"{100 * valu / life:.0f}% |",
+              f"| VALU and MFMA together (SQ_VALU_MFMA_COEXEC_CYCLES / 1024) | {coex:,.0f} cycles = "
+              f"{100 * coex / mfma:.0f}% of the MFMA-busy time |",
+              f"| VALU instructions per wave per 64-key tile (MFMA included) | {per_wave_tile('SQ_INSTS_VALU'):.0f} "
+              f"(transcendental: {per_wave_tile('SQ_INSTS_VALU_TRANS_F32'):.1f}) |",
+              f"| MFMA instructions per wave per tile | {per_wave_tile('SQ_INSTS_MFMA'):.0f} |",
+              f"| LDS instructions per wave per tile | {per_wave_tile('SQ_INSTS_LDS'):.1f} |",
+              f"| scalar instructions per wave per tile | {per_wave_tile('SQ_INSTS_SALU'):.1f} |",
+              f"| LDS bank conflicts | {m['SQ_LDS_BANK_CONFLICT']:.0f} cycles |", ""]
+    lines += ["Under counter collection the dispatches are serialised and run slower end to end, but the wave lifetime "
+              "matches", "the ~41 us of the bench, so the per-wave figures describe the kernel as it runs.  "
+              "SQ_ACTIVE_INST_VALU appears to", "count each MFMA for its 32 busy cycles: 16 x 32 plus about 2 cycles "
+              "for each other VALU instruction of a tile gives", "the measured figure within 2%.  The matrix cores are "
+              "busy about 40% of the wave's life; the VALU issues beside them for", "about three fifths of that time; "
+              "the rest is the latency of each wave's chain of dependent steps (LDS reads, the", "lazy-maximum check, "
+              "the exponentials, the 16-bit conversion of P), which two waves per SIMD do not cover.", "",
+              f"Summary written by `python -m tiled_attention_fa_amd.profile_report sq --workload {W} --dir {G} "
+              f"--run {pre}`.", ""]
+    open(os.path.join(ROOT, "profiles", f"fa_forward_{W}_sq_counters.md"), "w").write("\n".join(lines))
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("kind", choices=["warm", "cold", "trace"])
+    ap.add_argument("kind", choices=["warm", "cold", "trace", "sq"])
     ap.add_argument("--workload", default="prefill_b1h32n2048d64_f16")
     ap.add_argument("--dir", required=True, help="the directory the rocprofv3 runs wrote to")
     ap.add_argument("--run", default="", help="trace: the run's rocprofv3 -d name under --dir")
     ap.add_argument("--suffix", default="", help="trace: text appended to the workload in the file name")
+    ap.add_argument("--out", default="", help="trace: file name under profiles/ (instead of the suffix rule)")
+    ap.add_argument("--title", default="", help="trace: heading")
+    ap.add_argument("--note", default="", help="trace: paragraph under the heading")
+    ap.add_argument("--bench-args", default="", help="trace: the bench.py arguments of the traced run")
     args = ap.parse_args()
     sys.path.insert(0, ROOT)
     G = args.dir.rstrip("/")
     if args.kind == "trace":
-        trace(args.workload, G, args.run or f"prof_trace_{args.workload}", args.suffix)
+        trace(args.workload, G, args.run or f"prof_trace_{args.workload}", args.suffix, args.out, args.note, args.title,
+              args.bench_args)
+    elif args.kind == "sq":
+        sq(args.workload, G, args.run or "pmc")
     else:
         (warm if args.kind == "warm" else cold)(args.workload, G)
 
