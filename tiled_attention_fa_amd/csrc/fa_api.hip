@@ -191,12 +191,12 @@ int suggest_splits(int64_t BH, int64_t N, int64_t D, int dtype, bool causal, int
 // Key groups per workgroup (1 or 2) for the matrix-core kernel, and the
 // waves of the two-group workgroup (*ks_waves, 4 or 8), measured on MI355X.
 // Two groups halve each workgroup's chain of key tiles; the workgroup shape
-// decides how many rounds of workgroups the grid needs.  Rows within one key
+// decides how many passes of workgroups over the CUs the grid needs.  Rows within one key
 // tile have nothing to split.
 //  * Non-causal, with w = B*H times the blocks of 256 rows: w <= CUs / 4
-//    takes 4-wave workgroups of 64 rows (all CUs busy in one round; 24-47%
+//    takes 4-wave workgroups of 64 rows (all CUs busy in one pass; 24-47%
 //    faster); w <= CUs / 2 at D = 64 and 128 takes 8-wave workgroups of 128
-//    rows (one round, two waves per SIMD; 4-30% faster); fuller grids, and
+//    rows (one pass, two waves per SIMD; 4-30% faster); fuller grids, and
 //    D = 96 beyond a quarter, run faster with one group.
 //  * Causal, with the one-group grid's fill of the device's workgroup
 //    slots: up to one half, 4-wave workgroups; up to three quarters, where

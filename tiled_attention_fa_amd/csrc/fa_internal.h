@@ -76,7 +76,7 @@ constexpr int mfma_waves(int D, bool causal) { return D == 96 || (D == 64 && cau
 constexpr int mfma_wgs_per_cu(int D, bool causal) { return D == 64 && causal ? 2 : 1; }
 // With two key groups: 4 waves (2 row blocks of 32 x 2 groups, 64 rows per
 // workgroup), two workgroups per CU where the LDS allows it (D = 64); or, on
-// grids that would need more than one round of those, 8 waves (128 rows).
+// grids that would need more than one pass of those over the CUs, 8 waves (128 rows).
 constexpr int mfma_ks_waves = 4;
 constexpr int mfma_ks_occupancy(int D) { return D == 64 ? 2 : 1; }
 
