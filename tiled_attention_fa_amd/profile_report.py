@@ -26,6 +26,7 @@ import os
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OUT = os.path.join(ROOT, "profiles")  # where the summaries go (--out-dir)
 
 
 def agg(path, filt="fa_forward_kernel"):
@@ -65,7 +66,7 @@ def warm(W, G):
         "hbm_read_bytes_per_launch": int(round(fetch_b)), "hbm_write_bytes_per_launch": int(round(write_b)),
         "min_bytes": minb, "ratio_to_min": round((fetch_b + write_b) / minb, 4),
     }
-    P = os.path.join(ROOT, 'profiles')
+    P = OUT
     os.makedirs(P, exist_ok=True)
     json.dump(out, open(f'{P}/traffic_{W}.json', 'w'), indent=1)
     cmd_pmc = f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {G}/prof_FETCH_SIZE_{W} -o run -- python -u bench.py --workload {W} --steps 20 --warmup 5 --no-cpu-baseline --no-check"
@@ -180,7 +181,7 @@ def cold(W, G):
     import workloads
     f, nf = agg(f'{G}/prof_FETCH_SIZE_cold_{W}/run_counter_collection.csv')
     wr, nw = agg(f'{G}/prof_WRITE_SIZE_cold_{W}/run_counter_collection.csv')
-    P = os.path.join(ROOT, 'profiles')
+    P = OUT
     warm = json.load(open(f'{P}/traffic_{W}.json'))
     cal = warm['copy_calibration']
     fb = f['FETCH_SIZE'] * 1024 / cal['fetch_factor']
@@ -262,7 +263,7 @@ Summary written by `python -m tiled_attention_fa_amd.profile_report trace --work
 the title, note and file name given.
 """
     name = out or f"fa_forward_{W}{suffix}_kernel_trace.md"
-    open(os.path.join(ROOT, "profiles", name), "w").write(md)
+    open(os.path.join(OUT, name), "w").write(md)
 
 
 def sq(W, G, pre):
@@ -330,10 +331,11 @@ def sq(W, G, pre):
               "the exponentials, the 16-bit conversion of P), which two waves per SIMD do not cover.", "",
               f"Summary written by `python -m tiled_attention_fa_amd.profile_report sq --workload {W} --dir {G} "
               f"--run {pre}`.", ""]
-    open(os.path.join(ROOT, "profiles", f"fa_forward_{W}_sq_counters.md"), "w").write("\n".join(lines))
+    open(os.path.join(OUT, f"fa_forward_{W}_sq_counters.md"), "w").write("\n".join(lines))
 
 
 def main():
+    global OUT
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("kind", choices=["warm", "cold", "trace", "sq"])
     ap.add_argument("--workload", default="prefill_b1h32n2048d64_f16")
@@ -344,7 +346,9 @@ def main():
     ap.add_argument("--title", default="", help="trace: heading")
     ap.add_argument("--note", default="", help="trace: paragraph under the heading")
     ap.add_argument("--bench-args", default="", help="trace: the bench.py arguments of the traced run")
+    ap.add_argument("--out-dir", default=OUT, help="where the JSON and Markdown files go (default: profiles/)")
     args = ap.parse_args()
+    OUT = args.out_dir
     sys.path.insert(0, ROOT)
     G = args.dir.rstrip("/")
     if args.kind == "trace":
