@@ -374,7 +374,8 @@ def main():
     # Median of individually bracketed launches (each with its own event
     # pair, so it includes the event overhead; reported beside the mean).
     singles = cold_us if cold else []
-    for _ in range(0 if cold else max(20, min(args.steps, 50))):
+    n_singles = 0 if cold else max(20, min(args.steps, 50))
+    for _ in range(n_singles):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -420,6 +421,9 @@ def main():
             "min_bytes": workloads.min_bytes(w) * (w.H + kvh) // (2 * w.H),
         },
         "median_single_launch_us": round(median_single_us, 3),
+        # where the timed launches sit among the forward kernel's dispatches
+        # (a kernel trace of this run takes its steady-state figure from them)
+        "trace_window": {"timed_launches": args.steps, "launches_after_timed": n_singles},
         "untimed_settle": {"seconds": args.settle_s, "launches": settle_launches},
         "device": {"name": prop.name, "arch": getattr(prop, "gcnArchName", ""),
                    "cus": prop.multi_processor_count, "max_clock_mhz": round(fa.fa_device_info()[1] / 1000),

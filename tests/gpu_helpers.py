@@ -64,9 +64,10 @@ def parity(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = "") -> dict
         worst = float((err - bound).max()) if err.size else -1.0
         assert worst <= 0, (f"{what}: bf16 error exceeds 2e-3 + half ulp by {worst:.3e} "
                             f"(literal max abs {max_abs:.3e})")
-    else:
-        assert max_abs <= ABS_TOL[dtype], f"{what}: max abs error {max_abs:.3e} > {ABS_TOL[dtype]}"
-    return {"max_abs": max_abs}
+        return {"max_abs": max_abs, "bound": "2e-3 + half a bf16 ulp, elementwise",
+                "worst_over_bound": worst}
+    assert max_abs <= ABS_TOL[dtype], f"{what}: max abs error {max_abs:.3e} > {ABS_TOL[dtype]}"
+    return {"max_abs": max_abs, "bound": f"{ABS_TOL[dtype]:g}"}
 
 
 # ---- strided layouts and grouped key/value heads

@@ -197,6 +197,22 @@ def _stream_handle(stream, device):
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _used_on(stream, device, *tensors):
+    """Tensors allocated here on torch's current stream and written by
+    kernels enqueued on `stream`: when that is another stream, record it on
+    them, so that the caching allocator does not hand their memory out again
+    (to work on the current stream) before `stream` has finished with it."""
+    import torch
+    if stream is None:
+        return
+    s = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(int(stream), device=device)
+    if s == torch.cuda.current_stream(device):
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(s)
+
+
 def fa_forward(q, k, v, o, scale=None, causal=False, stream=None) -> None:
     """o <- softmax(scale * q k^T [+ causal mask]) v for torch tensors of shape
     [B, H, N, D] on the current HIP device (contiguous, one dtype).
@@ -216,10 +232,12 @@ def fa_forward(q, k, v, o, scale=None, causal=False, stream=None) -> None:
 
 
 def forward(q, k, v, scale=None, causal=False, stream=None):
-    """Allocate o like q and run fa_forward; returns o."""
+    """Allocate o like q and run fa_forward; returns o.  With a stream other
+    than torch's current one, o is recorded as in use by that stream."""
     import torch
     o = torch.empty_like(q)
     fa_forward(q, k, v, o, scale=scale, causal=causal, stream=stream)
+    _used_on(stream, q.device, o)
     return o
 
 
@@ -257,11 +275,13 @@ def fa_naive_forward(q, k, v, o, workspace, scale=None, causal=False, stream=Non
 
 def naive_forward(q, k, v, scale=None, causal=False, stream=None, workspace=None):
     """Allocate o (and the workspace unless given) and run the three-pass
-    path; returns o."""
+    path; returns o.  With a stream other than torch's current one, what was
+    allocated here is recorded as in use by that stream."""
     import torch
     o = torch.empty_like(q)
     ws = workspace if workspace is not None else naive_workspace(q)
     fa_naive_forward(q, k, v, o, ws, scale=scale, causal=causal, stream=stream)
+    _used_on(stream, q.device, o, ws if workspace is None else None)
     return o
 
 
@@ -307,7 +327,8 @@ def forward_ex(q, k, v, scale=None, causal=False, num_splits=1, lse=False, works
     """O (and, with lse=True, the [B, H, N] float32 log-sum-exp) through
     fa_forward_ex; num_splits 0 takes the suggestion.  Allocates o, the lse
     tensor and (unless given) the workspace with torch; returns o or
-    (o, lse)."""
+    (o, lse).  With a stream other than torch's current one, what was
+    allocated here is recorded as in use by that stream."""
     import torch
     o = torch.empty_like(q)
     B, H, N, _ = q.shape
@@ -316,6 +337,7 @@ def forward_ex(q, k, v, scale=None, causal=False, num_splits=1, lse=False, works
         ws = workspace if workspace is not None else splitkv_workspace(q, num_splits, causal)
     fa_forward_ex(q, k, v, o, lse_t, scale=scale, causal=causal, num_splits=num_splits, workspace=ws,
                   stream=stream)
+    _used_on(stream, q.device, o, lse_t, ws if workspace is None else None)
     return (o, lse_t) if lse else o
 
 

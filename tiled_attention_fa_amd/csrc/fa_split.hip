@@ -13,7 +13,9 @@
 //   O   = sum_r exp(lse_r - lse) O_r
 //
 // A range that held no visible key of the row has lse_r = -inf, O_r = 0 and
-// weight 0.
+// weight 0.  A row that no range saw (every lse_r = -inf, so the total
+// weight L is 0) is written as 0 with lse = -inf, as the fused epilogue
+// writes a row whose denominator is 0.
 // One thread per 4 consecutive columns of a row; the partials are fp32,
 // [splits, rows, D] and [splits, rows].
 #include <hip/hip_runtime.h>
@@ -69,8 +71,9 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeProblem p) {
       L += w;
       acc += w * o;
     }
-    store4<OutT>(p.o, (size_t)row * p.D + 4 * g, acc * (1.f / L));
-    if (p.lse != nullptr && g == 0) p.lse[row] = M + logf(L);
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    store4<OutT>(p.o, (size_t)row * p.D + 4 * g, acc * inv);
+    if (p.lse != nullptr && g == 0) p.lse[row] = L > 0.f ? M + logf(L) : -INFINITY;
   }
 }
 

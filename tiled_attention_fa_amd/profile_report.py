@@ -37,6 +37,39 @@ def agg(path, filt="fa_forward_kernel"):
     return {k: sum(v) / len(v) for k, v in per.items()}, {k: len(v) for k, v in per.items()}
 
 
+def steady(trace_csv, rec, filt="fa_forward_kernel"):
+    """Duration of the timed launches alone, from the per-dispatch kernel
+    trace: the forward kernel's dispatches in start order, of which the
+    bench's timed launches are the `timed_launches` before the last
+    `launches_after_timed` (the clock-settle and warm-up launches come
+    first).  Returns mean and median in microseconds, or None when the run
+    did not record its window."""
+    win = rec.get("trace_window")
+    if not win or not os.path.exists(trace_csv):
+        return None
+    rows = [r for r in csv.DictReader(open(trace_csv)) if filt in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    k, after = win["timed_launches"], win["launches_after_timed"]
+    timed = rows[len(rows) - after - k:len(rows) - after]
+    us = sorted((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in timed)
+    if not us:
+        return None
+    mid = len(us) // 2
+    med = us[mid] if len(us) % 2 else 0.5 * (us[mid - 1] + us[mid])
+    return {"n": len(us), "mean_us": sum(us) / len(us), "median_us": med,
+            "bench_ms_per_step_us": rec["ms_per_step"] * 1e3}
+
+
+def steady_md(st):
+    if st is None:
+        return ""
+    return (f"\nSteady state: the {st['n']} timed launches alone (from `run_kernel_trace.csv`, the clock-settle, "
+            f"warm-up and\nafter-loop launches left out) average {st['mean_us']:.2f} us, median {st['median_us']:.2f} us, "
+            f"against the bench's\n{st['bench_ms_per_step_us']:.3f} us per step "
+            f"({100 * (st['mean_us'] / st['bench_ms_per_step_us'] - 1):+.2f}%; the events also time the gaps between "
+            f"launches).\n")
+
+
 def warm(W, G):
     import workloads
     import bench
@@ -117,7 +150,7 @@ one launch the binding makes before the timed loop):
 The JSON line `bench.py` printed in the same run: value {rec['value']} TFLOP/s, mean launch
 {rec['roofline']['kernel_us_mean']} us (HIP events around {rec['steps']} back-to-back launches),
 against the trace's average of {float(kname['AverageNs'])/1e3:.2f} us for the forward kernel.
-"""
+{steady_md(steady(f'{G}/prof_trace_{W}/run_kernel_trace.csv', rec))}"""
     open(f'{P}/fa_forward_{W}_kernel_trace.md', 'w').write(md2 + by)
     print(json.dumps(out, indent=1))
 
@@ -258,7 +291,7 @@ forward kernel's template arguments end with the waves per workgroup, the waves_
 The JSON line `bench.py` printed in the same run: value {rec['value']} TFLOP/s, mean launch
 {rec['ms_per_step'] * 1e3:.3f} us (HIP events around {rec['steps']} back-to-back launches), against the trace's average of
 {float(fwd['AverageNs']) / 1e3:.2f} us for the forward kernel.
-
+{steady_md(steady(f"{G}/{run}/run_kernel_trace.csv", rec))}
 Summary written by `python -m tiled_attention_fa_amd.profile_report trace --workload {W} --dir {G} --run {run}` with
 the title, note and file name given.
 """
