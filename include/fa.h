@@ -58,7 +58,8 @@ typedef enum fa_status {
   FA_ERR_DEVICE = -10,        /* current device is not gfx950, or no device */
   FA_ERR_WORKSPACE = -11,     /* workspace NULL, misaligned, too small or overlapping */
   FA_ERR_SPLITS = -12,        /* num_splits outside 0..64 */
-  FA_ERR_STRIDE = -13         /* negative strides, rows shorter than D, overlapping o rows */
+  FA_ERR_STRIDE = -13,        /* negative strides, rows shorter than D, overlapping o rows */
+  FA_ERR_SCRATCH = -14        /* fa_forward_ex_noalloc: the partials exceed the fixed scratch */
 } fa_status;
 
 /*
@@ -171,6 +172,29 @@ int fa_forward_strided(const void* q, const int64_t* q_strides, const void* k,
 int fa_forward_ex(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
                   int64_t H, int64_t N, int64_t D, float scale, int causal, int dtype,
                   int num_splits, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * fa_forward_ex_noalloc -- fa_forward_ex for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments without workspace / workspace_bytes, the
+ * same kernels and results.  The split-KV partials go to a scratch array of
+ * FA_NOALLOC_SCRATCH_BYTES that the library holds in each device's memory
+ * from the first call on that device until the process ends; the call
+ * allocates nothing and clears nothing (every partial the merge reads is
+ * written earlier in the same call).
+ *
+ * A call whose partials (fa_forward_ex_workspace_bytes for the same
+ * arguments) exceed FA_NOALLOC_SCRATCH_BYTES returns FA_ERR_SCRATCH and
+ * enqueues nothing; num_splits resolving to 1 needs no scratch.  Other
+ * checks and codes as fa_forward_ex (FA_ERR_DEVICE also when the scratch
+ * address cannot be looked up).  All calls on one device share its scratch
+ * array: calls that overlap in time on one device (two streams, two host
+ * threads) race and must be serialised by the caller.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (64LL * 1024 * 1024)
+int fa_forward_ex_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int64_t B, int64_t H, int64_t N, int64_t D, float scale, int causal,
+                          int dtype, int num_splits, void* stream);
 
 /*
  * fa_forward_ex_workspace_bytes -- workspace bytes fa_forward_ex needs

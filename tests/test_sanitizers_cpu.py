@@ -6,7 +6,7 @@ fatal:
   * the fp64 oracle (gcc, -fsanitize=address,undefined) under the oracle's
     pins (test_oracle_pins.py);
   * the library's host code, the argument checks of every entry point
-    (fa_api.hip built by hipcc with the sanitizers on the
+    (fa_api.hip, fa_noalloc.hip built by hipcc with the sanitizers on the
     host side only, linked with the uninstrumented kernel objects) under the
     C ABI tests (test_abi_cpu.py), which call every entry point with valid
     and invalid arguments.
@@ -67,7 +67,7 @@ def _clang_asan_runtime():
 
 def test_abi_host_code_under_asan_ubsan(tmp_path):
     rt = _clang_asan_runtime()
-    host_srcs = ("fa_api.hip",)
+    host_srcs = ("fa_api.hip", "fa_noalloc.hip")
     objs = []
     for name in host_srcs:
         objs.append(hipbuild._compile(os.path.join(hipbuild.CSRC, name), HOST_SAN + ["-g"], str(tmp_path)))

@@ -15,6 +15,8 @@ from ._lib import (  # noqa: F401
     STATUS_NAMES,
     fa_forward,
     fa_forward_ex,
+    fa_forward_ex_noalloc,
+    fa_forward_ex_noalloc_raw,
     fa_forward_ex_raw,
     fa_forward_ex_workspace_bytes,
     fa_forward_raw,

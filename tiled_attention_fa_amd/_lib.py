@@ -24,10 +24,12 @@ STATUS_NAMES = {
     -11: "FA_ERR_WORKSPACE",
     -12: "FA_ERR_SPLITS",
     -13: "FA_ERR_STRIDE",
+    -14: "FA_ERR_SCRATCH",
 }
 
 # Every symbol include/fa.h declares.
-EXPORTS = ("fa_device_info", "fa_forward", "fa_forward_ex", "fa_forward_ex_workspace_bytes",
+EXPORTS = ("fa_device_info", "fa_forward", "fa_forward_ex", "fa_forward_ex_noalloc",
+           "fa_forward_ex_workspace_bytes",
            "fa_forward_strided", "fa_key_groups_suggest", "fa_naive_forward", "fa_naive_workspace_bytes",
            "fa_splitkv_suggest", "fa_status_string", "fa_version")
 
@@ -64,6 +66,9 @@ def load_library():
     lib.fa_forward_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float, ctypes.c_int,
                                   ctypes.c_int, ctypes.c_int, vp, i64, vp]
     lib.fa_forward_ex.restype = ctypes.c_int
+    lib.fa_forward_ex_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float,
+                                          ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
+    lib.fa_forward_ex_noalloc.restype = ctypes.c_int
     lib.fa_forward_ex_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int,
                                                   ctypes.c_int]
     lib.fa_forward_ex_workspace_bytes.restype = i64
@@ -134,6 +139,17 @@ def fa_forward_ex_raw(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, 
                                         int(B), int(H), int(N), int(D), float(scale),
                                         int(bool(causal)), int(dtype), int(num_splits),
                                         workspace or None, int(workspace_bytes), stream or None)
+
+
+def fa_forward_ex_noalloc_raw(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, N: int, D: int,
+                              scale: float, causal: bool, dtype: int, num_splits: int,
+                              stream: int = 0) -> int:
+    """Direct call of fa_forward_ex_noalloc (split-KV partials in the
+    library's fixed per-device scratch); returns the status code."""
+    return load_library().fa_forward_ex_noalloc(q or None, k or None, v or None, o or None, lse or None,
+                                                int(B), int(H), int(N), int(D), float(scale),
+                                                int(bool(causal)), int(dtype), int(num_splits),
+                                                stream or None)
 
 
 def fa_forward_ex_workspace_bytes(B: int, H: int, N: int, D: int, dtype: int, causal: bool,
@@ -318,6 +334,30 @@ def fa_forward_ex(q, k, v, o, lse=None, scale=None, causal=False, num_splits=1, 
         st = fa_forward_ex_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                lse.data_ptr() if lse is not None else 0, B, H, N, D, scale, causal,
                                _dtype_code(q), num_splits, ws_ptr, ws_bytes, handle)
+    if st != 0:
+        raise FAError(st)
+
+
+def fa_forward_ex_noalloc(q, k, v, o, lse=None, scale=None, causal=False, num_splits=1,
+                          stream=None) -> None:
+    """fa_forward_ex_noalloc on torch tensors: as fa_forward_ex without a
+    workspace (the library's fixed scratch holds the split-KV partials; the
+    call allocates nothing).  Calls that overlap in time on one device race.
+    Enqueues and returns; raises FAError on a rejected call (FA_ERR_SCRATCH
+    when the partials exceed the scratch)."""
+    import torch
+    _check_qkvo(q, k, v, o)
+    B, H, N, D = q.shape
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N)
+                            or not lse.is_contiguous() or lse.device != q.device):
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    handle = _stream_handle(stream, q.device)
+    with torch.cuda.device(q.device):
+        st = fa_forward_ex_noalloc_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                       lse.data_ptr() if lse is not None else 0, B, H, N, D, scale,
+                                       causal, _dtype_code(q), num_splits, handle)
     if st != 0:
         raise FAError(st)
 

@@ -533,6 +533,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_WORKSPACE: return "workspace NULL, not 256-byte aligned, too small or overlapping a tensor";
     case FA_ERR_SPLITS: return "num_splits out of range (0 for the suggestion, else 1..64)";
     case FA_ERR_STRIDE: return "invalid strides (negative, rows shorter than D, or overlapping output rows)";
+    case FA_ERR_SCRATCH: return "split-KV partials exceed the fixed scratch of fa_forward_ex_noalloc (64 MiB)";
     default: return "unknown status";
   }
 }
