@@ -324,18 +324,44 @@ def test_tune_library_exports_its_header():
     lib = tile_sweep.load_tune()
     text = re.sub(r"/\*.*?\*/", "", open(TUNE_HEADER).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(fa_\w+)\s*\(", text)))
-    assert names == ["fa_tune_forward", "fa_tune_shapes"]
+    assert names == ["fa_tune_forward", "fa_tune_shapes", "fa_tune_split_merge"]
     out = subprocess.run(["nm", "-D", "--defined-only", tile_sweep.TUNE_LIB], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (fa_\w+)", out))
     for n in names + list(EXPORTS):
         assert n in exported, n
-    assert tile_sweep.shapes(lib, 64) == [(2, 1, 1), (4, 1, 1), (4, 2, 1), (8, 1, 1), (4, 1, 2), (4, 2, 2),
-                                          (8, 1, 2)]
-    wide = [(2, 1, 1), (4, 1, 1), (8, 1, 1), (4, 1, 2), (8, 1, 2)]
+    assert tile_sweep.shapes(lib, 64) == [
+        (2, 1, 1, 64), (4, 1, 1, 64), (4, 2, 1, 64), (8, 1, 1, 64), (4, 1, 2, 64), (4, 2, 2, 64), (8, 1, 2, 64),
+        (2, 1, 1, 32), (4, 1, 1, 32), (4, 2, 1, 32), (8, 1, 1, 32), (2, 1, 1, 128), (4, 1, 1, 128),
+        (8, 1, 1, 128)]
+    wide = [(2, 1, 1, 64), (4, 1, 1, 64), (8, 1, 1, 64), (4, 1, 2, 64), (8, 1, 2, 64), (2, 1, 1, 32),
+            (4, 1, 1, 32), (8, 1, 1, 32)]
     assert tile_sweep.shapes(lib, 96) == wide
     assert tile_sweep.shapes(lib, 128) == wide
-    assert lib.fa_tune_shapes(80, None, None, None, 0) == -3
+    assert lib.fa_tune_shapes(80, None, None, None, None, 0) == -3
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(dtype=5), "FA_ERR_DTYPE"),
+    (dict(rows=-1), "FA_ERR_DIM"),
+    (dict(D=80), "FA_ERR_DIM"),
+    (dict(S=0), "FA_ERR_SPLITS"),
+    (dict(S=65), "FA_ERR_SPLITS"),
+    (dict(rows=0, po=0, pl=0, o=0), "FA_OK"),
+    (dict(po=0), "FA_ERR_NULL"),
+    (dict(o=O + 8), "FA_ERR_ALIGN"),
+    (dict(), "FA_ERR_DEVICE"),
+])
+def test_tune_split_merge_validation(args, status):
+    from tiled_attention_fa_amd import tile_sweep
+    lib = tile_sweep.load_tune()
+    kw = dict(po=A, pl=B_, o=O, lse=0, rows=4, D=64, S=2, dtype=1)
+    kw.update(args)
+    got = lib.fa_tune_split_merge(kw["po"] or None, kw["pl"] or None, kw["o"] or None, kw["lse"] or None,
+                                  kw["rows"], kw["D"], kw["S"], kw["dtype"], None)
+    if status == "FA_ERR_DEVICE" and got == 0:
+        pytest.skip("a gfx950 device is present; the no-device path is not reachable")
+    assert fa.STATUS_NAMES[got] == status
 
 
 @pytest.mark.parametrize("args,status", [
@@ -346,16 +372,21 @@ def test_tune_library_exports_its_header():
     (dict(D=128, waves=4, occ=2, ks=2), "FA_ERR_UNSUPPORTED_D"),
     (dict(waves=2, occ=1, ks=2), "FA_ERR_UNSUPPORTED_D"),
     (dict(ks=3), "FA_ERR_UNSUPPORTED_D"),
+    (dict(bn=96), "FA_ERR_UNSUPPORTED_D"),
+    (dict(bn=128, occ=2), "FA_ERR_UNSUPPORTED_D"),
+    (dict(D=128, waves=8, occ=1, bn=128), "FA_ERR_UNSUPPORTED_D"),
+    (dict(waves=4, occ=1, ks=2, bn=32), "FA_ERR_UNSUPPORTED_D"),
     (dict(o=A), "FA_ERR_ALIAS"),
     (dict(), "FA_ERR_DEVICE"),
+    (dict(waves=8, occ=1, bn=128), "FA_ERR_DEVICE"),
 ])
 def test_tune_forward_validation(args, status):
     from tiled_attention_fa_amd import tile_sweep
     lib = tile_sweep.load_tune()
-    kw = dict(q=A, k=B_, v=C, o=O, B=1, H=1, N=64, D=64, dtype=1, waves=4, occ=2, ks=1)
+    kw = dict(q=A, k=B_, v=C, o=O, B=1, H=1, N=64, D=64, dtype=1, waves=4, occ=2, ks=1, bn=64)
     kw.update(args)
     got = lib.fa_tune_forward(kw["q"], kw["k"], kw["v"], kw["o"], kw["B"], kw["H"], kw["N"], kw["D"],
-                              0.125, 0, kw["dtype"], kw["waves"], kw["occ"], kw["ks"], None)
+                              0.125, 0, kw["dtype"], kw["waves"], kw["occ"], kw["ks"], kw["bn"], None)
     if status == "FA_ERR_DEVICE" and got == 0:
         pytest.skip("a gfx950 device is present; the no-device path is not reachable")
     assert fa.STATUS_NAMES[got] == status

@@ -478,7 +478,7 @@ int fa_forward_strided(const void* q, const int64_t* q_strides, const void* k, c
 }
 
 #ifdef FA_TILE_SWEEP
-int fa_tune_shapes(int64_t D, int* waves, int* occupancy, int* key_groups, int capacity) {
+int fa_tune_shapes(int64_t D, int* waves, int* occupancy, int* key_groups, int* block_n, int capacity) {
   if (!head_dim_supported(D)) return FA_ERR_UNSUPPORTED_D;
   const int n = D == 64 ? fa::kTuneShapes64Count : fa::kTuneShapesWideCount;
   for (int i = 0; i < n && i < capacity; ++i) {
@@ -486,18 +486,20 @@ int fa_tune_shapes(int64_t D, int* waves, int* occupancy, int* key_groups, int c
     if (waves) waves[i] = s[0];
     if (occupancy) occupancy[i] = s[1];
     if (key_groups) key_groups[i] = s[2];
+    if (block_n) block_n[i] = s[3];
   }
   return n;
 }
 
 int fa_tune_forward(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H, int64_t N,
                     int64_t D, float scale, int causal, int dtype, int waves, int occupancy, int key_groups,
-                    void* stream) {
+                    int block_n, void* stream) {
   if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
-  int sw[8], so[8], sk[8];
-  const int n = fa_tune_shapes(D, sw, so, sk, 8);
+  int sw[16], so[16], sk[16], sb[16];
+  const int n = fa_tune_shapes(D, sw, so, sk, sb, 16);
   bool known = false;
-  for (int i = 0; i < n; ++i) known = known || (sw[i] == waves && so[i] == occupancy && sk[i] == key_groups);
+  for (int i = 0; i < n; ++i)
+    known = known || (sw[i] == waves && so[i] == occupancy && sk[i] == key_groups && sb[i] == block_n);
   int64_t BH = 0;
   // rows per workgroup bound the grid (any positive block is safe to check
   // before the shape itself is; an unknown shape is rejected below)
@@ -511,9 +513,34 @@ int fa_tune_forward(const void* q, const void* k, const void* v, void* o, int64_
   fa::Problem p = dense_problem(q, k, v, o, H, BH, N, D, scale, causal);
   p.key_groups = key_groups;
   const hipError_t err =
-      dtype == FA_F16 ? fa::launch_mfma_shape_f16(p, waves, occupancy, key_groups, (hipStream_t)stream)
-                      : fa::launch_mfma_shape_bf16(p, waves, occupancy, key_groups, (hipStream_t)stream);
+      dtype == FA_F16 ? fa::launch_mfma_shape_f16(p, waves, occupancy, key_groups, block_n, (hipStream_t)stream)
+                      : fa::launch_mfma_shape_bf16(p, waves, occupancy, key_groups, block_n, (hipStream_t)stream);
   return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+/* The split-KV merge alone, on caller-made partials (for its closed-form
+ * checks): part_o [splits, rows, D] fp32 and part_lse [splits, rows] fp32 in,
+ * o [rows, D] in the storage type and, if not NULL, lse [rows] out. */
+int fa_tune_split_merge(const float* part_o, const float* part_lse, void* o, float* lse, int64_t rows, int64_t D,
+                        int splits, int dtype, void* stream) {
+  if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (rows < 0 || !head_dim_supported(D)) return FA_ERR_DIM;
+  if (splits < 1 || splits > kMaxSplits) return FA_ERR_SPLITS;
+  if (rows == 0) return FA_OK;
+  if (!part_o || !part_lse || !o) return FA_ERR_NULL;
+  if (((uintptr_t)part_o | (uintptr_t)o) & 15u) return FA_ERR_ALIGN;
+  const int dev = check_device();
+  if (dev != FA_OK) return dev;
+  fa::MergeProblem m;
+  m.part_o = part_o;
+  m.part_lse = part_lse;
+  m.o = o;
+  m.lse = lse;
+  m.rows = rows;
+  m.D = (int)D;
+  m.splits = splits;
+  m.dtype = dtype;
+  return fa::launch_split_merge(m, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 #endif
 

@@ -73,6 +73,11 @@ struct MergeProblem {
 // (one wave per SIMD: 128-element LDS rows leave room for one workgroup per
 // CU).
 constexpr int mfma_waves(int D, bool causal) { return D == 96 || (D == 64 && causal) ? 4 : 8; }
+// Keys per LDS tile of the one-group kernel, from the same sweep over 32, 64
+// and 128: 64, except bf16 at D = 128 (split P), where 32-key tiles are 0.2-2%
+// faster (the 64-key build of that kernel needs a few more registers than it
+// has and spills them).  128-key tiles were never the fastest.
+constexpr int mfma_block_n(int D, bool split_p) { return D == 128 && split_p ? 32 : 64; }
 constexpr int mfma_wgs_per_cu(int D, bool causal) { return D == 64 && causal ? 2 : 1; }
 // With two key groups: 4 waves (2 row blocks of 32 x 2 groups, 64 rows per
 // workgroup), two workgroups per CU where the LDS allows it (D = 64); or, on
@@ -116,12 +121,18 @@ hipError_t launch_f32(const Problem& p, hipStream_t stream);
 hipError_t launch_split_merge(const MergeProblem& p, hipStream_t stream);
 #ifdef FA_TILE_SWEEP
 // The calibration sweep's shapes (tuning library only): (waves per
-// workgroup, waves_per_eu hint, key groups).
-constexpr int kTuneShapes64[][3] = {{2, 1, 1}, {4, 1, 1}, {4, 2, 1}, {8, 1, 1}, {4, 1, 2}, {4, 2, 2}, {8, 1, 2}};
-constexpr int kTuneShapesWide[][3] = {{2, 1, 1}, {4, 1, 1}, {8, 1, 1}, {4, 1, 2}, {8, 1, 2}};
-constexpr int kTuneShapes64Count = 7, kTuneShapesWideCount = 5;
-hipError_t launch_mfma_shape_f16(const Problem& p, int waves, int occupancy, int key_groups, hipStream_t stream);
-hipError_t launch_mfma_shape_bf16(const Problem& p, int waves, int occupancy, int key_groups, hipStream_t stream);
+// workgroup, waves_per_eu hint, key groups, keys per LDS tile).
+constexpr int kTuneShapes64[][4] = {{2, 1, 1, 64},  {4, 1, 1, 64},  {4, 2, 1, 64},  {8, 1, 1, 64},
+                                    {4, 1, 2, 64},  {4, 2, 2, 64},  {8, 1, 2, 64},  {2, 1, 1, 32},
+                                    {4, 1, 1, 32},  {4, 2, 1, 32},  {8, 1, 1, 32},  {2, 1, 1, 128},
+                                    {4, 1, 1, 128}, {8, 1, 1, 128}};
+constexpr int kTuneShapesWide[][4] = {{2, 1, 1, 64}, {4, 1, 1, 64}, {8, 1, 1, 64}, {4, 1, 2, 64},
+                                      {8, 1, 2, 64}, {2, 1, 1, 32}, {4, 1, 1, 32}, {8, 1, 1, 32}};
+constexpr int kTuneShapes64Count = 14, kTuneShapesWideCount = 8;
+hipError_t launch_mfma_shape_f16(const Problem& p, int waves, int occupancy, int key_groups, int block_n,
+                                  hipStream_t stream);
+hipError_t launch_mfma_shape_bf16(const Problem& p, int waves, int occupancy, int key_groups, int block_n,
+                                   hipStream_t stream);
 #endif
 hipError_t launch_naive_f16(const NaiveProblem& p, hipStream_t stream);
 hipError_t launch_naive_bf16(const NaiveProblem& p, hipStream_t stream);

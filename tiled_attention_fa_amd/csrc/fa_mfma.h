@@ -87,7 +87,7 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
-constexpr int kBlockN = 64;  // keys per iteration
+constexpr int kBlockN = 64;  // keys per LDS tile unless the shape says otherwise
 constexpr int kXcds = 8;     // MI355X: 8 accelerator complex dies, one L2 each
 constexpr float kLazy = 8.f;  // log2 of the largest p the lazy maximum allows
 
@@ -204,23 +204,41 @@ __device__ __forceinline__ float max32(const float (&x)[2][16]) {
   return fmaxf(fmaxf(b0, b1), fmaxf(b2, b3));
 }
 
+// Maximum of 16 values (one 32-key block).
+__device__ __forceinline__ float max16(const float (&x)[1][16]) {
+  const float a0 = fmaxf(fmaxf(x[0][0], x[0][1]), x[0][2]), a1 = fmaxf(fmaxf(x[0][3], x[0][4]), x[0][5]);
+  const float a2 = fmaxf(fmaxf(x[0][6], x[0][7]), x[0][8]), a3 = fmaxf(fmaxf(x[0][9], x[0][10]), x[0][11]);
+  const float a4 = fmaxf(fmaxf(x[0][12], x[0][13]), x[0][14]);
+  return fmaxf(fmaxf(fmaxf(a0, a1), a2), fmaxf(fmaxf(a3, a4), x[0][15]));
+}
+__device__ __forceinline__ float max_tile(const float (&x)[2][16]) { return max32(x); }
+__device__ __forceinline__ float max_tile(const float (&x)[1][16]) { return max16(x); }
+
 __device__ __forceinline__ u32x2 tr_read(const uint16_t* p) {
   const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_u16*)p);
   return __builtin_bit_cast(u32x2, r);
 }
 
-template <int D, int NW>
+// BN keys per LDS tile (one barrier and one ring slot each); the softmax
+// and products run on sub-tiles of CB = min(BN, 64) keys (KB blocks of 32),
+// SUB of them per LDS tile.
+template <int D, int NW, int BN_ = kBlockN>
 struct Shape {
-  static constexpr int BN = kBlockN;     // keys per tile
+  static constexpr int BN = BN_;         // keys per LDS tile
+  static constexpr int CB = BN < 64 ? BN : 64;  // keys per compute sub-tile
+  static constexpr int KB = CB / 32;     // 32-key blocks per sub-tile
+  static constexpr int SUB = BN / CB;    // sub-tiles per LDS tile
   static constexpr int NT = 64 * NW;     // threads per workgroup
   static constexpr int DP = D <= 64 ? 64 : 128;  // LDS row length (elements)
   static constexpr int CPR = DP / 8;     // 16-byte chunks per LDS row
   static constexpr int DC = D / 16;      // 16-wide contraction chunks of QK^T
   static constexpr int DB = D / 32;      // 32-row blocks of O^T
   static constexpr int TILE = BN * DP;   // elements per LDS tile buffer
-  static constexpr int LOADS = BN * CPR / NT;  // 16-byte loads per thread per tile
+  static constexpr int CHUNKS = BN * CPR;  // 16-byte chunks per tile operand
+  static constexpr int LOADS = (CHUNKS + NT - 1) / NT;  // 16-byte loads per thread per tile
   static_assert(D % 32 == 0 && D <= 128, "head dim");
-  static_assert((BN * CPR) % NT == 0, "whole wave-loads per tile");
+  static_assert(BN == 32 || BN == 64 || BN == 128, "key tile");
+  static_assert(CHUNKS % 64 == 0, "whole wave-loads per tile");
 };
 
 // LDS tile layouts.  A tile row (one key) is DP elements = CPR chunks of 16
@@ -240,17 +258,19 @@ __device__ __forceinline__ int k_swz(int row) {
 }
 __device__ __forceinline__ int v_swz(int row) { return 2 * (row & 3); }
 
-template <typename T, int D, bool CAUSAL, bool SPLIT_P, int NW, int OCC, int KS>
+template <typename T, int D, bool CAUSAL, bool SPLIT_P, int NW, int OCC, int KS, int BN_>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC)))
 void fa_forward_kernel(Args a) {
-  using S = Shape<D, NW>;
+  using S = Shape<D, NW, BN_>;
   // KS key groups: with KS = 2 the waves form two groups over the same query
   // rows, group g taking key tiles g, g+2, g+4, ... of the range, and their
   // results are merged at the end (for grids that leave CUs idle).
   static_assert(KS == 1 || (KS == 2 && NW % 2 == 0), "key groups");
+  static_assert(KS == 1 || S::BN == 64, "key groups take 64-key tiles");
   constexpr int NWR = NW / KS;  // waves per key group = 32-row blocks per workgroup
   constexpr int BN = S::BN, BM = 32 * NWR, NT = S::NT, DP = S::DP, CPR = S::CPR;
   constexpr int DC = S::DC, DB = S::DB, TILE = S::TILE, LOADS = S::LOADS;
+  constexpr int CB = S::CB, KB = S::KB, SUB = S::SUB;
   // A ring of four LDS slots per operand (tile t in slot t % 4), each slot
   // an array of its own, and the step loop unrolled over the ring: the
   // compiler can then tell the slots apart, so a transpose read of one slot
@@ -322,6 +342,9 @@ void fa_forward_kernel(Args a) {
   // into `splits` ranges (the whole range when splits == 1).
   const int t_lo = split * ntiles / a.splits;
   const int t_hi = (split + 1) * ntiles / a.splits;
+  // the same range in compute sub-tiles of CB keys
+  const int u_lo = t_lo * SUB;
+  const int u_hi = min(t_hi * SUB, (kv_end + CB - 1) / CB);
 
   // Direct global -> LDS loads of the next tile, through a buffer resource
   // whose range starts at the tile's first key and ends at key N, so rows
@@ -337,8 +360,10 @@ void fa_forward_kernel(Args a) {
     const int row = p / CPR, pc = p % CPR;
     koff[i] = (row * ldk + 8 * (pc ^ k_swz<DP>(row))) * 2;
     voff[i] = (row * ldv + 8 * (pc ^ v_swz(row))) * 2;
-    kpred[i] = DP == D || (pc ^ k_swz<DP>(row)) < D / 8;
-    vpred[i] = DP == D || (pc ^ v_swz(row)) < D / 8;
+    // whole waves past the tile (fewer chunks than threads) load nothing
+    const bool in_tile = S::CHUNKS % NT == 0 || p < S::CHUNKS;
+    kpred[i] = in_tile && (DP == D || (pc ^ k_swz<DP>(row)) < D / 8);
+    vpred[i] = in_tile && (DP == D || (pc ^ v_swz(row)) < D / 8);
   }
   // Tiles are loaded once each, in increasing order, so the loads follow a
   // running pointer and byte count (wave-uniform) instead of forming the
@@ -414,13 +439,13 @@ void fa_forward_kernel(Args a) {
   auto k_frag = [&](const uint16_t* kt, int ch, int kb) -> u32x4 {
     return *(const u32x4*)((const char*)kt + k_off[ch] + kb * (32 * DP * 2));
   };
-  auto qk = [&](const uint16_t* kt, f32x16 (&s)[2]) {
-    s[0] = f32x16{};
-    s[1] = f32x16{};
+  auto qk = [&](const uint16_t* kt, f32x16 (&s)[KB]) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16{};
 #pragma unroll
     for (int ch = 0; ch < DC; ++ch)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) s[kb] = Ops<T>::mma(k_frag(kt, ch, kb), qf[ch], s[kb]);
+      for (int kb = 0; kb < KB; ++kb) s[kb] = Ops<T>::mma(k_frag(kt, ch, kb), qf[ch], s[kb]);
   };
 
   // V^T transpose-read source of this lane: within each 16-lane group g,
@@ -433,11 +458,11 @@ void fa_forward_kernel(Args a) {
   const int tr_chunk_lo = (2 * (grp & 1) + ((gl & 3) >> 1)) ^ v_swz(tr_row);
   const int tr_byte = 8 * (gl & 1);
 
-  auto live = [&](int t) {  // tile t is in range and holds keys this wave sees
-    return t < t_hi && (!CAUSAL || t * BN <= q0 + 31);
+  auto live = [&](int u) {  // sub-tile u is in range and holds keys this wave sees
+    return u < u_hi && (!CAUSAL || u * CB <= q0 + 31);
   };
-  auto is_edge = [&](int t) {  // tile t needs the ragged / causal masks
-    return (t * BN + BN > N) || (CAUSAL && (t * BN + BN - 1 > q0));
+  auto is_edge = [&](int u) {  // sub-tile u needs the ragged / causal masks
+    return (u * CB + CB > N) || (CAUSAL && (u * CB + CB - 1 > q0));
   };
 
   // V^T fragment for P V: keys 16*kc .. +15 (in the P key order), head-dim
@@ -487,24 +512,24 @@ void fa_forward_kernel(Args a) {
   // FMAs and the first key block's exponentials (reading K as they go),
   // the check follows, and V is read during P V.
   constexpr bool check_first = D == 64;
-  auto tile_body = [&](const uint16_t* kt_next, const uint16_t* vt, f32x16 (&sc)[2],
-                       f32x16 (&sn)[2], bool first) {
+  auto tile_body = [&](const uint16_t* kt_next, const uint16_t* vt, f32x16 (&sc)[KB],
+                       f32x16 (&sn)[KB], bool first) {
     refresh_offsets();
-    [[maybe_unused]] u32x4 kf[DC][2], vf[4][DB];
+    [[maybe_unused]] u32x4 kf[DC][KB], vf[2 * KB][DB];
     if constexpr (check_first) {
 #pragma unroll
       for (int ch = 0; ch < DC; ++ch)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) kf[ch][kb] = k_frag(kt_next, ch, kb);
+        for (int kb = 0; kb < KB; ++kb) kf[ch][kb] = k_frag(kt_next, ch, kb);
     }
-    float x[2][16];
+    float x[KB][16];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) x[kb][e] = __builtin_fmaf(sc[kb][e], c, -mc);
     if constexpr (!check_first) qk(kt_next, sn);
-    const float xmax = max32(x);
-    float p[2][16];
+    const float xmax = max_tile(x);
+    float p[KB][16];
     if constexpr (!check_first) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -517,12 +542,12 @@ void fa_forward_kernel(Args a) {
       // keeps the compiler from turning this rare path into selects that
       // would run on every tile
       asm volatile("" ::: "memory");
-      float sm[2][16];
+      float sm[KB][16];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) sm[kb][e] = sc[kb][e];
-      const float mx = half_max(max32(sm));  // the row's maximum in this tile
+      const float mx = half_max(max_tile(sm));  // the row's maximum in this tile
       const float m_new = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);  // 0 when m_run = -inf
       m_run = m_new;
@@ -532,7 +557,7 @@ void fa_forward_kernel(Args a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) lp[i] *= alpha;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) x[kb][e] = __builtin_fmaf(sc[kb][e], c, -mc);
       if constexpr (!check_first) {
@@ -542,22 +567,24 @@ void fa_forward_kernel(Args a) {
     }
     if constexpr (check_first) {
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc)
+      for (int kc = 0; kc < 2 * KB; ++kc)
 #pragma unroll
         for (int db = 0; db < DB; ++db) vf[kc][db] = v_frag(vt, kc, db);
-      sn[0] = f32x16{};
-      sn[1] = f32x16{};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) sn[kb] = f32x16{};
 #pragma unroll
       for (int ch = 0; ch < DC; ++ch)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) sn[kb] = Ops<T>::mma(kf[ch][kb], qf[ch], sn[kb]);
+        for (int kb = 0; kb < KB; ++kb) sn[kb] = Ops<T>::mma(kf[ch][kb], qf[ch], sn[kb]);
 #pragma unroll
       for (int e = 0; e < 16; ++e) p[0][e] = __builtin_amdgcn_exp2f(x[0][e]);
     }
 #pragma unroll
-    for (int e = 0; e < 16; ++e) p[1][e] = __builtin_amdgcn_exp2f(x[1][e]);
+    for (int kb = 1; kb < KB; ++kb)
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
+      for (int e = 0; e < 16; ++e) p[kb][e] = __builtin_amdgcn_exp2f(x[kb][e]);
+#pragma unroll
+    for (int kc = 0; kc < 2 * KB; ++kc) {
       // chunk kc (16 keys) = pairs 4*(kc&1) .. +3 of key block kc>>1
       const int kb = kc >> 1, base = 8 * (kc & 1);
       u32x4 pf, pfl;
@@ -584,12 +611,12 @@ void fa_forward_kernel(Args a) {
     }
   };
 
-  // Ragged / causal masks of the scores of tile t.
-  auto mask_scores = [&](int t, f32x16 (&sc)[2]) {
-    if (is_edge(t)) {
-      const int k0 = t * BN;
+  // Ragged / causal masks of the scores of sub-tile u.
+  auto mask_scores = [&](int u, f32x16 (&sc)[KB]) {
+    if (is_edge(u)) {
+      const int k0 = u * CB;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int key = k0 + 32 * kb + 8 * (e >> 2) + 4 * hi + (e & 3);
@@ -602,7 +629,7 @@ void fa_forward_kernel(Args a) {
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
-  f32x16 sA[2], sB[2];
+  f32x16 sA[KB], sB[KB];
   if constexpr (KS == 1) {
     // Software pipeline over the ring.
     if (t_lo < t_hi) {
@@ -617,10 +644,11 @@ void fa_forward_kernel(Args a) {
     // Step t (t % 4 == J): pass the barrier (tile t+1, whose loads went out
     // in step t-1, is then visible, and every wave is done with step t-1);
     // issue the loads of tile t+2 into slot (t+2) % 4, last read in step
-    // t-2; then the tile body: softmax of tile t, whose scores were computed
-    // in step t-1, while the scores of tile t+1 are computed, and P V of
-    // tile t.
-    auto step = [&](int t, auto J, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+    // t-2; then the tile body on each of the tile's SUB sub-tiles: softmax
+    // of the sub-tile, whose scores were computed in the previous body,
+    // while the scores of the next sub-tile (the second half of this tile,
+    // or the first of tile t+1) are computed, and P V of the sub-tile.
+    auto step = [&](int t, auto J, f32x16 (&s0)[KB], f32x16 (&s1)[KB]) {
       constexpr int j = decltype(J)::value;
       using Next = std::integral_constant<int, (j + 1) & 3>;
       using Pre2 = std::integral_constant<int, (j + 2) & 3>;
@@ -629,22 +657,32 @@ void fa_forward_kernel(Args a) {
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile t+1 has landed
       __syncthreads();
       if (t + 2 < t_hi) load_next_tile(kbuf(Pre2{}), vbuf(Pre2{}));
-      if (live(t)) {
-        mask_scores(t, sc);
-        tile_body(kbuf(Next{}), vbuf(J), sc, sn, t == t_lo);
+      const int u = t * SUB;
+      if (live(u)) {
+        mask_scores(u, s0);
+        tile_body(SUB == 1 ? kbuf(Next{}) : kbuf(J) + CB * DP, vbuf(J), s0, s1, u == u_lo);
+      }
+      if constexpr (SUB == 2) {
+        if (live(u + 1)) {
+          mask_scores(u + 1, s1);
+          tile_body(kbuf(Next{}), vbuf(J) + CB * DP, s1, s0, u + 1 == u_lo);
+        }
       }
     };
     // The guards nest so that step t+2 is only reached through step t+1 (and
     // its wait for the loads of step t); with flat guards the compiler sees a
     // path that skips it and makes the transpose reads of step t+2 wait for
-    // those loads.
+    // those loads.  The score registers alternate per sub-tile: with two
+    // sub-tiles per tile every step starts on sA.
+    auto& sC = SUB == 1 ? sB : sA;  // the first score set of odd steps
+    auto& sD = SUB == 1 ? sA : sB;
     for (int t = t_lo; t < t_hi; t += 4) {
       step(t, I0{}, sA, sB);
       if (t + 1 < t_hi) {
-        step(t + 1, I1{}, sB, sA);
+        step(t + 1, I1{}, sC, sD);
         if (t + 2 < t_hi) {
           step(t + 2, I2{}, sA, sB);
-          if (t + 3 < t_hi) step(t + 3, I3{}, sB, sA);
+          if (t + 3 < t_hi) step(t + 3, I3{}, sC, sD);
         }
       }
     }
@@ -787,15 +825,15 @@ void fa_forward_kernel(Args a) {
   }
 }
 
-template <typename T, int D, bool CAUSAL, bool SPLIT_P, int NW, int OCC, int KS = 1>
+template <typename T, int D, bool CAUSAL, bool SPLIT_P, int NW, int OCC, int KS = 1, int BN = kBlockN>
 hipError_t launch_one(const Args& base, int64_t BH, hipStream_t stream) {
-  using S = Shape<D, NW>;
+  using S = Shape<D, NW, BN>;
   constexpr int BM = 32 * NW / KS;
   Args a = base;
   a.num_qtiles = (a.N + BM - 1) / BM;
   a.total_tiles = (int)(BH * a.num_qtiles * a.splits);
   void* args[] = {&a};
-  return hipLaunchKernel((const void*)fa_forward_kernel<T, D, CAUSAL, SPLIT_P, NW, OCC, KS>,
+  return hipLaunchKernel((const void*)fa_forward_kernel<T, D, CAUSAL, SPLIT_P, NW, OCC, KS, BN>,
                          dim3(a.total_tiles), dim3(S::NT), args, 0, stream);
 }
 
@@ -826,8 +864,8 @@ inline Args make_args(const Problem& p) {
   return a;
 }
 
-// Workgroup shape per head dimension and mask: mfma_waves (measured on
-// MI355X).  D = 64 causal runs two workgroups per CU (waves_per_eu 2).  With
+// Workgroup shape per head dimension and mask: mfma_waves and mfma_block_n
+// (measured on MI355X).  D = 64 causal runs two workgroups per CU (waves_per_eu 2).  With
 // two key groups (p.key_groups == 2, chosen by the host for grids that leave
 // CUs idle) the workgroup is p.ks_waves waves: 2 or 4 row blocks x 2 key
 // groups.
@@ -866,8 +904,11 @@ hipError_t launch(const Problem& p, hipStream_t stream) {
       return p.causal ? launch_one<T, 96, true, SPLIT_P, mfma_waves(96, true), 1>(a, p.BH, stream)
                       : launch_one<T, 96, false, SPLIT_P, mfma_waves(96, false), 1>(a, p.BH, stream);
     case 128:
-      return p.causal ? launch_one<T, 128, true, SPLIT_P, mfma_waves(128, true), 1>(a, p.BH, stream)
-                      : launch_one<T, 128, false, SPLIT_P, mfma_waves(128, false), 1>(a, p.BH, stream);
+      return p.causal
+                 ? launch_one<T, 128, true, SPLIT_P, mfma_waves(128, true), 1, 1, mfma_block_n(128, SPLIT_P)>(
+                       a, p.BH, stream)
+                 : launch_one<T, 128, false, SPLIT_P, mfma_waves(128, false), 1, 1, mfma_block_n(128, SPLIT_P)>(
+                       a, p.BH, stream);
     default:
       return hipErrorInvalidValue;
   }
@@ -875,20 +916,22 @@ hipError_t launch(const Problem& p, hipStream_t stream) {
 
 #ifdef FA_TILE_SWEEP
 // Every workgroup shape of the calibration sweep (the tuning library only):
-// (waves per workgroup, waves_per_eu hint, key groups).  Two workgroups per
-// CU need a 64-element LDS row (D = 64) and four waves per workgroup (two
-// waves of two workgroups sit on two SIMDs only); with D = 96 or 128 one
-// workgroup fills the LDS, so those sizes take the one-workgroup shapes only.
-template <typename T, bool SPLIT_P, int D, bool CAUSAL>
-hipError_t launch_shape_d(const Args& a, int64_t BH, int nw, int occ, int ks, hipStream_t s) {
+// (waves per workgroup, waves_per_eu hint, key groups, keys per LDS tile).
+// Two workgroups per CU need a 64-element LDS row (D = 64) and four waves per
+// workgroup (two waves of two workgroups sit on two SIMDs only); with D = 96
+// or 128 one workgroup fills the LDS, so those sizes take the one-workgroup
+// shapes only.  128-key tiles take 128 KiB of LDS at D = 64 (one workgroup
+// per CU) and do not fit at D = 96 or 128; key groups take 64-key tiles.
+template <typename T, bool SPLIT_P, int D, bool CAUSAL, int BN>
+hipError_t launch_shape_bn(const Args& a, int64_t BH, int nw, int occ, int ks, hipStream_t s) {
   if (ks == 1) {
-    if (nw == 2 && occ == 1) return launch_one<T, D, CAUSAL, SPLIT_P, 2, 1>(a, BH, s);
-    if (nw == 4 && occ == 1) return launch_one<T, D, CAUSAL, SPLIT_P, 4, 1>(a, BH, s);
-    if (nw == 8 && occ == 1) return launch_one<T, D, CAUSAL, SPLIT_P, 8, 1>(a, BH, s);
-    if constexpr (D == 64) {
-      if (nw == 4 && occ == 2) return launch_one<T, D, CAUSAL, SPLIT_P, 4, 2>(a, BH, s);
+    if (nw == 2 && occ == 1) return launch_one<T, D, CAUSAL, SPLIT_P, 2, 1, 1, BN>(a, BH, s);
+    if (nw == 4 && occ == 1) return launch_one<T, D, CAUSAL, SPLIT_P, 4, 1, 1, BN>(a, BH, s);
+    if (nw == 8 && occ == 1) return launch_one<T, D, CAUSAL, SPLIT_P, 8, 1, 1, BN>(a, BH, s);
+    if constexpr (D == 64 && BN <= 64) {
+      if (nw == 4 && occ == 2) return launch_one<T, D, CAUSAL, SPLIT_P, 4, 2, 1, BN>(a, BH, s);
     }
-  } else if (ks == 2) {
+  } else if (ks == 2 && BN == 64) {
     if (nw == 4 && occ == 1) return launch_one<T, D, CAUSAL, SPLIT_P, 4, 1, 2>(a, BH, s);
     if (nw == 8 && occ == 1) return launch_one<T, D, CAUSAL, SPLIT_P, 8, 1, 2>(a, BH, s);
     if constexpr (D == 64) {
@@ -898,19 +941,31 @@ hipError_t launch_shape_d(const Args& a, int64_t BH, int nw, int occ, int ks, hi
   return hipErrorInvalidValue;
 }
 
+template <typename T, bool SPLIT_P, int D, bool CAUSAL>
+hipError_t launch_shape_d(const Args& a, int64_t BH, int nw, int occ, int ks, int bn, hipStream_t s) {
+  switch (bn) {
+    case 32: return launch_shape_bn<T, SPLIT_P, D, CAUSAL, 32>(a, BH, nw, occ, ks, s);
+    case 64: return launch_shape_bn<T, SPLIT_P, D, CAUSAL, 64>(a, BH, nw, occ, ks, s);
+    case 128:
+      if constexpr (D == 64) return launch_shape_bn<T, SPLIT_P, D, CAUSAL, 128>(a, BH, nw, occ, ks, s);
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <typename T, bool SPLIT_P>
-hipError_t launch_shape(const Problem& p, int nw, int occ, int ks, hipStream_t s) {
+hipError_t launch_shape(const Problem& p, int nw, int occ, int ks, int bn, hipStream_t s) {
   const Args a = make_args(p);
   switch (p.D) {
     case 64:
-      return p.causal ? launch_shape_d<T, SPLIT_P, 64, true>(a, p.BH, nw, occ, ks, s)
-                      : launch_shape_d<T, SPLIT_P, 64, false>(a, p.BH, nw, occ, ks, s);
+      return p.causal ? launch_shape_d<T, SPLIT_P, 64, true>(a, p.BH, nw, occ, ks, bn, s)
+                      : launch_shape_d<T, SPLIT_P, 64, false>(a, p.BH, nw, occ, ks, bn, s);
     case 96:
-      return p.causal ? launch_shape_d<T, SPLIT_P, 96, true>(a, p.BH, nw, occ, ks, s)
-                      : launch_shape_d<T, SPLIT_P, 96, false>(a, p.BH, nw, occ, ks, s);
+      return p.causal ? launch_shape_d<T, SPLIT_P, 96, true>(a, p.BH, nw, occ, ks, bn, s)
+                      : launch_shape_d<T, SPLIT_P, 96, false>(a, p.BH, nw, occ, ks, bn, s);
     case 128:
-      return p.causal ? launch_shape_d<T, SPLIT_P, 128, true>(a, p.BH, nw, occ, ks, s)
-                      : launch_shape_d<T, SPLIT_P, 128, false>(a, p.BH, nw, occ, ks, s);
+      return p.causal ? launch_shape_d<T, SPLIT_P, 128, true>(a, p.BH, nw, occ, ks, bn, s)
+                      : launch_shape_d<T, SPLIT_P, 128, false>(a, p.BH, nw, occ, ks, bn, s);
     default:
       return hipErrorInvalidValue;
   }

@@ -5,11 +5,11 @@ detail that breaks naive ports: tile calibration", found the best tile size
 to differ between GPUs and asks for it to be measured on each target;
 "Android Transformer Optimization: Attention and Mobile GPU Bottlenecks",
 section "Implementation Recommendations", sizes tiles from the on-chip
-memory.  On MI355X the tile is 32 query rows per wave by 64 keys (the
-32x32 matrix-core tile and the LDS ring); what is left to calibrate is how
-many waves share a workgroup (and so its K/V tiles in LDS), how many
-workgroups share a CU, and whether the waves split the key tiles in two
-groups (for grids that leave CUs idle).  This tool times every shape that the calibration
+memory.  On MI355X a wave owns 32 query rows (the 32x32 matrix-core
+tile); what is calibrated is the number of keys staged in LDS per tile and
+barrier (32, 64 or 128), how many waves share a workgroup (and so its K/V
+tiles in LDS), how many workgroups share a CU, and whether the waves split
+the key tiles in two groups (for grids that leave CUs idle).  This tool times every shape that the calibration
 library (libfa_tune.so) instantiates, for each head dimension, storage
 type and mask, on synthetic inputs drawn by the workload generator, and
 writes a table:
@@ -56,29 +56,30 @@ def load_tune():
         raise ImportError(f"{TUNE_LIB} is not built; run tiled_attention_fa_amd/build.py")
     lib = ctypes.CDLL(TUNE_LIB)
     i64, vp, ip = ctypes.c_int64, ctypes.c_void_p, ctypes.POINTER(ctypes.c_int)
-    lib.fa_tune_shapes.argtypes = [i64, ip, ip, ip, ctypes.c_int]
+    lib.fa_tune_shapes.argtypes = [i64, ip, ip, ip, ip, ctypes.c_int]
     lib.fa_tune_shapes.restype = ctypes.c_int
     lib.fa_tune_forward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float, ctypes.c_int,
-                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
+                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
     lib.fa_tune_forward.restype = ctypes.c_int
+    lib.fa_tune_split_merge.argtypes = [vp, vp, vp, vp, i64, i64, ctypes.c_int, ctypes.c_int, vp]
+    lib.fa_tune_split_merge.restype = ctypes.c_int
     return lib
 
 
 def shapes(lib, D):
-    """(waves, waves_per_eu, key_groups) of every shape the library has for D."""
-    w = (ctypes.c_int * 8)()
-    o = (ctypes.c_int * 8)()
-    g = (ctypes.c_int * 8)()
-    n = lib.fa_tune_shapes(D, w, o, g, 8)
+    """(waves, waves_per_eu, key_groups, keys per LDS tile) of every shape the
+    library has for D."""
+    w, o, g, b = ((ctypes.c_int * 16)() for _ in range(4))
+    n = lib.fa_tune_shapes(D, w, o, g, b, 16)
     if n < 0:
         raise ValueError(f"no shapes for D={D}")
-    return [(w[i], o[i], g[i]) for i in range(n)]
+    return [(w[i], o[i], g[i], b[i]) for i in range(n)]
 
 
-def tune_forward(lib, q, k, v, o, scale, causal, code, waves, occ, key_groups, stream):
+def tune_forward(lib, q, k, v, o, scale, causal, code, waves, occ, key_groups, block_n, stream):
     B, H, N, D = q.shape
     st = lib.fa_tune_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, H, N, D,
-                             float(scale), int(causal), code, waves, occ, key_groups, stream)
+                             float(scale), int(causal), code, waves, occ, key_groups, block_n, stream)
     if st != 0:
         raise RuntimeError(f"fa_tune_forward status {st}")
 
@@ -156,18 +157,23 @@ def main():
                     best[sh] = min(best[sh], timed(lambda: lib.fa_tune_forward(*targs)))
             rec = {"case": w.name, "B": B, "H": H, "N": N, "D": D, "dtype": dt, "causal": causal,
                    "fa_forward_us": round(best_lib, 2), "shapes": []}
-            for waves, occ, ks in variants:
-                tune_forward(lib, q, k, v, out, w.scale, causal, codes[dt], waves, occ, ks, stream.cuda_stream)
+            for waves, occ, ks, bn in variants:
+                tune_forward(lib, q, k, v, out, w.scale, causal, codes[dt], waves, occ, ks, bn,
+                             stream.cuda_stream)
                 torch.cuda.synchronize()
                 diff = float((out.float() - ref.float()).abs().max().item())
-                t = best[(waves, occ, ks)]
+                t = best[(waves, occ, ks, bn)]
                 rec["shapes"].append({"waves": waves, "rows": 32 * waves // ks, "waves_per_eu": occ,
-                                      "key_groups": ks, "us": round(t, 2),
+                                      "key_groups": ks, "block_n": bn, "us": round(t, 2),
                                       "tflops": round(flops / (t * 1e-6) / 1e12, 1),
                                       "max_abs_diff_vs_fa_forward": diff})
             best = min(rec["shapes"], key=lambda s: s["us"])
             rec["best"] = {"waves": best["waves"], "waves_per_eu": best["waves_per_eu"],
-                           "key_groups": best["key_groups"], "us": best["us"]}
+                           "key_groups": best["key_groups"], "block_n": best["block_n"], "us": best["us"]}
+            by_bn = {}
+            for sh in rec["shapes"]:
+                by_bn[sh["block_n"]] = min(by_bn.get(sh["block_n"], float("inf")), sh["us"])
+            rec["best_us_by_block_n"] = by_bn
             rows.append(rec)
             print(json.dumps(rec), flush=True)
             del q, k, v, ref, out
@@ -184,19 +190,27 @@ def main():
                  f"best of {args.rounds} interleaved rounds, after 0.25 s of untimed launches per case; "
                  "every workgroup shape of libfa_tune.so: `Nw` = N waves per workgroup (32 query rows "
                  "each), `occK` = waves_per_eu hint K, `ks2` = the waves in two key groups over half as many "
-                 "rows, alternate key tiles each. `fa_forward` is the shipped library's own choice on the "
-                 "same inputs.", "",
-                 "| case | fa_forward | " + " | ".join(["shape / us"] * 7) + " | best |",
-                 "|---|---|" + "---|" * 7 + "---|"]
+                 "rows, alternate key tiles each, `bnB` = B keys per LDS tile (one barrier each). "
+                 "`fa_forward` is the shipped library's own choice on the same inputs. The first table "
+                 "gives the fastest shape per key-tile size, the second every shape.", "",
+                 "| case | fa_forward | best bn32 | best bn64 | best bn128 | best shape |",
+                 "|---|---|---|---|---|---|"]
 
         def label(s):
-            return f"{s['waves']}w occ{s['waves_per_eu']}" + (" ks2" if s["key_groups"] == 2 else "")
+            return (f"{s['waves']}w occ{s['waves_per_eu']}" + (" ks2" if s["key_groups"] == 2 else "")
+                    + f" bn{s['block_n']}")
 
         for r in rows:
+            bb = r["best_us_by_block_n"]
+            cell = lambda b: str(bb[b]) if b in bb else "-"
+            lines.append(f"| {r['case']} | {r['fa_forward_us']} | {cell(32)} | {cell(64)} | {cell(128)} | "
+                         f"{label(r['best'])} |")
+        nmax = max(len(r["shapes"]) for r in rows)
+        lines += ["", "| case | " + " | ".join(["shape / us"] * nmax) + " |", "|---|" + "---|" * nmax]
+        for r in rows:
             cells = [f"{label(s)}: {s['us']}" for s in r["shapes"]]
-            cells += [""] * (7 - len(cells))
-            lines.append(f"| {r['case']} | {r['fa_forward_us']} | " + " | ".join(cells) +
-                         f" | {label(r['best'])} |")
+            cells += [""] * (nmax - len(cells))
+            lines.append(f"| {r['case']} | " + " | ".join(cells) + " |")
         worst = max(s["max_abs_diff_vs_fa_forward"] for r in rows for s in r["shapes"])
         lines += ["", f"Largest difference of any shape's O from fa_forward's: {worst:.3e}."]
         open(args.out + ".md", "w").write("\n".join(lines) + "\n")
