@@ -63,7 +63,9 @@
 //    issues beside running MFMAs), so the weights applied to V sum to one.
 //    bf16: P is kept as an unevaluated sum of two bf16 numbers (hi + lo)
 //    and two PV products are issued, so P carries ~16 significant bits, as
-//    with fp16; l sums the fp32 p.
+//    with fp16, and l sums the fp32 p; except on tiles where every weight
+//    is small against the row's running sum (below kSplitTau of it), which
+//    take P rounded once to bf16 and add the rounded values to l.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -90,6 +92,9 @@ typedef __attribute__((address_space(3))) uint16_t lds_u16;
 constexpr int kBlockN = 64;  // keys per LDS tile unless the shape says otherwise
 constexpr int kXcds = 8;     // MI355X: 8 accelerator complex dies, one L2 each
 constexpr float kLazy = 8.f;  // log2 of the largest p the lazy maximum allows
+// bf16: a tile whose weights all stay below this share of the row's running
+// denominator is multiplied with P rounded once (see the tile body)
+constexpr float kSplitTau = 0.125f;
 
 struct Args {
   const uint16_t* q;
@@ -583,6 +588,27 @@ void fa_forward_kernel(Args a) {
     for (int kb = 1; kb < KB; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) p[kb][e] = __builtin_amdgcn_exp2f(x[kb][e]);
+    // bf16 keeps 8 significant bits of each weight.  A wave multiplies
+    // with P rounded once when no lane's largest p of this tile exceeds
+    // kSplitTau of that lane's share of the row's running denominator (lanes
+    // 0-31 and 32-63 hold the two halves of each row's keys, so the row's
+    // largest weight then stays below kSplitTau of the row's sum so far);
+    // on a row's first tile (denominator 0), and whenever a few keys carry a
+    // large share of the row, it also multiplies with the rounded remainder
+    // lo = p - hi, so that P carries ~16 significant bits.  xmax may be
+    // stale after a rescale of m, which only overstates p.
+    // (The two-key-group kernels at D = 96 and 128 have no registers to
+    // spare for the branch and always take both products, interleaved.)
+    constexpr bool ADAPT = SPLIT_P && (KS == 1 || D == 64);
+    [[maybe_unused]] bool split = false;
+    if constexpr (ADAPT) {
+      const float lane_l = (lp[0] + lp[1]) + (lp[2] + lp[3]);
+      const float pmax = __builtin_amdgcn_exp2f(xmax);
+      split = __builtin_amdgcn_ballot_w64(!(pmax <= kSplitTau * lane_l)) != 0;
+    }
+    // P V over the chunks of 16 keys, with P rounded once (RNE); the row
+    // sums add the rounded values, so that the weights applied to V sum to
+    // one (this matters when a few keys dominate a row).
 #pragma unroll
     for (int kc = 0; kc < 2 * KB; ++kc) {
       // chunk kc (16 keys) = pairs 4*(kc&1) .. +3 of key block kc>>1
@@ -593,12 +619,13 @@ void fa_forward_kernel(Args a) {
         const float p0 = p[kb][base + 2 * j], p1 = p[kb][base + 2 * j + 1];
         const uint32_t w = Ops<T>::pack(p0, p1);
         pf[j] = w;
-        if constexpr (SPLIT_P) {
-          pfl[j] = Ops<T>::pack(p0 - Ops<T>::lo_to_f32(w), p1 - Ops<T>::hi_to_f32(w));
-          lp[j] += p0 + p1;
+        if constexpr (SPLIT_P && !ADAPT) {
+          const uint32_t wl = Ops<T>::pack(p0 - Ops<T>::lo_to_f32(w), p1 - Ops<T>::hi_to_f32(w));
+          pfl[j] = wl;
+          lp[j] += p0 + p1;  // hi + lo carry p to ~16 significant bits
+        } else if constexpr (SPLIT_P) {
+          lp[j] += Ops<T>::lo_to_f32(w) + Ops<T>::hi_to_f32(w);
         } else {
-          // the sum of the rounded P, so that the weights applied to V sum
-          // to one (this matters when a few keys dominate a row)
           lp[j] = Ops<T>::add_hi(w, Ops<T>::add_lo(w, lp[j]));
         }
       }
@@ -606,7 +633,30 @@ void fa_forward_kernel(Args a) {
       for (int db = 0; db < DB; ++db) {
         const u32x4 v = check_first ? vf[kc][db] : v_frag(vt, kc, db);
         oacc[db] = Ops<T>::mma(v, pf, oacc[db]);
-        if constexpr (SPLIT_P) oacc[db] = Ops<T>::mma(v, pfl, oacc[db]);
+        if constexpr (SPLIT_P && !ADAPT) oacc[db] = Ops<T>::mma(v, pfl, oacc[db]);
+      }
+    }
+    if constexpr (ADAPT) {
+      if (split) {
+        // the rounded remainders, their products and their row sums
+#pragma unroll
+        for (int kc = 0; kc < 2 * KB; ++kc) {
+          const int kb = kc >> 1, base = 8 * (kc & 1);
+          u32x4 pfl;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float p0 = p[kb][base + 2 * j], p1 = p[kb][base + 2 * j + 1];
+            const uint32_t w = Ops<T>::pack(p0, p1);
+            const uint32_t wl = Ops<T>::pack(p0 - Ops<T>::lo_to_f32(w), p1 - Ops<T>::hi_to_f32(w));
+            pfl[j] = wl;
+            lp[j] += Ops<T>::lo_to_f32(wl) + Ops<T>::hi_to_f32(wl);
+          }
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const u32x4 v = check_first ? vf[kc][db] : v_frag(vt, kc, db);
+            oacc[db] = Ops<T>::mma(v, pfl, oacc[db]);
+          }
+        }
       }
     }
   };
