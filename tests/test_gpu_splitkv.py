@@ -53,8 +53,9 @@ def lse_parity(got, ref, dtype, what):
 @pytest.mark.parametrize("causal", [False, True])
 def test_lse_and_splits_sweep(dtype, D, causal):
     """Every split count from 1 (LSE only) to more ranges than key tiles
-    (empty ranges), on ragged lengths."""
-    for i, (N, S) in enumerate([(1, 1), (65, 1), (200, 2), (129, 3), (300, 5), (65, 16), (1000, 4)]):
+    (empty ranges), on ragged lengths and on whole tiles cut unevenly."""
+    for i, (N, S) in enumerate([(1, 1), (65, 1), (200, 2), (129, 3), (300, 5), (65, 16), (1000, 4),
+                                (192, 2), (256, 3)]):
         BH = (1, 1) if i % 2 == 0 else (1, 3)
         w = Workload(f"ex_{dtype}_d{D}_n{N}_s{S}", BH[0], BH[1], N, D, dtype, causal,
                      seed=30_000 + 53 * N + D + 7 * S + (1 if causal else 0))

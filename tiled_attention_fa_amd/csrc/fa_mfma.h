@@ -263,7 +263,10 @@ __device__ __forceinline__ int k_swz(int row) {
 }
 __device__ __forceinline__ int v_swz(int row) { return 2 * (row & 3); }
 
-template <typename T, int D, bool CAUSAL, bool SPLIT_P, int NW, int OCC, int KS, int BN_>
+// FULL: no causal mask and N a multiple of the key tile, so every tile of
+// the loop holds keys for every row and none needs a mask (the host picks
+// this instance when that holds; it skips the per-tile checks).
+template <typename T, int D, bool CAUSAL, bool SPLIT_P, int NW, int OCC, int KS, int BN_, bool FULL>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC)))
 void fa_forward_kernel(Args a) {
   using S = Shape<D, NW, BN_>;
@@ -463,10 +466,15 @@ void fa_forward_kernel(Args a) {
   const int tr_chunk_lo = (2 * (grp & 1) + ((gl & 3) >> 1)) ^ v_swz(tr_row);
   const int tr_byte = 8 * (gl & 1);
 
+  static_assert(!(FULL && CAUSAL), "a causal tile loop has masked tiles");
   auto live = [&](int u) {  // sub-tile u is in range and holds keys this wave sees
+    // one key group: the loop stops at the last tile; two: the second
+    // group's last tile may lie past the range
+    if constexpr (FULL && KS == 1) return true;
     return u < u_hi && (!CAUSAL || u * CB <= q0 + 31);
   };
   auto is_edge = [&](int u) {  // sub-tile u needs the ragged / causal masks
+    if constexpr (FULL) return false;
     return (u * CB + CB > N) || (CAUSAL && (u * CB + CB - 1 > q0));
   };
 
@@ -883,8 +891,10 @@ hipError_t launch_one(const Args& base, int64_t BH, hipStream_t stream) {
   a.num_qtiles = (a.N + BM - 1) / BM;
   a.total_tiles = (int)(BH * a.num_qtiles * a.splits);
   void* args[] = {&a};
-  return hipLaunchKernel((const void*)fa_forward_kernel<T, D, CAUSAL, SPLIT_P, NW, OCC, KS, BN>,
-                         dim3(a.total_tiles), dim3(S::NT), args, 0, stream);
+  const bool full = !CAUSAL && a.N % BN == 0;
+  const void* kernel = full ? (const void*)fa_forward_kernel<T, D, CAUSAL, SPLIT_P, NW, OCC, KS, BN, !CAUSAL>
+                            : (const void*)fa_forward_kernel<T, D, CAUSAL, SPLIT_P, NW, OCC, KS, BN, false>;
+  return hipLaunchKernel(kernel, dim3(a.total_tiles), dim3(S::NT), args, 0, stream);
 }
 
 inline Args make_args(const Problem& p) {
