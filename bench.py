@@ -164,6 +164,16 @@ def naive_leg(w, q, k, v, o, stream, code, lib, steps, tiled_ms):
     ev1.record(stream)
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / steps
+    # the median of individually bracketed calls, as the pages report theirs
+    singles = []
+    for _ in range(max(20, min(steps, 50))):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        e1.synchronize()
+        singles.append(e0.elapsed_time(e1) * 1e3)
     nb = workloads.naive_bytes(w)
     diff = float((on.float() - o.float()).abs().max().item())
     log(f"three-pass: {ms * 1e3:.2f} us per call ({steps} calls), {nb / (ms * 1e-3) / 1e9:.0f} GB/s "
@@ -171,6 +181,8 @@ def naive_leg(w, q, k, v, o, stream, code, lib, steps, tiled_ms):
     return {
         "ms_per_call": round(ms, 5),
         "calls": steps,
+        "median_single_call_us": round(float(np.median(singles)), 3),
+        "single_calls": len(singles),
         "tiled_speedup": round(ms / tiled_ms, 3),
         "algorithmic_bytes": nb,
         "achieved_GBs": round(nb / (ms * 1e-3) / 1e9, 1),
@@ -188,7 +200,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default=workloads.HEADLINE, choices=workloads.ORDER)
+    ap.add_argument("--workload", default=workloads.HEADLINE, choices=workloads.ORDER + workloads.PAGE_TABLE)
     ap.add_argument("--settle-s", type=float, default=0.3,
                     help="seconds of untimed launches before the warm-up steps, so that the "
                          "GPU clock has left its ramp (it takes tens of ms under this load)")

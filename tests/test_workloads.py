@@ -34,9 +34,15 @@ def test_headline_accounting():
 
 
 def test_five_workloads():
-    assert len(CONFIGS) == 5
+    assert len(workloads.ORDER) == 5
+    assert len(CONFIGS) == 5 + len(workloads.PAGE_TABLE)
     for w in CONFIGS.values():
         assert math.isclose(w.scale, 1 / math.sqrt(w.D))
+    # the second page's comparison shapes: 32 heads, D = 128, N = 512 and 1024
+    assert [(workloads.get(n).H, workloads.get(n).D, workloads.get(n).N) for n in workloads.PAGE_TABLE] == \
+        [(32, 128, 512), (32, 128, 1024)]
+    seeds = [w.seed for w in CONFIGS.values()]
+    assert len(set(seeds)) == len(seeds)
 
 
 def test_deterministic_and_distinct_seeds():

@@ -54,8 +54,19 @@ _LIST = [
              uniform_head=True),
 ]
 
-CONFIGS = {w.name: w for w in _LIST}
+# The shapes of the second page's comparison of the tiled pass with naive
+# attention ("Flash Attention on Android: tiled SGEMM with RenderScript",
+# section "Benchmark results: Snapdragon vs. Dimensity": 32 heads, head
+# dimension 128, sequence lengths 512 and 1024), at fp16 storage.  They are
+# benchmark cases for that comparison, not among the five parity workloads.
+_PAGE_TABLE = [
+    Workload("page_table_b1h32n512d128_f16", 1, 32, 512, 128, "f16", False, 1006),
+    Workload("page_table_b1h32n1024d128_f16", 1, 32, 1024, 128, "f16", False, 1007),
+]
+
+CONFIGS = {w.name: w for w in _LIST + _PAGE_TABLE}
 ORDER = [w.name for w in _LIST]
+PAGE_TABLE = [w.name for w in _PAGE_TABLE]
 # The workload the throughput figure is quoted on: 1B-LLM prefill, fp16.
 HEADLINE = "prefill_b1h32n2048d64_f16"
 
