@@ -168,6 +168,12 @@ struct Ops<__bf16> {
   static __device__ __forceinline__ float hi_to_f32(uint32_t w) {
     return __builtin_bit_cast(float, w & 0xffff0000u);
   }
+  // acc + both bf16 halves of w, in fp32: one v_dot2c_f32_bf16 against
+  // (1, 1) (the products are exact) in place of two widenings and two adds.
+  static __device__ __forceinline__ float add_pair(uint32_t w, float acc) {
+    const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
+  }
 };
 
 // Workgroup id -> logical tile id.  Workgroups are dispatched round-robin
@@ -632,7 +638,7 @@ void fa_forward_kernel(Args a) {
           pfl[j] = wl;
           lp[j] += p0 + p1;  // hi + lo carry p to ~16 significant bits
         } else if constexpr (SPLIT_P) {
-          lp[j] += Ops<T>::lo_to_f32(w) + Ops<T>::hi_to_f32(w);
+          lp[j] = Ops<T>::add_pair(w, lp[j]);
         } else {
           lp[j] = Ops<T>::add_hi(w, Ops<T>::add_lo(w, lp[j]));
         }
@@ -657,7 +663,7 @@ void fa_forward_kernel(Args a) {
             const uint32_t w = Ops<T>::pack(p0, p1);
             const uint32_t wl = Ops<T>::pack(p0 - Ops<T>::lo_to_f32(w), p1 - Ops<T>::hi_to_f32(w));
             pfl[j] = wl;
-            lp[j] += Ops<T>::lo_to_f32(wl) + Ops<T>::hi_to_f32(wl);
+            lp[j] = Ops<T>::add_pair(wl, lp[j]);
           }
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
