@@ -29,15 +29,24 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 OUT = os.path.join(ROOT, "profiles")  # where the summaries go (--out-dir)
 
 
-def agg(path, filt="fa_forward_kernel"):
+FORWARD = "fa_forward_"  # the forward kernels: fa_forward_kernel (16-bit) and fa_forward_f32_kernel
+
+
+def is_forward(name, filt=FORWARD):
+    if filt != FORWARD:
+        return filt in name
+    return "fa_forward_kernel" in name or "fa_forward_f32_kernel" in name
+
+
+def agg(path, filt=FORWARD):
     per = collections.defaultdict(list)
     for r in csv.DictReader(open(path)):
-        if filt in r["Kernel_Name"]:
+        if is_forward(r["Kernel_Name"], filt):
             per[r["Counter_Name"]].append(float(r["Counter_Value"]))
     return {k: sum(v) / len(v) for k, v in per.items()}, {k: len(v) for k, v in per.items()}
 
 
-def steady(trace_csv, rec, filt="fa_forward_kernel"):
+def steady(trace_csv, rec, filt=FORWARD):
     """Duration of the timed launches alone, from the per-dispatch kernel
     trace: the forward kernel's dispatches in start order, of which the
     bench's timed launches are the `timed_launches` before the last
@@ -47,7 +56,7 @@ def steady(trace_csv, rec, filt="fa_forward_kernel"):
     win = rec.get("trace_window")
     if not win or not os.path.exists(trace_csv):
         return None
-    rows = [r for r in csv.DictReader(open(trace_csv)) if filt in r["Kernel_Name"]]
+    rows = [r for r in csv.DictReader(open(trace_csv)) if is_forward(r["Kernel_Name"], filt)]
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
     k, after = win["timed_launches"], win["launches_after_timed"]
     timed = rows[len(rows) - after - k:len(rows) - after]
@@ -73,8 +82,8 @@ def steady_md(st):
 def warm(W, G):
     import workloads
     import bench
-    fk, nk = agg(f'{G}/prof_FETCH_SIZE_{W}/run_counter_collection.csv', 'fa_forward_kernel')
-    wk, _ = agg(f'{G}/prof_WRITE_SIZE_{W}/run_counter_collection.csv', 'fa_forward_kernel')
+    fk, nk = agg(f'{G}/prof_FETCH_SIZE_{W}/run_counter_collection.csv')
+    wk, _ = agg(f'{G}/prof_WRITE_SIZE_{W}/run_counter_collection.csv')
     fc, _ = agg(f'{G}/prof_FETCH_SIZE_copy256/run_counter_collection.csv', 'copyBuffer')
     wc, _ = agg(f'{G}/prof_WRITE_SIZE_copy256/run_counter_collection.csv', 'copyBuffer')
     copy_kib = 256 * 1024
@@ -88,7 +97,7 @@ def warm(W, G):
     w = workloads.get(W)
     minb = workloads.min_bytes(w)
     stats = list(csv.DictReader(open(f'{G}/prof_trace_{W}/run_kernel_stats.csv')))
-    kname = [r for r in stats if 'fa_forward_kernel' in r['Name']][0]
+    kname = [r for r in stats if is_forward(r['Name'])][0]
     out = {
         "workload": W, "kernel": kname['Name'], "kernel_source_hash": src_hash,
         "fetch_size_kib_per_dispatch": round(fk['FETCH_SIZE'], 2), "write_size_kib_per_dispatch": round(wk['WRITE_SIZE'], 2),
@@ -105,7 +114,7 @@ def warm(W, G):
     cmd_pmc = f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {G}/prof_FETCH_SIZE_{W} -o run -- python -u bench.py --workload {W} --steps 20 --warmup 5 --no-cpu-baseline --no-check"
     md = f"""# HBM bytes of the forward kernel: {W}
 
-Kernel `{kname['Name']}` (kernel source hash `{src_hash}` over the fp16 kernel's source files with comments removed, as `bench.py` computes it).
+Kernel `{kname['Name']}` (kernel source hash `{src_hash}` over the source files of the workload's kernel with comments removed, as `bench.py` computes it).
 
 Commands (run from the repository root on one MI355X, each pass its own process):
 
@@ -127,8 +136,8 @@ Commands (run from the repository root on one MI355X, each pass its own process)
 | ratio | {(fetch_b+write_b)/minb:.3f} |
 
 The counters measure L2-to-memory traffic, an upper bound on HBM bytes (reads served by the
-Infinity Cache count too).  K and V are re-read by every 128-query workgroup of a head; those
-re-reads are served from the XCD's L2, so the kernel moves about the minimum.
+Infinity Cache count too).  K and V are read by every query block of a head; the re-reads that the
+XCD's L2 serves do not reach these counters, so the ratio shows how much of that re-reading L2 absorbs.
 """
     by = f"\nSummary written by `python -m tiled_attention_fa_amd.profile_report warm --workload {W} --dir {G}`.\n"
     open(f'{P}/fa_forward_{W}_hbm_bytes.md', 'w').write(md + by)
@@ -267,7 +276,7 @@ def trace(W, G, run, suffix, out="", note="", title="", bench_args=""):
     `rocprofv3 --kernel-trace --stats -d G/run`, its output in G/run.log."""
     stats = list(csv.DictReader(open(f"{G}/{run}/run_kernel_stats.csv")))
     rec = json.loads([l for l in open(f"{G}/{run}.log") if l.startswith("{")][-1])
-    fwd = [r for r in stats if "fa_forward_kernel" in r["Name"]][0]
+    fwd = [r for r in stats if is_forward(r["Name"])][0]
     args = bench_args or f"--workload {W} --steps {rec['steps']} --warmup {rec['warmup']} --no-cpu-baseline"
     cmd = f"rocprofv3 --kernel-trace --stats --output-format csv -d {G}/{run} -o run -- python -u bench.py {args}"
     rows = "\n".join(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
@@ -307,7 +316,7 @@ def sq(W, G, pre):
     kname = ""
     for f in sorted(glob.glob(f"{G}/{pre}_*/run_counter_collection.csv")):
         for r in csv.DictReader(open(f)):
-            if "fa_forward_kernel" in r["Kernel_Name"]:
+            if is_forward(r["Kernel_Name"]):
                 vals[r["Counter_Name"]].append(float(r["Counter_Value"]))
                 kname = r["Kernel_Name"]
     m = {k: sum(v) / len(v) for k, v in vals.items()}
@@ -322,31 +331,46 @@ def sq(W, G, pre):
         "D": "SQ_ACTIVE_INST_SCA SQ_LDS_ADDR_CONFLICT SQ_LDS_UNALIGNED_STALL SQ_LDS_CMD_FIFO_FULL SQ_INST_CYCLES_SALU "
              "SQ_ACTIVE_INST_FLAT SQ_INSTS_BRANCH SQ_ACTIVE_INST_VMEM",
     }
+    import workloads
+    w = workloads.get(W)
     waves = m["SQ_WAVES"]
-    simds, tiles = 1024, 32
+    simds = 1024
+    # 64-key tiles per wave, averaged over the waves of the workload's grid:
+    # N / 64 without the mask; with it, a wave of rows q0 .. q0 + 31 sees the
+    # tiles up to its diagonal
+    if w.causal:
+        per_head = [-(-(q0 + 32) // 64) for q0 in range(0, w.N, 32)]
+        tiles = sum(per_head) / len(per_head)
+    else:
+        tiles = -(-w.N // 64)
     life = m["SQ_WAVE_CYCLES"] * 4 / waves
     mfma = m["SQ_VALU_MFMA_BUSY_CYCLES"] / simds
     valu = m["SQ_ACTIVE_INST_VALU"] * 4 / simds
     coex = m["SQ_VALU_MFMA_COEXEC_CYCLES"] / simds
+    span = m["GRBM_GUI_ACTIVE"] / 8
 
     def per_wave_tile(k):
         return m[k] / waves / tiles
 
     lines = [f"# SQ counters of the forward kernel: {W}", "",
-             f"Kernel `{kname}` (8 waves x 32 query rows per workgroup, 256 workgroups, 2048 waves).  Four counter",
+             f"Kernel `{kname}` ({waves:,.0f} waves of 32 query rows, {tiles:.1f} key tiles of 64 per wave on "
+             "average).  Four counter",
              "passes, each its own process (repository root, one MI355X):", ""]
     for k, c in passes.items():
         lines.append(f"    rocprofv3 --pmc {c} --output-format csv -d {G}/{pre}_{k} -o run -- {B}")
     lines += ["", "Mean per dispatch over the ~2000 dispatches of each pass:", "", "| counter | value |", "|---|---|"]
     for k in sorted(m):
         lines.append(f"| `{k}` | {m[k]:,.0f} |")
-    lines += ["", "Derived (MI355X: 256 CUs x 4 SIMDs = 1024 SIMDs, two waves per SIMD; SQ cycle counters in units of 4 "
+    lines += ["", "Derived (MI355X: 256 CUs x 4 SIMDs = 1024 SIMDs; SQ cycle counters in units of 4 "
               "cycles; one", "MFMA 32x32x16 counts 32 busy cycles):", "", "| quantity | value |", "|---|---|",
               f"| wave lifetime (SQ_WAVE_CYCLES x 4 / waves) | {life:,.0f} cycles (~{life / 2.0e3:.1f} us at 2.0 GHz) |",
-              f"| matrix-core busy per SIMD (SQ_VALU_MFMA_BUSY_CYCLES / 1024) | {mfma:,.0f} cycles = "
-              f"{100 * mfma / life:.0f}% |",
-              f"| VALU issue per SIMD, MFMA included (SQ_ACTIVE_INST_VALU x 4 / 1024) | {valu:,.0f} cycles = "
-              f"{100 * valu / life:.0f}% |",
+              f"| dispatch span per XCD (GRBM_GUI_ACTIVE / 8 XCDs) | {span:,.0f} cycles |",
+              f"| waves resident per SIMD, averaged over the span (SQ_WAVE_CYCLES x 4 / 1024 / span) | "
+              f"{m['SQ_WAVE_CYCLES'] * 4 / simds / span:.2f} |",
+              f"| matrix-core busy per SIMD (SQ_VALU_MFMA_BUSY_CYCLES / 1024), against the span | "
+              f"{mfma:,.0f} cycles = {100 * mfma / span:.0f}% |",
+              f"| VALU issue per SIMD, MFMA included (SQ_ACTIVE_INST_VALU x 4 / 1024), against the span | "
+              f"{valu:,.0f} cycles = {100 * valu / span:.0f}% |",
               f"| VALU and MFMA together (SQ_VALU_MFMA_COEXEC_CYCLES / 1024) | {coex:,.0f} cycles = "
               f"{100 * coex / mfma:.0f}% of the MFMA-busy time |",
               f"| VALU instructions per wave per 64-key tile (MFMA included) | {per_wave_tile('SQ_INSTS_VALU'):.0f} "
@@ -355,22 +379,74 @@ def sq(W, G, pre):
               f"| LDS instructions per wave per tile | {per_wave_tile('SQ_INSTS_LDS'):.1f} |",
               f"| scalar instructions per wave per tile | {per_wave_tile('SQ_INSTS_SALU'):.1f} |",
               f"| LDS bank conflicts | {m['SQ_LDS_BANK_CONFLICT']:.0f} cycles |", ""]
-    lines += ["Under counter collection the dispatches are serialised and run slower end to end, but the wave lifetime "
-              "matches", "the ~41 us of the bench, so the per-wave figures describe the kernel as it runs.  "
-              "SQ_ACTIVE_INST_VALU appears to", "count each MFMA for its 32 busy cycles: 16 x 32 plus about 2 cycles "
-              "for each other VALU instruction of a tile gives", "the measured figure within 2%.  The matrix cores are "
-              "busy about 40% of the wave's life; the VALU issues beside them for", "about three fifths of that time; "
-              "the rest is the latency of each wave's chain of dependent steps (LDS reads, the", "lazy-maximum check, "
-              "the exponentials, the 16-bit conversion of P), which two waves per SIMD do not cover.", "",
+    lines += ["Under counter collection the dispatches are serialised, but each wave's lifetime is that of the "
+              "timed kernel,", "so the per-wave figures describe the kernel as it runs.  SQ_ACTIVE_INST_VALU counts "
+              "each MFMA for its busy", "cycles.  Matrix-core busy against the dispatch span is the figure the "
+              "roofline fraction follows.", "",
               f"Summary written by `python -m tiled_attention_fa_amd.profile_report sq --workload {W} --dir {G} "
               f"--run {pre}`.", ""]
     open(os.path.join(OUT, f"fa_forward_{W}_sq_counters.md"), "w").write("\n".join(lines))
 
 
+def pages(G):
+    """The second page's comparison table ("Flash Attention on Android: tiled
+    SGEMM with RenderScript", section "Benchmark results: Snapdragon vs.
+    Dimensity": 32 heads, D = 128, N = 512 and 1024, peak memory bandwidth of a
+    naive pass against the tiled one) on MI355X, from the kernel-trace bench
+    runs of the page-table workloads (G/prof_trace_W.log) and their committed
+    traffic files."""
+    import workloads
+    rows = []
+    for W in workloads.PAGE_TABLE:
+        rec = json.loads([l for l in open(f"{G}/prof_trace_{W}.log") if l.startswith("{")][-1])
+        n = rec["naive_three_pass"]
+        t = json.load(open(os.path.join(OUT, f"traffic_{W}.json")))
+        tn = json.load(open(os.path.join(OUT, f"traffic_naive_{W}.json")))
+        w = workloads.get(W)
+        t_us, n_us = rec["ms_per_step"] * 1e3, n["ms_per_call"] * 1e3
+        tb, nb = t["hbm_bytes_per_launch"], tn["hbm_bytes_per_launch"]
+        rows.append((w, t_us, rec["median_single_launch_us"], n_us, n["median_single_call_us"], tb, nb))
+    lines = ["# Tiled against three-pass attention at the second page's shapes (MI355X)", "",
+             "The page's table compares the peak memory bandwidth of a naive FP32 attention with its tiled pass on two",
+             "phones, 32 heads, head dimension 128, sequence lengths 512 and 1024 (\"Flash Attention on Android: tiled",
+             "SGEMM with RenderScript\", section \"Benchmark results: Snapdragon vs. Dimensity\"; the median of 20",
+             "sustained runs, read and write bytes from the vendors' profiler counters).  Here the same shapes run at fp16",
+             "storage (the three-pass path takes 16-bit storage; its S is fp32 either way and its P takes 2 bytes where",
+             "FP32 would take 4, so these three-pass bytes understate an FP32 baseline's).  Bytes per call are the",
+             "copy-calibrated FETCH_SIZE + WRITE_SIZE counters of each path's kernels; time is the mean of back-to-back",
+             "calls (sustained) and, beside it, the median of individually timed calls (each after a synchronisation,",
+             "so it includes launch latency and a clock that has dropped while idle).", "",
+             "| N | path | bytes per call | of which the n x n matrices | us per call (sustained) | median single call (us) | "
+             "achieved GB/s (sustained) |",
+             "|---|---|---|---|---|---|---|"]
+    for w, t_us, t_med, n_us, n_med, tb, nb in rows:
+        extra = nb - workloads.min_bytes(w)
+        lines.append(f"| {w.N} | tiled (`fa_forward`) | {tb / 1e6:.1f} MB | 0 | {t_us:.2f} | {t_med:.2f} | "
+                     f"{tb / (t_us * 1e-6) / 1e9:,.0f} |")
+        lines.append(f"| {w.N} | three-pass (`fa_naive_forward`) | {nb / 1e6:.1f} MB | {extra / 1e6:.1f} MB | "
+                     f"{n_us:.2f} | {n_med:.2f} | {nb / (n_us * 1e-6) / 1e9:,.0f} |")
+    lines += ["", "| N | bytes: three-pass / tiled | time: three-pass / tiled | bandwidth the tiled pass draws, "
+              "against the three-pass one | the page's reduction (phones) |", "|---|---|---|---|---|"]
+    page = {512: "38.4 -> 23.1 GB/s (-40%), 35.1 -> 21.4 GB/s (-39%)",
+            1024: "61.7 -> 29.6 GB/s (-52%), 57.8 -> 26.0 GB/s (-55%)"}
+    for w, t_us, t_med, n_us, n_med, tb, nb in rows:
+        bw_t, bw_n = tb / (t_us * 1e-6), nb / (n_us * 1e-6)
+        lines.append(f"| {w.N} | {nb / tb:.1f}x | {n_us / t_us:.2f}x | {100 * (1 - bw_t / bw_n):.0f}% lower | "
+                     f"{page.get(w.N, '-')} |")
+    lines += ["", "On the phones the two passes take similar times and the page reports the drop in bandwidth.  Here the",
+              "tiled pass also finishes several times sooner, so its bandwidth drop understates what it saves: the",
+              "bytes fall by the ratio in the second column.  The per-path summaries and counters are in",
+              "`fa_forward_<workload>_hbm_bytes.md` and `fa_naive_<workload>_hbm_bytes.md`.", "",
+              f"Written by `python -m tiled_attention_fa_amd.profile_report pages --dir {G}` from the runs those "
+              "summaries list.", ""]
+    open(os.path.join(OUT, "page_table_comparison_mi355x.md"), "w").write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def main():
     global OUT
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("kind", choices=["warm", "cold", "trace", "sq"])
+    ap.add_argument("kind", choices=["warm", "cold", "trace", "sq", "pages"])
     ap.add_argument("--workload", default="prefill_b1h32n2048d64_f16")
     ap.add_argument("--dir", required=True, help="the directory the rocprofv3 runs wrote to")
     ap.add_argument("--run", default="", help="trace: the run's rocprofv3 -d name under --dir")
@@ -384,7 +460,9 @@ def main():
     OUT = args.out_dir
     sys.path.insert(0, ROOT)
     G = args.dir.rstrip("/")
-    if args.kind == "trace":
+    if args.kind == "pages":
+        pages(G)
+    elif args.kind == "trace":
         trace(args.workload, G, args.run or f"prof_trace_{args.workload}", args.suffix, args.out, args.note, args.title,
               args.bench_args)
     elif args.kind == "sq":
