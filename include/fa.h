@@ -226,7 +226,8 @@ int fa_splitkv_suggest(int64_t B, int64_t H, int64_t N, int64_t D, int dtype, in
  *     the CU count, or at most half of it for D = 64 and 128; or
  *   - causal: B*H times the one-group kernel's query blocks (256 rows; 128
  *     for D = 64 and 96) fill at most three quarters of the device's
- *     workgroup slots (one per CU; two for D = 64);
+ *     workgroup slots (one per CU; two for D = 64), except bf16 at D = 96
+ *     and 128 between one half and three quarters;
  * else 1.  With 2 the waves of a workgroup (64 query rows, or 128 on the
  * fuller of those grids) form two groups that take alternate key tiles,
  * and their running maxima, denominators and accumulators are merged in
@@ -237,6 +238,23 @@ int fa_splitkv_suggest(int64_t B, int64_t H, int64_t N, int64_t D, int dtype, in
  * FA_ERR_DEVICE when no device is current).
  */
 int fa_key_groups_suggest(int64_t B, int64_t H, int64_t N, int64_t D, int dtype, int causal);
+
+/*
+ * fa_workgroup_shape -- the workgroup shape fa_forward (and fa_forward_ex
+ * with one key range, and fa_forward_strided) launches on the current
+ * device for these sizes, for dtype FA_F16 or FA_BF16: *waves wave64s per
+ * workgroup, *key_groups (1 or 2, as fa_key_groups_suggest) and *block_n
+ * keys per LDS tile (32 or 64), the tile loop of "Android Transformer
+ * Optimization: Attention and Mobile GPU Bottlenecks", section "A Complete
+ * Tile Loop", sized as "Flash Attention on Android: tiled SGEMM with
+ * RenderScript", section "The detail that breaks naive ports: tile
+ * calibration", asks (measured per device).  Each wave owns 32 query rows of
+ * its group.  Any output pointer may be NULL.  Host only; returns FA_OK or
+ * FA_ERR_DTYPE, FA_ERR_DIM, FA_ERR_UNSUPPORTED_D, FA_ERR_TOO_LARGE,
+ * FA_ERR_DEVICE.
+ */
+int fa_workgroup_shape(int64_t B, int64_t H, int64_t N, int64_t D, int dtype, int causal, int* waves,
+                       int* key_groups, int* block_n);
 
 /*
  * The three-pass ("naive") attention that tiling is measured against:

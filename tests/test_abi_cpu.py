@@ -267,6 +267,16 @@ def test_key_groups_suggest_without_device(lib):
     assert fa.STATUS_NAMES[fa.fa_key_groups_suggest(0, 8, 1000, 64, 1, False)] == "FA_ERR_DIM"
 
 
+def test_workgroup_shape_without_device(lib):
+    got = fa.fa_workgroup_shape(1, 8, 1000, 96, 1, False)
+    if isinstance(got, tuple):
+        pytest.skip("a device is present")
+    assert fa.STATUS_NAMES[got] == "FA_ERR_DEVICE"
+    assert fa.STATUS_NAMES[fa.fa_workgroup_shape(1, 8, 1000, 80, 1, False)] == "FA_ERR_UNSUPPORTED_D"
+    assert fa.STATUS_NAMES[fa.fa_workgroup_shape(1, 8, 1000, 64, 0, False)] == "FA_ERR_DTYPE"
+    assert fa.STATUS_NAMES[fa.fa_workgroup_shape(1, 0, 1000, 64, 2, True)] == "FA_ERR_DIM"
+
+
 # ------------------------------------------------------ fa_forward_strided
 
 DENSE = (4 * 64 * 64, 64 * 64, 64)          # [B, H=4, N=64, D=64]

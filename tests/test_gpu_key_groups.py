@@ -130,8 +130,10 @@ def test_one_group_same_problems(dtype, D, causal):
 @pytest.mark.parametrize("D", [64, 96, 128])
 def test_two_groups_causal_partial_grids(dtype, D):
     """Causal grids between half and three quarters of the slots run two
-    groups (8-wave workgroups at D = 96 and 128); non-causal ones of the same
-    size run one.  Three heads of each are checked against the oracle."""
+    groups (8-wave workgroups at D = 96 and 128), except bf16 at D = 96 and
+    128, which runs one group there (2 waves with 32-key tiles at D = 128);
+    non-causal ones of the same size run one.  Three heads of each are
+    checked against the oracle."""
     cus, _ = fa.fa_device_info()
     block, per_cu = {64: (128, 2), 96: (128, 1), 128: (256, 1)}[D]
     N = 2048
@@ -139,10 +141,11 @@ def test_two_groups_causal_partial_grids(dtype, D):
     slots = cus * per_cu
     H = (5 * slots // 8) // blocks  # ~5/8 of the slots
     assert 2 * H * blocks > slots and 4 * H * blocks <= 3 * slots
-    assert groups(1, H, N, D, dtype, True) == 2
+    want = 1 if (dtype == "bf16" and D != 64) else 2
+    assert groups(1, H, N, D, dtype, True) == want
     assert groups(1, H, N, D, dtype, False) == 1
     w = Workload(f"kgp_{dtype}_d{D}", 1, H, N, D, dtype, True, seed=73_000 + D)
-    _say(f"[key groups 2, partial causal grid] {w.name} H={H}")
+    _say(f"[key groups {want}, partial causal grid] {w.name} H={H}")
     x = make_inputs(w)
     q, k, v = (to_device(x[n], dtype) for n in "qkv")
     o = fa.forward(q, k, v, scale=w.scale, causal=True)

@@ -30,6 +30,7 @@ from ._lib import (  # noqa: F401
     fa_splitkv_suggest,
     fa_status_string,
     fa_version,
+    fa_workgroup_shape,
     forward,
     forward_ex,
     library_path,

@@ -31,7 +31,7 @@ STATUS_NAMES = {
 EXPORTS = ("fa_device_info", "fa_forward", "fa_forward_ex", "fa_forward_ex_noalloc",
            "fa_forward_ex_workspace_bytes",
            "fa_forward_strided", "fa_key_groups_suggest", "fa_naive_forward", "fa_naive_workspace_bytes",
-           "fa_splitkv_suggest", "fa_status_string", "fa_version")
+           "fa_splitkv_suggest", "fa_status_string", "fa_version", "fa_workgroup_shape")
 
 _lib = None
 
@@ -76,6 +76,9 @@ def load_library():
     lib.fa_splitkv_suggest.restype = ctypes.c_int
     lib.fa_key_groups_suggest.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
     lib.fa_key_groups_suggest.restype = ctypes.c_int
+    ip = ctypes.POINTER(ctypes.c_int)
+    lib.fa_workgroup_shape.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int, ip, ip, ip]
+    lib.fa_workgroup_shape.restype = ctypes.c_int
     lib.fa_naive_forward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float, ctypes.c_int,
                                      ctypes.c_int, vp, i64, vp]
     lib.fa_naive_forward.restype = ctypes.c_int
@@ -168,6 +171,17 @@ def fa_key_groups_suggest(B: int, H: int, N: int, D: int, dtype: int, causal: bo
     current device, or a negative status."""
     return int(load_library().fa_key_groups_suggest(int(B), int(H), int(N), int(D), int(dtype),
                                                     int(bool(causal))))
+
+
+def fa_workgroup_shape(B: int, H: int, N: int, D: int, dtype: int, causal: bool):
+    """(waves, key_groups, block_n) of the 16-bit forward kernel for these
+    sizes on the current device, or a negative status (an int)."""
+    w, g, bn = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
+    st = int(load_library().fa_workgroup_shape(int(B), int(H), int(N), int(D), int(dtype), int(bool(causal)),
+                                               ctypes.byref(w), ctypes.byref(g), ctypes.byref(bn)))
+    if st != 0:
+        return st
+    return (w.value, g.value, bn.value)
 
 
 def fa_naive_workspace_bytes(B: int, H: int, N: int, dtype: int) -> int:

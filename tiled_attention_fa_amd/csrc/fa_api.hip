@@ -201,7 +201,9 @@ int suggest_splits(int64_t BH, int64_t N, int64_t D, int dtype, bool causal, int
 //  * Causal, with the one-group grid's fill of the device's workgroup
 //    slots: up to one half, 4-wave workgroups; up to three quarters, where
 //    the rows that see every key set the time, 4 waves at D = 64 and 8 at
-//    D = 96 and 128 (2-29% faster); fuller grids run one group.
+//    D = 96 and 128 (2-29% faster), except bf16 at D = 96 and 128, which
+//    runs one group in that band too (its two-group kernels always form the
+//    two-term P; one group runs 6-17% faster); fuller grids run one group.
 int suggest_key_groups(int64_t BH, int64_t N, int64_t D, int dtype, bool causal, int cus, int* ks_waves) {
   *ks_waves = fa::mfma_ks_waves;
   if (dtype == FA_F32 || N <= 64) return 1;
@@ -219,10 +221,40 @@ int suggest_key_groups(int64_t BH, int64_t N, int64_t D, int dtype, bool causal,
   const int64_t slots = (int64_t)cus * fa::mfma_wgs_per_cu((int)D, causal);
   if (2 * total <= slots) return 2;
   if (4 * total <= 3 * slots) {
+    if (dtype == FA_BF16 && D != 64) return 1;
     if (D != 64) *ks_waves = 8;
     return 2;
   }
   return 1;
+}
+
+// The one-group shape for bf16 causal grids (measured on MI355X, where it
+// differs from the table): at D = 128, 2 waves (64 rows) with 32-key tiles
+// where the 8-wave grid fills at most three quarters of the workgroup slots
+// (16-17% faster) and 4 waves with 32-key tiles above (1-5%); at D = 64,
+// 32-key tiles on grids of two or more passes over the slots (3%).  fp16
+// keeps the table's shape.  Sets *waves1 and *block_n1 (0 = the table's).
+void one_group_shape(int64_t BH, int64_t N, int64_t D, int dtype, bool causal, int cus, int* waves1,
+                     int* block_n1) {
+  *waves1 = 0;
+  *block_n1 = 0;
+  if (dtype != FA_BF16 || !causal || N <= 64) return;
+  const int64_t block_m = 32 * fa::mfma_waves((int)D, causal);
+  const int64_t total = BH * ((N + block_m - 1) / block_m);
+  const int64_t slots = (int64_t)cus * fa::mfma_wgs_per_cu((int)D, causal);
+  if (D == 128) {
+    *waves1 = 4 * total <= 3 * slots ? 2 : 4;
+    *block_n1 = 32;
+  } else if (D == 64 && total >= 2 * slots) {
+    *block_n1 = 32;
+  }
+}
+
+// Key groups and workgroup shape of a forward problem with one key range.
+void choose_shape(fa::Problem& p, int dtype, int cus) {
+  const bool causal = p.causal;
+  p.key_groups = suggest_key_groups(p.BH, p.N, p.D, dtype, causal, cus, &p.ks_waves);
+  if (p.key_groups == 1) one_group_shape(p.BH, p.N, p.D, dtype, causal, cus, &p.waves1, &p.block_n1);
 }
 
 // Workspace of split-KV: the fp32 partials [splits, BH, N, D], then their
@@ -256,7 +288,7 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, int64_t B, 
   if (cus < 0) return cus;
 
   fa::Problem p = dense_problem(q, k, v, o, H, BH, N, D, scale, causal);
-  p.key_groups = suggest_key_groups(BH, N, D, dtype, causal != 0, cus, &p.ks_waves);
+  choose_shape(p, dtype, cus);
   return launch_forward(p, dtype, (hipStream_t)stream);
 }
 
@@ -330,6 +362,32 @@ int fa_key_groups_suggest(int64_t B, int64_t H, int64_t N, int64_t D, int dtype,
   return suggest_key_groups(B * H, N, D, dtype, causal != 0, cus, &waves);
 }
 
+int fa_workgroup_shape(int64_t B, int64_t H, int64_t N, int64_t D, int dtype, int causal, int* waves,
+                       int* key_groups, int* block_n) {
+  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (B < 1 || H < 1 || N < 0 || D < 1) return FA_ERR_DIM;
+  if (!head_dim_supported(D)) return FA_ERR_UNSUPPORTED_D;
+  if (B > ((int64_t)1 << 31) / H) return FA_ERR_TOO_LARGE;
+  const int cus = current_cus();
+  if (cus < 0) return cus;
+  fa::Problem p{};
+  p.BH = B * H;
+  p.N = (int)std::min<int64_t>(N, INT32_MAX);
+  p.D = (int)D;
+  p.causal = causal != 0;
+  choose_shape(p, dtype, cus);
+  int w = p.ks_waves, g = 2, bn = 64;
+  if (p.key_groups == 1) {
+    g = 1;
+    w = p.waves1 ? p.waves1 : fa::mfma_waves(p.D, p.causal);
+    bn = p.block_n1 ? p.block_n1 : fa::mfma_block_n(p.D, dtype == FA_BF16);
+  }
+  if (waves) *waves = w;
+  if (key_groups) *key_groups = g;
+  if (block_n) *block_n = bn;
+  return FA_OK;
+}
+
 int64_t fa_forward_ex_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int dtype, int causal,
                                       int num_splits) {
   if (num_splits < 0 || num_splits > kMaxSplits) return FA_ERR_SPLITS;
@@ -397,7 +455,7 @@ int fa_forward_ex(const void* q, const void* k, const void* v, void* o, float* l
   if (splits == 1) {
     const int cus = current_cus();
     if (cus < 0) return cus;
-    p.key_groups = suggest_key_groups(BH, N, D, dtype, causal != 0, cus, &p.ks_waves);
+    choose_shape(p, dtype, cus);
   }
   if (splits > 1) {
     p.part_o = (float*)workspace;
@@ -471,7 +529,7 @@ int fa_forward_strided(const void* q, const int64_t* q_strides, const void* k, c
 
   fa::Problem p = dense_problem(q, k, v, o, H, BH, N, D, scale, causal);
   p.group = (int)(H / H_kv);
-  p.key_groups = suggest_key_groups(BH, N, D, dtype, causal != 0, cus, &p.ks_waves);
+  choose_shape(p, dtype, cus);
   fa::Layout* lay[4] = {&p.lq, &p.lk, &p.lv, &p.lo};
   for (int t = 0; t < 4; ++t) *lay[t] = fa::Layout{st[t][0], st[t][1], (int)st[t][2]};
   return launch_forward(p, dtype, (hipStream_t)stream);

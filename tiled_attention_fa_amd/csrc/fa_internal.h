@@ -48,6 +48,12 @@ struct Problem {
   // workgroup's wave count (4, or 8 for D = 96 and 128).
   int key_groups = 1;
   int ks_waves = 4;
+  // One key group and one key range: the host may replace the table's
+  // workgroup shape (mfma_waves, mfma_block_n) for bf16 causal grids with
+  // waves1 waves (2 or 4) and block_n1 keys per LDS tile (32); 0 keeps the
+  // table's choice.
+  int waves1 = 0;
+  int block_n1 = 0;
 };
 
 // Merge of split-KV partials: O = sum_s exp(lse_s - lse) O_s with

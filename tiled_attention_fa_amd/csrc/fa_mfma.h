@@ -934,7 +934,9 @@ inline Args make_args(const Problem& p) {
 // (measured on MI355X).  D = 64 causal runs two workgroups per CU (waves_per_eu 2).  With
 // two key groups (p.key_groups == 2, chosen by the host for grids that leave
 // CUs idle) the workgroup is p.ks_waves waves: 2 or 4 row blocks x 2 key
-// groups.
+// groups.  For bf16 causal grids the host may name another one-group shape
+// (p.waves1, p.block_n1): 32-key tiles at D = 64, or 2 or 4 waves with
+// 32-key tiles at D = 128.
 template <typename T, bool SPLIT_P>
 hipError_t launch(const Problem& p, hipStream_t stream) {
   const Args a = make_args(p);
@@ -962,6 +964,16 @@ hipError_t launch(const Problem& p, hipStream_t stream) {
         return hipErrorInvalidValue;
     }
   }
+  // the host's bf16 causal shapes (p.waves1, p.block_n1)
+  if constexpr (SPLIT_P) {
+    if (p.causal && p.block_n1 == 32) {
+      if (p.D == 64 && p.waves1 == 0) return launch_one<T, 64, true, SPLIT_P, 4, 2, 1, 32>(a, p.BH, stream);
+      if (p.D == 128 && p.waves1 == 2) return launch_one<T, 128, true, SPLIT_P, 2, 1, 1, 32>(a, p.BH, stream);
+      if (p.D == 128 && p.waves1 == 4) return launch_one<T, 128, true, SPLIT_P, 4, 1, 1, 32>(a, p.BH, stream);
+      return hipErrorInvalidValue;
+    }
+  }
+  if (p.waves1 != 0 || p.block_n1 != 0) return hipErrorInvalidValue;
   switch (p.D) {
     case 64:
       return p.causal ? launch_one<T, 64, true, SPLIT_P, mfma_waves(64, true), 2>(a, p.BH, stream)

@@ -90,7 +90,10 @@ def main():
     ap.add_argument("--launches", type=int, default=40)
     ap.add_argument("--rounds", type=int, default=3,
                     help="interleaved rounds over fa_forward and the shapes; the best round counts")
+    ap.add_argument("--only", default="",
+                    help="comma-separated substrings: sweep only the cases whose name contains one")
     args = ap.parse_args()
+    only = [x for x in args.only.split(",") if x]
 
     sys.path.insert(0, ROOT)
     import numpy as np
@@ -123,6 +126,8 @@ def main():
         for dt in DTYPES:
             w = workloads.Workload(f"sweep_b{B}h{H}n{N}d{D}_{dt}{'_causal' if causal else ''}", B, H, N, D, dt,
                                    causal, seed=50_000 + N + D)
+            if only and not any(o in w.name for o in only):
+                continue
             x = workloads.make_inputs(w)
             q, k, v = (torch.from_numpy(np.ascontiguousarray(x[n]).view(np.int16)).view(tdt[dt]).to(dev)
                        for n in "qkv")
