@@ -611,9 +611,10 @@ void fa_forward_kernel(Args a) {
     // large share of the row, it also multiplies with the rounded remainder
     // lo = p - hi, so that P carries ~16 significant bits.  xmax may be
     // stale after a rescale of m, which only overstates p.
-    // (The two-key-group kernels at D = 96 and 128 have no registers to
-    // spare for the branch and always take both products, interleaved.)
-    constexpr bool ADAPT = SPLIT_P && (KS == 1 || D == 64);
+    // (The eight-wave two-key-group kernels at D = 96 and 128 have no
+    // registers to spare for the branch and always take both products,
+    // interleaved; with four waves, one per SIMD, they have.)
+    constexpr bool ADAPT = SPLIT_P && (KS == 1 || D == 64 || NW == 4);
     [[maybe_unused]] bool split = false;
     if constexpr (ADAPT) {
       const float lane_l = (lp[0] + lp[1]) + (lp[2] + lp[3]);
