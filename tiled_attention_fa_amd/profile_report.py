@@ -391,6 +391,59 @@ def sq(W, G, pre):
     open(os.path.join(OUT, f"fa_forward_{W}_sq_counters.md"), "w").write("\n".join(lines))
 
 
+def requests(G, names):
+    """HBM request counts by size (TCC_EA0_RDREQ / _32B, TCC_BUBBLE; TCC_EA0_WRREQ / _64B; the DRAM-bound
+    ones) for the forward kernel of each workload and for the 256 MiB copy, from three counter passes each
+    (G/req1_<name> .. G/req3_<name>), written to profiles/hbm_request_sizes_mi355x.md."""
+    import workloads
+    passes = ["TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_32B_sum TCC_BUBBLE_sum", "TCC_EA0_WRREQ_sum TCC_EA0_WRREQ_64B_sum",
+              "TCC_EA0_RDREQ_DRAM_sum TCC_EA0_WRREQ_DRAM_sum"]
+    rows = []
+    for name in names + ["copy256"]:
+        vals = collections.defaultdict(list)
+        for i in (1, 2, 3):
+            for r in csv.DictReader(open(f"{G}/req{i}_{name}/run_counter_collection.csv")):
+                kn = r["Kernel_Name"]
+                if (name == "copy256" and "copyBuffer" in kn) or (name != "copy256" and is_forward(kn)):
+                    vals[r["Counter_Name"]].append(float(r["Counter_Value"]))
+        # the copy: its largest dispatch is the 256 MiB copy itself
+        m = {k: (max(v) if name == "copy256" else sum(v) / len(v)) for k, v in vals.items()}
+        if name == "copy256":
+            rmin, wmin = 256 << 20, 256 << 20
+        else:
+            w = workloads.get(name)
+            wmin = w.B * w.H * w.N * w.D * workloads.storage_itemsize(w.dtype)
+            rmin = 3 * wmin
+        rows.append((name, m, rmin, wmin))
+    lines = ["# HBM requests by size on MI355X", "",
+             "`FETCH_SIZE` on this ROCm is (TCC_BUBBLE x 128 + (TCC_EA0_RDREQ - TCC_BUBBLE - TCC_EA0_RDREQ_32B) x 64 +",
+             "TCC_EA0_RDREQ_32B x 32) / 1024 and `WRITE_SIZE` ((TCC_EA0_WRREQ - TCC_EA0_WRREQ_64B) x 32 + TCC_EA0_WRREQ_64B x 64)",
+             "/ 1024 (`rocprofv3 --list-avail`).  The request counters themselves, per dispatch (the workloads: mean over",
+             "the dispatches of their forward kernel; the copy: its 256 MiB dispatch), three passes each, each its own process:",
+             ""]
+    for i, P in enumerate(passes, 1):
+        lines.append(f"    rocprofv3 --pmc {P} --output-format csv -d {G}/req{i}_<name> -o run -- <bench command>")
+    lines += ["", "with `<bench command>` = `python -u bench.py --workload <name> --steps 20 --warmup 5 --no-cpu-baseline "
+              "--no-check --no-naive`, or `python -u bench.py --copy-calibration-mib 256 --steps 10 --warmup 2` for the copy.",
+              "", "| dispatch | RDREQ | RDREQ_32B | BUBBLE (128 B) | RDREQ x 128 B | reads, minimum | WRREQ | WRREQ_64B | "
+              "WRREQ_64B x 64 B | writes, minimum | RDREQ_DRAM / RDREQ |", "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for name, m, rmin, wmin in rows:
+        rd, r32, bub = m["TCC_EA0_RDREQ_sum"], m["TCC_EA0_RDREQ_32B_sum"], m["TCC_BUBBLE_sum"]
+        wr, w64, rdd = m["TCC_EA0_WRREQ_sum"], m["TCC_EA0_WRREQ_64B_sum"], m["TCC_EA0_RDREQ_DRAM_sum"]
+        lines.append(f"| `{name}` | {rd:,.0f} | {r32:,.0f} | {bub:,.0f} | {rd * 128:,.0f} ({rd * 128 / rmin:.4f}x) | "
+                     f"{rmin:,} | {wr:,.0f} | {w64:,.0f} | {w64 * 64:,.0f} ({w64 * 64 / wmin:.4f}x) | {wmin:,} | "
+                     f"{rdd / rd:.4f} |")
+    lines += ["", "Every read request is 128 bytes: no 32-byte requests, and the copy's read requests times 128 B are its",
+              "256 MiB exactly, while TCC_BUBBLE, which the expression relies on to count the 128-byte requests, reads 0.",
+              "So `FETCH_SIZE` counts each 128-byte request as 64 bytes, and the factor 2 that the copy calibration applies to",
+              "it is that request size.  Every write request is 64 bytes and `WRITE_SIZE` needs no factor.  The DRAM-bound",
+              "counter equals the total on every kernel, so it does not separate Infinity Cache hits from DRAM reads.", "",
+              f"Summary written by `python -m tiled_attention_fa_amd.profile_report requests --dir {G} --workload "
+              f"{','.join(names)}`.", ""]
+    open(os.path.join(OUT, "hbm_request_sizes_mi355x.md"), "w").write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def pages(G):
     """The second page's comparison table ("Flash Attention on Android: tiled
     SGEMM with RenderScript", section "Benchmark results: Snapdragon vs.
@@ -449,7 +502,7 @@ def pages(G):
 def main():
     global OUT
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("kind", choices=["warm", "cold", "trace", "sq", "pages"])
+    ap.add_argument("kind", choices=["warm", "cold", "trace", "sq", "pages", "requests"])
     ap.add_argument("--workload", default="prefill_b1h32n2048d64_f16")
     ap.add_argument("--dir", required=True, help="the directory the rocprofv3 runs wrote to")
     ap.add_argument("--run", default="", help="trace: the run's rocprofv3 -d name under --dir")
@@ -470,6 +523,8 @@ def main():
               args.bench_args)
     elif args.kind == "sq":
         sq(args.workload, G, args.run or "pmc")
+    elif args.kind == "requests":
+        requests(G, args.workload.split(","))
     else:
         (warm if args.kind == "warm" else cold)(args.workload, G)
 
