@@ -8,8 +8,9 @@
  * calibration" (the best size differs between devices and has to be
  * measured on each).  This library is built from the same kernel
  * sources as libfa.so, with every workgroup shape of the calibration sweep
- * instantiated (32 query rows per wave; 32-, 64- or 128-key tiles; one or
- * two key groups), so that a sweep can time each shape on the device.  libfa.so
+ * instantiated (matrix-core kernel: 32 query rows per wave; 32-, 64- or
+ * 128-key tiles; one or two key groups; fp32 kernel: 2, 4 or 8 waves over
+ * 64 query rows), so that a sweep can time each shape on the device.  libfa.so
  * itself launches the shape its table names and is not changed by loading
  * this library.
  *
@@ -51,6 +52,26 @@ int fa_tune_shapes(int64_t D, int* waves, int* occupancy, int* key_groups, int* 
 int fa_tune_forward(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H,
                     int64_t N, int64_t D, float scale, int causal, int dtype, int waves,
                     int occupancy, int key_groups, int block_n, void* stream);
+
+/*
+ * fa_tune_f32_shapes -- the workgroup shapes of the fp32 (vector) kernel
+ * the sweep covers for head dimension D: writes up to `capacity` wave
+ * counts into waves[] (may be NULL) and returns how many there are (3 for
+ * D = 64: 2, 4, 8; 2 for D = 96 and 128: 2, 4), or FA_ERR_UNSUPPORTED_D.  A
+ * workgroup owns 64 query rows, one per lane of each wave; its key tiles
+ * (16 keys) are dealt round-robin to the waves, which merge their partial
+ * results at the end.  Host only.
+ */
+int fa_tune_f32_shapes(int64_t D, int* waves, int capacity);
+
+/*
+ * fa_tune_forward_f32 -- fa_forward with dtype FA_F32 (same arguments
+ * otherwise, same checks and status codes, dense [B, H, N, D]) on the fp32
+ * kernel with `waves` waves per workgroup.  A count that fa_tune_f32_shapes
+ * does not list for D returns FA_ERR_UNSUPPORTED_D.  One kernel on `stream`.
+ */
+int fa_tune_forward_f32(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H,
+                        int64_t N, int64_t D, float scale, int causal, int waves, void* stream);
 
 /*
  * fa_tune_split_merge -- the merge kernel of fa_forward_ex's split-KV path

@@ -334,7 +334,8 @@ def test_tune_library_exports_its_header():
     lib = tile_sweep.load_tune()
     text = re.sub(r"/\*.*?\*/", "", open(TUNE_HEADER).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(fa_\w+)\s*\(", text)))
-    assert names == ["fa_tune_forward", "fa_tune_shapes", "fa_tune_split_merge"]
+    assert names == ["fa_tune_f32_shapes", "fa_tune_forward", "fa_tune_forward_f32", "fa_tune_shapes",
+                     "fa_tune_split_merge"]
     out = subprocess.run(["nm", "-D", "--defined-only", tile_sweep.TUNE_LIB], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (fa_\w+)", out))
@@ -349,6 +350,10 @@ def test_tune_library_exports_its_header():
     assert tile_sweep.shapes(lib, 96) == wide
     assert tile_sweep.shapes(lib, 128) == wide
     assert lib.fa_tune_shapes(80, None, None, None, None, 0) == -3
+    assert tile_sweep.f32_shapes(lib, 64) == [2, 4, 8]
+    assert tile_sweep.f32_shapes(lib, 96) == [2, 4]
+    assert tile_sweep.f32_shapes(lib, 128) == [2, 4]
+    assert lib.fa_tune_f32_shapes(80, None, 0) == -3
 
 
 @pytest.mark.parametrize("args,status", [
@@ -369,6 +374,30 @@ def test_tune_split_merge_validation(args, status):
     kw.update(args)
     got = lib.fa_tune_split_merge(kw["po"] or None, kw["pl"] or None, kw["o"] or None, kw["lse"] or None,
                                   kw["rows"], kw["D"], kw["S"], kw["dtype"], None)
+    if status == "FA_ERR_DEVICE" and got == 0:
+        pytest.skip("a gfx950 device is present; the no-device path is not reachable")
+    assert fa.STATUS_NAMES[got] == status
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(B=0), "FA_ERR_DIM"),
+    (dict(D=80), "FA_ERR_UNSUPPORTED_D"),
+    (dict(waves=3), "FA_ERR_UNSUPPORTED_D"),
+    (dict(D=128, waves=8), "FA_ERR_UNSUPPORTED_D"),
+    (dict(D=96, waves=8), "FA_ERR_UNSUPPORTED_D"),
+    (dict(q=0), "FA_ERR_NULL"),
+    (dict(o=A), "FA_ERR_ALIAS"),
+    (dict(N=0, q=0, k=0, v=0, o=0), "FA_OK"),
+    (dict(), "FA_ERR_DEVICE"),
+    (dict(D=128, waves=2), "FA_ERR_DEVICE"),
+])
+def test_tune_forward_f32_validation(args, status):
+    from tiled_attention_fa_amd import tile_sweep
+    lib = tile_sweep.load_tune()
+    kw = dict(q=A, k=B_, v=C, o=O, B=1, H=1, N=64, D=64, waves=8)
+    kw.update(args)
+    got = lib.fa_tune_forward_f32(kw["q"] or None, kw["k"] or None, kw["v"] or None, kw["o"] or None, kw["B"],
+                                  kw["H"], kw["N"], kw["D"], 0.125, 0, kw["waves"], None)
     if status == "FA_ERR_DEVICE" and got == 0:
         pytest.skip("a gfx950 device is present; the no-device path is not reachable")
     assert fa.STATUS_NAMES[got] == status

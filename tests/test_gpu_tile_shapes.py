@@ -1,9 +1,9 @@
 """GPU parity of every workgroup shape of the tile-calibration library
-(libfa_tune.so, include/fa_tune.h) against the fp64 oracle: the sweep may
-only choose among shapes that compute the same attention.  Ragged lengths
-(a partial last tile of every key-tile size, and a 128-key tile whose second
-half holds no key), both masks, all head dimensions, fp16 and bf16, through
-the C ABI."""
+(libfa_tune.so, include/fa_tune.h), the matrix-core kernel's and the fp32
+kernel's, against the fp64 oracle: the sweep may only choose among shapes
+that compute the same attention.  Ragged lengths (a partial last tile of
+every key-tile size, and a 128-key tile whose second half holds no key),
+both masks, all head dimensions, fp16, bf16 and fp32, through the C ABI."""
 
 import numpy as np
 import pytest
@@ -75,3 +75,22 @@ def test_split_merge_closed_forms(tune, dtype):
     gl = lse.double().cpu().numpy()
     assert gl[3] == ninf and np.all(got[3] == 0.0)
     assert np.abs(gl[:3] - expect_lse[:3]).max() <= 2e-6
+
+
+@pytest.mark.parametrize("D", [64, 96, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_every_f32_shape_matches_oracle(tune, D, causal):
+    """The fp32 kernel at every wave count of the sweep: ragged lengths (a
+    partial last 16-key tile, fewer tiles than waves), both masks."""
+    for N, BH in ((200, (1, 2)), (129, (2, 1)), (1, (1, 1)), (40, (1, 1))):
+        w = Workload(f"shape_f32_d{D}_n{N}", BH[0], BH[1], N, D, "f32", causal,
+                     seed=61_000 + N + D + (1 if causal else 0))
+        x = make_inputs(w)
+        ref = oracle.forward(x["q"], x["k"], x["v"], "f32", w.scale, causal)
+        q, k, v = (to_device(x[n], "f32") for n in "qkv")
+        for waves in tile_sweep.f32_shapes(tune, D):
+            print(f"[shape] {w.name} causal={causal} fp32 waves={waves}", flush=True)
+            o = torch.empty_like(q)
+            tile_sweep.tune_forward_f32(tune, q, k, v, o, w.scale, causal, waves, 0)
+            torch.cuda.synchronize()
+            parity(to_numpy64(o), ref, "f32", f"{w.name} causal={causal} fp32 {waves} waves")

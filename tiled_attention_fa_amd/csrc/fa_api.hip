@@ -576,6 +576,34 @@ int fa_tune_forward(const void* q, const void* k, const void* v, void* o, int64_
   return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+int fa_tune_f32_shapes(int64_t D, int* waves, int capacity) {
+  if (!head_dim_supported(D)) return FA_ERR_UNSUPPORTED_D;
+  const int* s = D == 64 ? fa::kTuneF32Waves64 : fa::kTuneF32WavesWide;
+  const int n = D == 64 ? (int)(sizeof(fa::kTuneF32Waves64) / sizeof(int))
+                        : (int)(sizeof(fa::kTuneF32WavesWide) / sizeof(int));
+  for (int i = 0; i < n && i < capacity; ++i)
+    if (waves) waves[i] = s[i];
+  return n;
+}
+
+int fa_tune_forward_f32(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H, int64_t N,
+                        int64_t D, float scale, int causal, int waves, void* stream) {
+  int sw[8];
+  const int n = fa_tune_f32_shapes(D, sw, 8);
+  bool known = false;
+  for (int i = 0; i < n; ++i) known = known || sw[i] == waves;
+  int64_t BH = 0;
+  const int st = validate(q, k, v, o, B, H, N, D, scale, FA_F32, fa::kF32BlockM, &BH);
+  if (st == 1) return FA_OK;
+  if (st != FA_OK) return st;
+  if (!known) return FA_ERR_UNSUPPORTED_D;
+  const int dev = check_device();
+  if (dev != FA_OK) return dev;
+  fa::Problem p = dense_problem(q, k, v, o, H, BH, N, D, scale, causal);
+  const hipError_t err = fa::launch_f32_shape(p, waves, (hipStream_t)stream);
+  return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 /* The split-KV merge alone, on caller-made partials (for its closed-form
  * checks): part_o [splits, rows, D] fp32 and part_lse [splits, rows] fp32 in,
  * o [rows, D] in the storage type and, if not NULL, lse [rows] out. */

@@ -67,10 +67,11 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kBlockM * waves_for<D>()) void fa_forward_f32_kernel(Args a) {
+template <int D, bool CAUSAL, int W = waves_for<D>()>
+__global__ __launch_bounds__(kBlockM * W) void fa_forward_f32_kernel(Args a) {
   constexpr int BN = kBlockN;
-  constexpr int kWaves = waves_for<D>();
+  constexpr int kWaves = W;
+  static_assert((D / W) % 4 == 0, "each wave merges whole 16-byte column groups");
   static_assert(D % 16 == 0 && D <= 128, "head dim");
   // Per wave: a K tile and a V tile; after the loop the same memory holds
   // the waves' accumulators (64 rows x D) for the merge.
@@ -272,7 +273,8 @@ __global__ __launch_bounds__(kBlockM * waves_for<D>()) void fa_forward_f32_kerne
 
 }  // namespace f32k
 
-hipError_t launch_f32(const Problem& p, hipStream_t stream) {
+namespace {
+f32k::Args f32_args(const Problem& p) {
   using namespace f32k;
   Args a;
   a.q = (const float*)p.q;
@@ -294,6 +296,13 @@ hipError_t launch_f32(const Problem& p, hipStream_t stream) {
   a.part_o = p.part_o;
   a.part_lse = p.part_lse;
   a.lse = p.lse;
+  return a;
+}
+}  // namespace
+
+hipError_t launch_f32(const Problem& p, hipStream_t stream) {
+  using namespace f32k;
+  Args a = f32_args(p);
   void (*kern)(Args) = nullptr;
   int waves = 0;
   if (p.D == 64) {
@@ -312,5 +321,29 @@ hipError_t launch_f32(const Problem& p, hipStream_t stream) {
   void* args[] = {&a};
   return hipLaunchKernel((const void*)kern, dim3(a.total_tiles), dim3(kBlockM * waves), args, 0, stream);
 }
+
+#ifdef FA_TILE_SWEEP
+// The fp32 kernel with the wave count given (the tuning library only): 2, 4
+// or 8 waves at D = 64 (8 fill 128 KiB of LDS), 2 or 4 at D = 96 and 128.
+hipError_t launch_f32_shape(const Problem& p, int waves, hipStream_t stream) {
+  using namespace f32k;
+  Args a = f32_args(p);
+  void (*kern)(Args) = nullptr;
+  if (p.D == 64) {
+    if (waves == 2) kern = p.causal ? fa_forward_f32_kernel<64, true, 2> : fa_forward_f32_kernel<64, false, 2>;
+    if (waves == 4) kern = p.causal ? fa_forward_f32_kernel<64, true, 4> : fa_forward_f32_kernel<64, false, 4>;
+    if (waves == 8) kern = p.causal ? fa_forward_f32_kernel<64, true, 8> : fa_forward_f32_kernel<64, false, 8>;
+  } else if (p.D == 96) {
+    if (waves == 2) kern = p.causal ? fa_forward_f32_kernel<96, true, 2> : fa_forward_f32_kernel<96, false, 2>;
+    if (waves == 4) kern = p.causal ? fa_forward_f32_kernel<96, true, 4> : fa_forward_f32_kernel<96, false, 4>;
+  } else if (p.D == 128) {
+    if (waves == 2) kern = p.causal ? fa_forward_f32_kernel<128, true, 2> : fa_forward_f32_kernel<128, false, 2>;
+    if (waves == 4) kern = p.causal ? fa_forward_f32_kernel<128, true, 4> : fa_forward_f32_kernel<128, false, 4>;
+  }
+  if (!kern) return hipErrorInvalidValue;
+  void* args[] = {&a};
+  return hipLaunchKernel((const void*)kern, dim3(a.total_tiles), dim3(kBlockM * waves), args, 0, stream);
+}
+#endif
 
 }  // namespace fa

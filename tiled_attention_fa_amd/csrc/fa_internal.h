@@ -139,6 +139,11 @@ hipError_t launch_mfma_shape_f16(const Problem& p, int waves, int occupancy, int
                                   hipStream_t stream);
 hipError_t launch_mfma_shape_bf16(const Problem& p, int waves, int occupancy, int key_groups, int block_n,
                                    hipStream_t stream);
+// The fp32 kernel's shapes: waves per workgroup (64 query rows, the key
+// tiles dealt round-robin to the waves).
+constexpr int kTuneF32Waves64[] = {2, 4, 8};
+constexpr int kTuneF32WavesWide[] = {2, 4};
+hipError_t launch_f32_shape(const Problem& p, int waves, hipStream_t stream);
 #endif
 hipError_t launch_naive_f16(const NaiveProblem& p, hipStream_t stream);
 hipError_t launch_naive_bf16(const NaiveProblem& p, hipStream_t stream);

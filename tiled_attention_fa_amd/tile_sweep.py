@@ -49,6 +49,12 @@ CASES = [
     (1, 14, 4096, 128, True),
 ]
 DTYPES = ("f16", "bf16")
+# fp32 (vector kernel): the single-head workload, longer rows at each D, and
+# a grid of several workgroups per CU
+F32_CASES = [
+    (1, 1, 128, 64, False), (1, 8, 1024, 64, False), (1, 32, 2048, 64, True),
+    (1, 2, 512, 128, False), (2, 8, 1000, 96, False), (1, 16, 1024, 128, True),
+]
 
 
 def load_tune():
@@ -63,6 +69,11 @@ def load_tune():
     lib.fa_tune_forward.restype = ctypes.c_int
     lib.fa_tune_split_merge.argtypes = [vp, vp, vp, vp, i64, i64, ctypes.c_int, ctypes.c_int, vp]
     lib.fa_tune_split_merge.restype = ctypes.c_int
+    lib.fa_tune_f32_shapes.argtypes = [i64, ip, ctypes.c_int]
+    lib.fa_tune_f32_shapes.restype = ctypes.c_int
+    lib.fa_tune_forward_f32.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float, ctypes.c_int,
+                                        ctypes.c_int, vp]
+    lib.fa_tune_forward_f32.restype = ctypes.c_int
     return lib
 
 
@@ -74,6 +85,23 @@ def shapes(lib, D):
     if n < 0:
         raise ValueError(f"no shapes for D={D}")
     return [(w[i], o[i], g[i], b[i]) for i in range(n)]
+
+
+def f32_shapes(lib, D):
+    """Waves per workgroup of every fp32-kernel shape the library has for D."""
+    w = (ctypes.c_int * 8)()
+    n = lib.fa_tune_f32_shapes(D, w, 8)
+    if n < 0:
+        raise ValueError(f"no fp32 shapes for D={D}")
+    return [w[i] for i in range(n)]
+
+
+def tune_forward_f32(lib, q, k, v, o, scale, causal, waves, stream):
+    B, H, N, D = q.shape
+    st = lib.fa_tune_forward_f32(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, H, N, D,
+                                 float(scale), int(causal), waves, stream)
+    if st != 0:
+        raise RuntimeError(f"fa_tune_forward_f32 status {st}")
 
 
 def tune_forward(lib, q, k, v, o, scale, causal, code, waves, occ, key_groups, block_n, stream):
@@ -183,12 +211,57 @@ def main():
             print(json.dumps(rec), flush=True)
             del q, k, v, ref, out
 
+    rows32 = []
+    for B, H, N, D, causal in F32_CASES:
+        w = workloads.Workload(f"sweep_b{B}h{H}n{N}d{D}_f32{'_causal' if causal else ''}", B, H, N, D, "f32",
+                               causal, seed=52_000 + N + D)
+        if only and not any(o in w.name for o in only):
+            continue
+        x = workloads.make_inputs(w)
+        q, k, v = (torch.from_numpy(np.ascontiguousarray(x[n]).view(np.float32)).to(dev) for n in "qkv")
+        ref = torch.empty_like(q)
+        out = torch.empty_like(q)
+        lib_fa = fa.load_library()
+        base = (q.data_ptr(), k.data_ptr(), v.data_ptr())
+        fwd_args = base + (ref.data_ptr(), B, H, N, D, float(w.scale), int(causal), fa.FA_F32, stream.cuda_stream)
+
+        def call32():
+            if lib_fa.fa_forward(*fwd_args) != 0:
+                raise RuntimeError("fa_forward failed")
+
+        t0 = time.time()
+        while time.time() - t0 < 0.25:
+            call32()
+        torch.cuda.synchronize()
+        variants = f32_shapes(lib, D)
+        best_lib = float("inf")
+        best = {wv: float("inf") for wv in variants}
+        for _ in range(args.rounds):
+            best_lib = min(best_lib, timed(call32))
+            for wv in variants:
+                targs = base + (out.data_ptr(), B, H, N, D, float(w.scale), int(causal), wv, stream.cuda_stream)
+                best[wv] = min(best[wv], timed(lambda: lib.fa_tune_forward_f32(*targs)))
+        flops = workloads.flops(w)
+        rec = {"case": w.name, "B": B, "H": H, "N": N, "D": D, "dtype": "f32", "causal": causal,
+               "fa_forward_us": round(best_lib, 2), "shapes": []}
+        for wv in variants:
+            tune_forward_f32(lib, q, k, v, out, w.scale, causal, wv, stream.cuda_stream)
+            torch.cuda.synchronize()
+            diff = float((out - ref).abs().max().item())
+            rec["shapes"].append({"waves": wv, "rows": 64, "us": round(best[wv], 2),
+                                  "tflops": round(flops / (best[wv] * 1e-6) / 1e12, 3),
+                                  "max_abs_diff_vs_fa_forward": diff})
+        rec["best"] = min(rec["shapes"], key=lambda s: s["us"])
+        rows32.append(rec)
+        print(json.dumps(rec), flush=True)
+        del q, k, v, ref, out
+
     if args.out:
         prop = torch.cuda.get_device_properties(dev)
         meta = {"device": prop.name, "arch": getattr(prop, "gcnArchName", ""), "cus": prop.multi_processor_count,
                 "launches_per_timing": args.launches,
                 "command": "python -m tiled_attention_fa_amd.tile_sweep --out " + args.out}
-        json.dump({"meta": meta, "cases": rows}, open(args.out + ".json", "w"), indent=1)
+        json.dump({"meta": meta, "cases": rows, "f32_cases": rows32}, open(args.out + ".json", "w"), indent=1)
         lines = [f"# Tile calibration sweep ({meta['arch']}, {meta['cus']} CUs)", "",
                  f"Command (repository root): `{meta['command']}`", "",
                  f"Mean microseconds per launch over {args.launches} back-to-back launches (HIP events), "
@@ -210,14 +283,26 @@ def main():
             cell = lambda b: str(bb[b]) if b in bb else "-"
             lines.append(f"| {r['case']} | {r['fa_forward_us']} | {cell(32)} | {cell(64)} | {cell(128)} | "
                          f"{label(r['best'])} |")
-        nmax = max(len(r["shapes"]) for r in rows)
-        lines += ["", "| case | " + " | ".join(["shape / us"] * nmax) + " |", "|---|" + "---|" * nmax]
+        nmax = max([len(r["shapes"]) for r in rows] or [0])
+        if rows:
+            lines += ["", "| case | " + " | ".join(["shape / us"] * nmax) + " |", "|---|" + "---|" * nmax]
         for r in rows:
             cells = [f"{label(s)}: {s['us']}" for s in r["shapes"]]
             cells += [""] * (nmax - len(cells))
             lines.append(f"| {r['case']} | " + " | ".join(cells) + " |")
-        worst = max(s["max_abs_diff_vs_fa_forward"] for r in rows for s in r["shapes"])
-        lines += ["", f"Largest difference of any shape's O from fa_forward's: {worst:.3e}."]
+        worst = max([s["max_abs_diff_vs_fa_forward"] for r in rows for s in r["shapes"]] or [0.0])
+        lines += ["", f"Largest difference of any 16-bit shape's O from fa_forward's: {worst:.3e}."]
+        if rows32:
+            lines += ["", "fp32 (vector kernel: 64 query rows per workgroup, 16-key tiles dealt round-robin to the "
+                      "waves, merged at the end), microseconds per launch:", "",
+                      "| case | fa_forward | 2 waves | 4 waves | 8 waves | best |", "|---|---|---|---|---|---|"]
+            for r in rows32:
+                by = {s["waves"]: s["us"] for s in r["shapes"]}
+                cell = lambda wv: str(by[wv]) if wv in by else "-"
+                lines.append(f"| {r['case']} | {r['fa_forward_us']} | {cell(2)} | {cell(4)} | {cell(8)} | "
+                             f"{r['best']['waves']} waves |")
+            w32 = max(s["max_abs_diff_vs_fa_forward"] for r in rows32 for s in r["shapes"])
+            lines += ["", f"Largest difference of any fp32 shape's O from fa_forward's: {w32:.3e}."]
         open(args.out + ".md", "w").write("\n".join(lines) + "\n")
 
 
