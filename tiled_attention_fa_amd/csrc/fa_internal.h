@@ -80,9 +80,10 @@ struct MergeProblem {
 // CU).
 constexpr int mfma_waves(int D, bool causal) { return D == 96 || (D == 64 && causal) ? 4 : 8; }
 // Keys per LDS tile of the one-group kernel, from the same sweep over 32, 64
-// and 128: 64, except bf16 at D = 128 (split P), where 32-key tiles are 0.2-2%
-// faster (the 64-key build of that kernel needs a few more registers than it
-// has and spills them).  128-key tiles were never the fastest.
+// and 128: 64, except bf16 at D = 128 (split P), where the 64-key build of
+// the kernel needs a few more registers than it has.  128-key tiles come
+// within 1% at best.  (For bf16 causal grids the host names 32-key tiles in
+// more cases: Problem::block_n1.)
 constexpr int mfma_block_n(int D, bool split_p) { return D == 128 && split_p ? 32 : 64; }
 constexpr int mfma_wgs_per_cu(int D, bool causal) { return D == 64 && causal ? 2 : 1; }
 // With two key groups: 4 waves (2 row blocks of 32 x 2 groups, 64 rows per
