@@ -85,3 +85,28 @@ def test_shape_query_matches_key_groups_noncausal():
                 waves = 4 if D == 96 else 8
                 bn = 32 if (D == 128 and dtype == "bf16") else 64
                 assert s == (waves, 1, bn), (B, H, N, D, dtype, s)
+
+
+@pytest.mark.parametrize("B,H,N,D,H_kv", [(1, 12, 4096, 128, 4), (1, 16, 4096, 128, 8), (4, 32, 2048, 64, 8)])
+def test_bf16_causal_shapes_strided_grouped(B, H, N, D, H_kv):
+    """The bf16 causal shapes above through fa_forward_strided: Q and O as
+    [B, N, H, D], K and V with H_kv heads in rows padded by 8 elements.
+    Sampled rows against the oracle on the expanded K/V heads."""
+    from gpu_helpers import bits_to, empty_out, expand, make_gqa_inputs
+    got_shape = fa.fa_workgroup_shape(B, H, N, D, fa.FA_BF16, True)
+    w = Workload(f"shape_strided_b{B}h{H}kv{H_kv}n{N}d{D}_bf16", B, H, N, D, "bf16", True, seed=82_000 + H + D)
+    _say(f"[shape strided] {w.name} shape={got_shape}")
+    q_bits, k_bits, v_bits = make_gqa_inputs(w, H_kv)
+    q = bits_to(q_bits, "bf16", "bnhd")
+    k = bits_to(k_bits, "bf16", "pad", pad=8)
+    v = bits_to(v_bits, "bf16", "pad", pad=8)
+    o = empty_out(B, H, N, D, "bf16", "bnhd")
+    fa.fa_forward_strided(q, k, v, o, scale=w.scale, causal=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(H + D)
+    bh, ri = sample_rows(N, B * H, rng, n=32)
+    group = H // H_kv
+    ref = oracle.rows(q_bits, expand(k_bits, group), expand(v_bits, group), "bf16", w.scale, True, bh, ri)
+    got = to_numpy64(o.contiguous()).reshape(B * H, N, D)[bh, ri]
+    e = parity(got, ref, "bf16", w.name)
+    _say(f"[shape strided] {w.name}: {len(ri)} rows, max abs err {e['max_abs']:.3e}")
