@@ -220,20 +220,23 @@ int fa_splitkv_suggest(int64_t B, int64_t H, int64_t N, int64_t D, int dtype, in
 /*
  * fa_key_groups_suggest -- how many key groups the workgroups of fa_forward,
  * fa_forward_strided and fa_forward_ex (with one key range) use on the
- * current device for these sizes: 2 when dtype is FA_F16 or FA_BF16, N > 64
- * and either
+ * current device for these sizes, when dtype is FA_F16 or FA_BF16 and
+ * N > 64:
  *   - non-causal: B*H times the blocks of 256 rows is at most a quarter of
- *     the CU count, or at most half of it for D = 64 and 128; or
+ *     the CU count (4 at D = 96 and 128, else 2), or at most half of it for
+ *     D = 64 and 128 (2); or
  *   - causal: B*H times the one-group kernel's query blocks (256 rows; 128
- *     for D = 64 and 96) fill at most three quarters of the device's
- *     workgroup slots (one per CU; two for D = 64), except bf16 at D = 96
- *     and 128 between one half and three quarters;
+ *     for D = 64 and 96) fill at most half of the device's workgroup slots
+ *     (one per CU; two for D = 64; 4 at D = 96 and 128, else 2), or at most
+ *     three quarters (2), except bf16 at D = 96 and 128 in that last band;
  * else 1.  With 2 the waves of a workgroup (64 query rows, or 128 on the
- * fuller of those grids) form two groups that take alternate key tiles,
- * and their running maxima, denominators and accumulators are merged in
- * LDS by the rescaling rule of the online softmax ("Android Transformer
- * Optimization: Attention and Mobile GPU Bottlenecks", section "A Complete
- * Tile Loop").  Host only; returns 1, 2 or a negative fa_status
+ * fuller of those grids) form two groups that take alternate key tiles;
+ * with 4, eight waves over 64 query rows form four groups that take every
+ * fourth 32-key tile.  The groups' running maxima, denominators and
+ * accumulators are merged in LDS by the rescaling rule of the online
+ * softmax ("Android Transformer Optimization: Attention and Mobile GPU
+ * Bottlenecks", section "A Complete Tile Loop").  Host only; returns 1, 2,
+ * 4 or a negative fa_status
  * (FA_ERR_DTYPE, FA_ERR_DIM, FA_ERR_UNSUPPORTED_D, FA_ERR_TOO_LARGE,
  * FA_ERR_DEVICE when no device is current).
  */
@@ -243,7 +246,7 @@ int fa_key_groups_suggest(int64_t B, int64_t H, int64_t N, int64_t D, int dtype,
  * fa_workgroup_shape -- the workgroup shape fa_forward (and fa_forward_ex
  * with one key range, and fa_forward_strided) launches on the current
  * device for these sizes, for dtype FA_F16 or FA_BF16: *waves wave64s per
- * workgroup, *key_groups (1 or 2, as fa_key_groups_suggest) and *block_n
+ * workgroup, *key_groups (1, 2 or 4, as fa_key_groups_suggest) and *block_n
  * keys per LDS tile (32 or 64), the tile loop of "Android Transformer
  * Optimization: Attention and Mobile GPU Bottlenecks", section "A Complete
  * Tile Loop", sized as "Flash Attention on Android: tiled SGEMM with

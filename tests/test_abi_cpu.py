@@ -344,9 +344,9 @@ def test_tune_library_exports_its_header():
     assert tile_sweep.shapes(lib, 64) == [
         (2, 1, 1, 64), (4, 1, 1, 64), (4, 2, 1, 64), (8, 1, 1, 64), (4, 1, 2, 64), (4, 2, 2, 64), (8, 1, 2, 64),
         (2, 1, 1, 32), (4, 1, 1, 32), (4, 2, 1, 32), (8, 1, 1, 32), (2, 1, 1, 128), (4, 1, 1, 128),
-        (8, 1, 1, 128)]
+        (8, 1, 1, 128), (8, 1, 4, 32)]
     wide = [(2, 1, 1, 64), (4, 1, 1, 64), (8, 1, 1, 64), (4, 1, 2, 64), (8, 1, 2, 64), (2, 1, 1, 32),
-            (4, 1, 1, 32), (8, 1, 1, 32)]
+            (4, 1, 1, 32), (8, 1, 1, 32), (8, 1, 4, 32)]
     assert tile_sweep.shapes(lib, 96) == wide
     assert tile_sweep.shapes(lib, 128) == wide
     assert lib.fa_tune_shapes(80, None, None, None, None, 0) == -3
@@ -415,6 +415,8 @@ def test_tune_forward_f32_validation(args, status):
     (dict(bn=128, occ=2), "FA_ERR_UNSUPPORTED_D"),
     (dict(D=128, waves=8, occ=1, bn=128), "FA_ERR_UNSUPPORTED_D"),
     (dict(waves=4, occ=1, ks=2, bn=32), "FA_ERR_UNSUPPORTED_D"),
+    (dict(waves=8, occ=1, ks=4, bn=64), "FA_ERR_UNSUPPORTED_D"),
+    (dict(waves=4, occ=1, ks=4, bn=32), "FA_ERR_UNSUPPORTED_D"),
     (dict(o=A), "FA_ERR_ALIAS"),
     (dict(), "FA_ERR_DEVICE"),
     (dict(waves=8, occ=1, bn=128), "FA_ERR_DEVICE"),

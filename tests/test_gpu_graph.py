@@ -3,9 +3,10 @@ fa_forward_ex with split-KV (ranges + merge), fa_forward_strided and
 fa_naive_forward (three kernels) are captured into one torch CUDA graph,
 replayed several times with new inputs copied in and eager work between the
 replays, and every replay must equal the eager result bit for bit (same
-kernels, same inputs).  Four heads run the two-key-group kernel, 256 heads
-the one-group kernel.  None of the entry points records a memset or an
-allocation, so capture is safe; a launch-bound loop can replay the graph."""
+kernels, same inputs).  Four heads run the two-key-group kernel (four groups
+at D = 128), 256 heads the one-group kernel.  None of the entry points
+records a memset or an allocation, so capture is safe; a launch-bound loop
+can replay the graph."""
 
 import numpy as np
 import pytest
@@ -18,11 +19,11 @@ from workloads import Workload, make_inputs
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("H,key_groups", [(4, 2), (256, 1)])
-def test_graph_replays_match_eager(H, key_groups):
+@pytest.mark.parametrize("H,D,key_groups", [(4, 64, 2), (4, 128, 4), (256, 64, 1)])
+def test_graph_replays_match_eager(H, D, key_groups):
     dev = torch.device("cuda:0")
-    w = Workload("graph_f16", 1, H, 300, 64, "f16", True, seed=777)
-    assert fa.fa_key_groups_suggest(1, H, 300, 64, fa.FA_F16, True) == key_groups
+    w = Workload("graph_f16", 1, H, 300, D, "f16", True, seed=777)
+    assert fa.fa_key_groups_suggest(1, H, 300, D, fa.FA_F16, True) == key_groups
     shape = w.shape
     q = torch.empty(shape, dtype=torch.float16, device=dev)
     k = torch.empty_like(q)
@@ -31,8 +32,8 @@ def test_graph_replays_match_eager(H, key_groups):
     lse = torch.empty(shape[:3], dtype=torch.float32, device=dev)
     ws_split = fa.splitkv_workspace(q, 3, True)
     ws_naive = fa.naive_workspace(q)
-    qs = torch.empty((1, 300, H, 64), dtype=torch.float16, device=dev).permute(0, 2, 1, 3)
-    os_ = torch.empty((1, 300, H, 64), dtype=torch.float16, device=dev).permute(0, 2, 1, 3)
+    qs = torch.empty((1, 300, H, D), dtype=torch.float16, device=dev).permute(0, 2, 1, 3)
+    os_ = torch.empty((1, 300, H, D), dtype=torch.float16, device=dev).permute(0, 2, 1, 3)
     side = torch.cuda.Stream()
 
     def work(stream):

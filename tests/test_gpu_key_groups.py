@@ -1,18 +1,20 @@
-"""GPU parity of the two key groups of the matrix-core kernel, and of the one
-group on the same problems, against the fp64 oracle, through the C ABI.
+"""GPU parity of the key groups of the matrix-core kernel (two, or four at
+D = 96 and 128), and of the one group on the same problems, against the fp64
+oracle, through the C ABI.
 
 When B*H times the query blocks leave most of the device idle (few heads,
 short rows), fa_forward, fa_forward_strided and fa_forward_ex (one key range)
-run workgroups whose waves form two groups over the same query rows, taking
-alternate key tiles; each group keeps its own running maximum, denominator
-and accumulator, and the two are merged in LDS by the rescaling rule of the
-online softmax ("Android Transformer Optimization: Attention and Mobile GPU
+run workgroups whose waves form two or four groups over the same query rows,
+taking every second or fourth key tile; each group keeps its own running
+maximum, denominator and accumulator, and they are merged in LDS by the
+rescaling rule of the online softmax ("Android Transformer Optimization: Attention and Mobile GPU
 Bottlenecks", sections "The Essence of FlashAttention: Reordering the
 Computation" and "A Complete Tile Loop").  fa_key_groups_suggest names the
 choice, so every case here asserts which path it runs:
 
-  * small grids: two groups (ragged N, both masks, every head dimension,
-    fp16 and bf16; rows whose second group sees no key at all);
+  * small grids: two groups at D = 64, four at D = 96 and 128 (ragged N,
+    both masks, every head dimension, fp16 and bf16; rows whose later groups
+    see no key at all);
   * the same heads repeated until the grid fills the device: one group, on
     the same feature matrix (log-sum-exp output, strided layouts, grouped
     key/value heads), so that both kernels keep that coverage.
@@ -45,14 +47,14 @@ def _say(msg):
 
 def groups(B, H, N, D, dtype, causal):
     g = fa.fa_key_groups_suggest(B, H, N, D, CODES[dtype], causal)
-    assert g in (1, 2), f"fa_key_groups_suggest returned {g}"
+    assert g in (1, 2, 4), f"fa_key_groups_suggest returned {g}"
     return g
 
 
 def heads_for_one_group(N, D, dtype, causal):
     """Fewest heads (a power of two) at which B = 1 runs one key group."""
     H = 1
-    while groups(1, H, N, D, dtype, causal) == 2:
+    while groups(1, H, N, D, dtype, causal) != 1:
         H *= 2
     return H
 
@@ -69,10 +71,11 @@ def tile_heads(bits, H):
 @pytest.mark.parametrize("causal", [False, True])
 def test_two_groups_small_grid(dtype, D, causal):
     for N, (B, H) in CASES:
-        assert groups(B, H, N, D, dtype, causal) == 2, f"N={N} B={B} H={H}: expected two key groups"
+        want = 2 if D == 64 else 4
+        assert groups(B, H, N, D, dtype, causal) == want, f"N={N} B={B} H={H}: expected {want} key groups"
         w = Workload(f"kg2_{dtype}_d{D}_n{N}", B, H, N, D, dtype, causal,
                      seed=70_000 + 17 * N + D + (1 if causal else 0))
-        _say(f"[key groups 2] {w.name} causal={causal} B={B} H={H}")
+        _say(f"[key groups {want}] {w.name} causal={causal} B={B} H={H}")
         x = make_inputs(w)
         ref, ref_lse = oracle.forward(x["q"], x["k"], x["v"], dtype, w.scale, causal, return_lse=True)
         q, k, v = (to_device(x[n], dtype) for n in "qkv")
@@ -100,8 +103,9 @@ def test_full_grids_take_one_group():
     assert groups(4, 32, 2048, 64, "bf16", True) == 1
     assert groups(1, 16, 8192, 128, "f16", True) == 1
     cus, _ = fa.fa_device_info()
-    # the ragged workload: 16 heads x 8 blocks of 128 rows, one workgroup per CU
-    assert groups(2, 8, 1000, 96, "f16", False) == (2 if 2 * 128 <= cus else 1)
+    # the ragged workload: 16 heads x 4 blocks of 256 rows, a quarter of the
+    # CUs: four groups at D = 96
+    assert groups(2, 8, 1000, 96, "f16", False) == (4 if 4 * 16 * 4 <= cus else 1)
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
@@ -188,14 +192,15 @@ LAYOUTS = [("bnhd", "bnhd", "bnhd", "bnhd"), ("pad", "bhnd", "pad", "bnhd")]
 @pytest.mark.parametrize("causal", [False, True])
 def test_strided_gqa_both_paths(dtype, D, causal):
     """Strided layouts with grouped key/value heads: on a small grid (two
-    groups) and with the query heads repeated to fill the device (one group;
-    the key/value heads repeated alike keep each query head's pairing)."""
+    key groups at D = 64, four at D = 128) and with the query heads repeated
+    to fill the device (one group; the key/value heads repeated alike keep
+    each query head's pairing)."""
     N, H, Hkv = 200, 4, 2
     w = Workload(f"kgs_{dtype}_d{D}", 1, H, N, D, dtype, causal, seed=72_000 + D + (1 if causal else 0))
     q, k, v = make_gqa_inputs(w, Hkv)
     ref = oracle.forward(q, expand(k, H // Hkv), expand(v, H // Hkv), dtype, w.scale, causal)
     H1 = max(heads_for_one_group(N, D, dtype, causal), H)
-    for Hq, want in ((H, 2), (H1, 1)):
+    for Hq, want in ((H, 2 if D == 64 else 4), (H1, 1)):
         assert groups(1, Hq, N, D, dtype, causal) == want
         rep = Hq // H
         qb, kb, vb = tile_heads(q, Hq), tile_heads(k, Hkv * rep), tile_heads(v, Hkv * rep)

@@ -55,11 +55,13 @@ def test_one_long_head(causal):
 
 @pytest.mark.parametrize("dtype,D,H,causal", [("f16", 64, 1, False), ("bf16", 128, 2, True), ("f16", 96, 1, True)])
 def test_long_rows_two_key_groups(dtype, D, H, causal):
-    """16,384-token rows on grids small enough for two key groups: chains of
-    128 key tiles per group, merged at the end.  Sampled rows against the
-    oracle, with fa_forward_ex's log-sum-exp."""
+    """16,384-token rows on grids small enough for key groups (two at D = 64,
+    chains of 128 64-key tiles per group; four at D = 96 and 128, chains of
+    128 32-key tiles), merged at the end.  Sampled rows against the oracle,
+    with fa_forward_ex's log-sum-exp."""
     N = 16384
-    assert fa.fa_key_groups_suggest(1, H, N, D, {"f16": fa.FA_F16, "bf16": fa.FA_BF16}[dtype], causal) == 2
+    want = 2 if D == 64 else 4
+    assert fa.fa_key_groups_suggest(1, H, N, D, {"f16": fa.FA_F16, "bf16": fa.FA_BF16}[dtype], causal) == want
     w = Workload(f"limit_kg2_{dtype}_d{D}", 1, H, N, D, dtype, causal, seed=9010 + D)
     _say(f"[limits] {w.name} H={H} causal={causal}")
     x = make_inputs(w)

@@ -31,7 +31,7 @@ CODES = {"f16": 1, "bf16": 2}
 CASES = [
     (1, 12, 4096, 128, "bf16", (2, 1, 32)),  # the 8-wave grid fills 3/4 of the slots
     (1, 14, 4096, 128, "bf16", (4, 1, 32)),  # above 3/4
-    (1, 4, 4096, 128, "bf16", (4, 2, 64)),  # at most 1/2: two key groups
+    (1, 4, 4096, 128, "bf16", (8, 4, 32)),  # at most 1/2: four key groups at D = 128
     (1, 12, 2048, 96, "bf16", (4, 1, 64)),  # 3/4 band at D = 96: one group
     (4, 32, 2048, 64, "bf16", (4, 1, 32)),  # D = 64, four passes: 32-key tiles
     (1, 28, 2048, 64, "bf16", (4, 1, 64)),  # one pass: the table's tiles

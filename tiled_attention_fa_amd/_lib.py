@@ -167,7 +167,7 @@ def fa_splitkv_suggest(B: int, H: int, N: int, D: int, dtype: int, causal: bool)
 
 
 def fa_key_groups_suggest(B: int, H: int, N: int, D: int, dtype: int, causal: bool) -> int:
-    """Key groups (1 or 2) the forward kernel uses for these sizes on the
+    """Key groups (1, 2 or 4) the forward kernel uses for these sizes on the
     current device, or a negative status."""
     return int(load_library().fa_key_groups_suggest(int(B), int(H), int(N), int(D), int(dtype),
                                                     int(bool(causal))))

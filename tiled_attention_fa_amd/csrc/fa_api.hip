@@ -188,8 +188,8 @@ int suggest_splits(int64_t BH, int64_t N, int64_t D, int dtype, bool causal, int
   return s < 1 ? 1 : (int)s;
 }
 
-// Key groups per workgroup (1 or 2) for the matrix-core kernel, and the
-// waves of the two-group workgroup (*ks_waves, 4 or 8), measured on MI355X.
+// Key groups per workgroup (1, 2 or 4) for the matrix-core kernel, and the
+// waves of the multi-group workgroup (*ks_waves, 4 or 8), measured on MI355X.
 // Two groups halve each workgroup's chain of key tiles; the workgroup shape
 // decides how many passes of workgroups over the CUs the grid needs.  Rows within one key
 // tile have nothing to split.
@@ -204,12 +204,22 @@ int suggest_splits(int64_t BH, int64_t N, int64_t D, int dtype, bool causal, int
 //    D = 96 and 128 (2-29% faster), except bf16 at D = 96 and 128, which
 //    runs one group in that band too (its two-group kernels always form the
 //    two-term P; one group runs 6-17% faster); fuller grids run one group.
+//  * At D = 96 and 128, where those rules take the 4-wave two-group shape,
+//    four groups of two 32-row blocks with 32-key tiles run instead (8
+//    waves, two per SIMD, each chain a quarter of the keys; 1.5-7% faster
+//    in the sweep; at D = 64 they are slower).
 int suggest_key_groups(int64_t BH, int64_t N, int64_t D, int dtype, bool causal, int cus, int* ks_waves) {
   *ks_waves = fa::mfma_ks_waves;
   if (dtype == FA_F32 || N <= 64) return 1;
+  // the 4-wave two-group shape, or four groups where they measured faster
+  auto small = [&]() {
+    if (D == 64) return 2;
+    *ks_waves = 8;
+    return 4;
+  };
   if (!causal) {
     const int64_t w = BH * ((N + 255) / 256);
-    if (4 * w <= cus) return 2;
+    if (4 * w <= cus) return small();
     if (D != 96 && 2 * w <= cus) {
       *ks_waves = 8;
       return 2;
@@ -219,7 +229,7 @@ int suggest_key_groups(int64_t BH, int64_t N, int64_t D, int dtype, bool causal,
   const int64_t block_m = 32 * fa::mfma_waves((int)D, causal);
   const int64_t total = BH * ((N + block_m - 1) / block_m);
   const int64_t slots = (int64_t)cus * fa::mfma_wgs_per_cu((int)D, causal);
-  if (2 * total <= slots) return 2;
+  if (2 * total <= slots) return small();
   if (4 * total <= 3 * slots) {
     if (dtype == FA_BF16 && D != 64) return 1;
     if (D != 64) *ks_waves = 8;
@@ -376,7 +386,7 @@ int fa_workgroup_shape(int64_t B, int64_t H, int64_t N, int64_t D, int dtype, in
   p.D = (int)D;
   p.causal = causal != 0;
   choose_shape(p, dtype, cus);
-  int w = p.ks_waves, g = 2, bn = 64;
+  int w = p.ks_waves, g = p.key_groups, bn = p.key_groups == 4 ? 32 : 64;
   if (p.key_groups == 1) {
     g = 1;
     w = p.waves1 ? p.waves1 : fa::mfma_waves(p.D, p.causal);

@@ -132,10 +132,11 @@ hipError_t launch_split_merge(const MergeProblem& p, hipStream_t stream);
 constexpr int kTuneShapes64[][4] = {{2, 1, 1, 64},  {4, 1, 1, 64},  {4, 2, 1, 64},  {8, 1, 1, 64},
                                     {4, 1, 2, 64},  {4, 2, 2, 64},  {8, 1, 2, 64},  {2, 1, 1, 32},
                                     {4, 1, 1, 32},  {4, 2, 1, 32},  {8, 1, 1, 32},  {2, 1, 1, 128},
-                                    {4, 1, 1, 128}, {8, 1, 1, 128}};
+                                    {4, 1, 1, 128}, {8, 1, 1, 128}, {8, 1, 4, 32}};
 constexpr int kTuneShapesWide[][4] = {{2, 1, 1, 64}, {4, 1, 1, 64}, {8, 1, 1, 64}, {4, 1, 2, 64},
-                                      {8, 1, 2, 64}, {2, 1, 1, 32}, {4, 1, 1, 32}, {8, 1, 1, 32}};
-constexpr int kTuneShapes64Count = 14, kTuneShapesWideCount = 8;
+                                      {8, 1, 2, 64}, {2, 1, 1, 32}, {4, 1, 1, 32}, {8, 1, 1, 32},
+                                      {8, 1, 4, 32}};
+constexpr int kTuneShapes64Count = 15, kTuneShapesWideCount = 9;
 hipError_t launch_mfma_shape_f16(const Problem& p, int waves, int occupancy, int key_groups, int block_n,
                                   hipStream_t stream);
 hipError_t launch_mfma_shape_bf16(const Problem& p, int waves, int occupancy, int key_groups, int block_n,

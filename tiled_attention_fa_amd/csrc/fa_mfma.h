@@ -279,8 +279,9 @@ void fa_forward_kernel(Args a) {
   // KS key groups: with KS = 2 the waves form two groups over the same query
   // rows, group g taking key tiles g, g+2, g+4, ... of the range, and their
   // results are merged at the end (for grids that leave CUs idle).
-  static_assert(KS == 1 || (KS == 2 && NW % 2 == 0), "key groups");
-  static_assert(KS == 1 || S::BN == 64, "key groups take 64-key tiles");
+  static_assert(KS == 1 || ((KS == 2 || KS == 4) && NW % KS == 0), "key groups");
+  static_assert(KS == 1 || (KS == 2 && S::BN == 64) || (KS == 4 && S::BN == 32),
+                "two key groups take 64-key tiles, four take 32-key tiles");
   constexpr int NWR = NW / KS;  // waves per key group = 32-row blocks per workgroup
   constexpr int BN = S::BN, BM = 32 * NWR, NT = S::NT, DP = S::DP, CPR = S::CPR;
   constexpr int DC = S::DC, DB = S::DB, TILE = S::TILE, LOADS = S::LOADS;
@@ -291,19 +292,31 @@ void fa_forward_kernel(Args a) {
   // does not wait for the global->LDS loads still in flight into another.
   __shared__ __attribute__((aligned(1024))) uint16_t k0s[TILE], k1s[TILE], k2s[TILE], k3s[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t v0s[TILE], v1s[TILE], v2s[TILE], v3s[TILE];
+  // four key groups: two slots of four tiles per operand, eight arrays each
+  constexpr int TILE4 = KS == 4 ? TILE : 1;
+  __shared__ __attribute__((aligned(1024))) uint16_t k4s[TILE4], k5s[TILE4], k6s[TILE4], k7s[TILE4];
+  __shared__ __attribute__((aligned(1024))) uint16_t v4s[TILE4], v5s[TILE4], v6s[TILE4], v7s[TILE4];
   auto kbuf = [&](auto slot) -> uint16_t* {
-    constexpr int j = decltype(slot)::value & 3;
+    constexpr int j = decltype(slot)::value & 7;
     if constexpr (j == 0) return k0s;
     else if constexpr (j == 1) return k1s;
     else if constexpr (j == 2) return k2s;
-    else return k3s;
+    else if constexpr (j == 3) return k3s;
+    else if constexpr (j == 4) return k4s;
+    else if constexpr (j == 5) return k5s;
+    else if constexpr (j == 6) return k6s;
+    else return k7s;
   };
   auto vbuf = [&](auto slot) -> uint16_t* {
-    constexpr int j = decltype(slot)::value & 3;
+    constexpr int j = decltype(slot)::value & 7;
     if constexpr (j == 0) return v0s;
     else if constexpr (j == 1) return v1s;
     else if constexpr (j == 2) return v2s;
-    else return v3s;
+    else if constexpr (j == 3) return v3s;
+    else if constexpr (j == 4) return v4s;
+    else if constexpr (j == 5) return v5s;
+    else if constexpr (j == 6) return v6s;
+    else return v7s;
   };
 
   const int tid = threadIdx.x;
@@ -614,7 +627,7 @@ void fa_forward_kernel(Args a) {
     // (The eight-wave two-key-group kernels at D = 96 and 128 have no
     // registers to spare for the branch and always take both products,
     // interleaved; with four waves, one per SIMD, they have.)
-    constexpr bool ADAPT = SPLIT_P && (KS == 1 || D == 64 || NW == 4);
+    constexpr bool ADAPT = SPLIT_P && (KS != 2 || D == 64 || NW == 4);
     [[maybe_unused]] bool split = false;
     if constexpr (ADAPT) {
       const float lane_l = (lp[0] + lp[1]) + (lp[2] + lp[3]);
@@ -751,7 +764,7 @@ void fa_forward_kernel(Args a) {
         }
       }
     }
-  } else {
+  } else if constexpr (KS == 2) {
     // Two key groups over pairs of tiles.  K slot j holds K tiles 2p, 2p+1
     // of pair p in arrays k(2j), k(2j+1), V slot j likewise in v(2j),
     // v(2j+1); the K pairs run one ahead of the V pairs.  Step s (j = s % 2)
@@ -851,6 +864,144 @@ void fa_forward_kernel(Args a) {
     for (int i = 0; i < 4; ++i) lp[i] = lp[i] * a0 + ml[i * 64] * a1;
     m_run = M;
     mc = M == -INFINITY ? 0.f : M * c;
+  } else {
+    // Four key groups over quads of 32-key tiles, for grids whose one- and
+    // two-group shapes leave a SIMD one wave: the workgroup's 8 waves are 2
+    // row blocks x 4 groups, two waves per SIMD.  K slot j (of two) holds
+    // the K tiles 4p .. 4p+3 of quad p in arrays k(4j) .. k(4j+3), V slot j
+    // likewise; the K quads run one ahead of the V quads, step by step as
+    // the pairs of two groups do.  Group g takes tile 4s + g of step s.
+    auto load_k_quad = [&](int u0, auto J) {  // tiles t_lo+u0 .. t_lo+u0+3
+      constexpr int j = decltype(J)::value;
+      if (t_lo + u0 < t_hi) load_k_tile(kbuf(std::integral_constant<int, 4 * j>{}));
+      if (t_lo + u0 + 1 < t_hi) load_k_tile(kbuf(std::integral_constant<int, 4 * j + 1>{}));
+      if (t_lo + u0 + 2 < t_hi) load_k_tile(kbuf(std::integral_constant<int, 4 * j + 2>{}));
+      if (t_lo + u0 + 3 < t_hi) load_k_tile(kbuf(std::integral_constant<int, 4 * j + 3>{}));
+    };
+    auto load_v_quad = [&](int u0, auto J) {
+      constexpr int j = decltype(J)::value;
+      if (t_lo + u0 < t_hi) load_v_tile(vbuf(std::integral_constant<int, 4 * j>{}));
+      if (t_lo + u0 + 1 < t_hi) load_v_tile(vbuf(std::integral_constant<int, 4 * j + 1>{}));
+      if (t_lo + u0 + 2 < t_hi) load_v_tile(vbuf(std::integral_constant<int, 4 * j + 2>{}));
+      if (t_lo + u0 + 3 < t_hi) load_v_tile(vbuf(std::integral_constant<int, 4 * j + 3>{}));
+    };
+    // this wave's tile of the quad in slot J (a wave-uniform select)
+    auto my_k = [&](auto J) -> uint16_t* {
+      constexpr int j = decltype(J)::value;
+      uint16_t* const a0 = kbuf(std::integral_constant<int, 4 * j>{});
+      uint16_t* const a1 = kbuf(std::integral_constant<int, 4 * j + 1>{});
+      uint16_t* const a2 = kbuf(std::integral_constant<int, 4 * j + 2>{});
+      uint16_t* const a3 = kbuf(std::integral_constant<int, 4 * j + 3>{});
+      return kgrp == 0 ? a0 : kgrp == 1 ? a1 : kgrp == 2 ? a2 : a3;
+    };
+    auto my_v = [&](auto J) -> uint16_t* {
+      constexpr int j = decltype(J)::value;
+      uint16_t* const a0 = vbuf(std::integral_constant<int, 4 * j>{});
+      uint16_t* const a1 = vbuf(std::integral_constant<int, 4 * j + 1>{});
+      uint16_t* const a2 = vbuf(std::integral_constant<int, 4 * j + 2>{});
+      uint16_t* const a3 = vbuf(std::integral_constant<int, 4 * j + 3>{});
+      return kgrp == 0 ? a0 : kgrp == 1 ? a1 : kgrp == 2 ? a2 : a3;
+    };
+    const int nsteps = (t_hi - t_lo + 3) / 4;
+    if (nsteps > 0) {
+      load_k_quad(0, I0{});
+      load_k_quad(4, I1{});
+      load_v_quad(0, I0{});
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      __syncthreads();
+      qk(my_k(I0{}), sA);
+    }
+    auto qstep = [&](int st, auto J, f32x16 (&sc)[KB], f32x16 (&sn)[KB]) {
+      constexpr int j = decltype(J)::value;
+      using Nx = std::integral_constant<int, (j + 1) & 1>;
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      __syncthreads();
+      load_k_quad(4 * st + 8, J);
+      load_v_quad(4 * st + 4, Nx{});
+      const int t = t_lo + 4 * st + kgrp;
+      if (live(t)) {
+        mask_scores(t, sc);
+        tile_body(my_k(Nx{}), my_v(J), sc, sn, st == 0);
+      }
+    };
+    for (int st = 0; st < nsteps; st += 2) {
+      qstep(st, I0{}, sA, sB);
+      if (st + 1 < nsteps) qstep(st + 1, I1{}, sB, sA);
+    }
+
+    // Merge of the four groups by the same rescaling rule: groups 1-3 leave
+    // their accumulators (4 KiB blocks in the ring arrays k0..k7, v1..v7),
+    // denominator shares and m (mlbuf) in LDS, lane by lane; group 0 takes
+    // M = max_g m_g and a_g = exp2((m_g - M) c), O = sum_g a_g O_g and
+    // l = sum_g a_g l_g (a group that saw no key has weight 0).
+    __shared__ float mlbuf[3 * NWR * 5 * 64];
+    __syncthreads();  // every wave is done with the ring
+    constexpr int per_array = TILE * 2 / 4096;  // 4 KiB blocks per ring array
+    static_assert(per_array >= 1 && 3 * DB * NWR <= 15 * per_array, "merge blocks fit the ring");
+    auto acc_block = [&](int q) -> float* {
+      const int arr = q / per_array, off = (q - arr * per_array) * 1024;
+      uint16_t* base;
+      switch (arr) {
+        case 0: base = kbuf(I0{}); break;
+        case 1: base = kbuf(I1{}); break;
+        case 2: base = kbuf(I2{}); break;
+        case 3: base = kbuf(I3{}); break;
+        case 4: base = kbuf(std::integral_constant<int, 4>{}); break;
+        case 5: base = kbuf(std::integral_constant<int, 5>{}); break;
+        case 6: base = kbuf(std::integral_constant<int, 6>{}); break;
+        case 7: base = kbuf(std::integral_constant<int, 7>{}); break;
+        case 8: base = vbuf(I1{}); break;
+        case 9: base = vbuf(I2{}); break;
+        case 10: base = vbuf(I3{}); break;
+        case 11: base = vbuf(std::integral_constant<int, 4>{}); break;
+        case 12: base = vbuf(std::integral_constant<int, 5>{}); break;
+        case 13: base = vbuf(std::integral_constant<int, 6>{}); break;
+        default: base = vbuf(std::integral_constant<int, 7>{}); break;
+      }
+      return (float*)base + off;
+    };
+    auto ml = [&](int g) -> float* { return mlbuf + ((g - 1) * NWR + rb) * 5 * 64 + lane; };
+    if (kgrp != 0) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        float* blk = acc_block(((kgrp - 1) * DB + db) * NWR + rb) + lane;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) blk[e * 64] = oacc[db][e];
+      }
+      float* const mg = ml(kgrp);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mg[i * 64] = lp[i];
+      mg[4 * 64] = m_run;
+    }
+    __syncthreads();
+    if (kgrp != 0) return;
+    float mo[3];
+    float M = m_run;
+#pragma unroll
+    for (int g = 1; g < 4; ++g) {
+      mo[g - 1] = ml(g)[4 * 64];
+      M = fmaxf(M, mo[g - 1]);
+    }
+    const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run - M) * c);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db] *= a0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lp[i] *= a0;
+#pragma unroll
+    for (int g = 1; g < 4; ++g) {
+      const float ag = mo[g - 1] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((mo[g - 1] - M) * c);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const float* blk = acc_block(((g - 1) * DB + db) * NWR + rb) + lane;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[db][e] += blk[e * 64] * ag;
+      }
+      const float* mg = ml(g);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lp[i] += mg[i * 64] * ag;
+    }
+    m_run = M;
+    mc = M == -INFINITY ? 0.f : M * c;
   }
 
   // Epilogue: divide by the row's denominator once, round, store.
@@ -941,6 +1092,23 @@ inline Args make_args(const Problem& p) {
 template <typename T, bool SPLIT_P>
 hipError_t launch(const Problem& p, hipStream_t stream) {
   const Args a = make_args(p);
+  if (p.key_groups == 4) {
+    // four groups of two 32-row blocks, 32-key tiles (the host's choice for
+    // grids whose two-group shape leaves a SIMD one wave)
+    switch (p.D) {
+      case 64:
+        return p.causal ? launch_one<T, 64, true, SPLIT_P, 8, 1, 4, 32>(a, p.BH, stream)
+                        : launch_one<T, 64, false, SPLIT_P, 8, 1, 4, 32>(a, p.BH, stream);
+      case 96:
+        return p.causal ? launch_one<T, 96, true, SPLIT_P, 8, 1, 4, 32>(a, p.BH, stream)
+                        : launch_one<T, 96, false, SPLIT_P, 8, 1, 4, 32>(a, p.BH, stream);
+      case 128:
+        return p.causal ? launch_one<T, 128, true, SPLIT_P, 8, 1, 4, 32>(a, p.BH, stream)
+                        : launch_one<T, 128, false, SPLIT_P, 8, 1, 4, 32>(a, p.BH, stream);
+      default:
+        return hipErrorInvalidValue;
+    }
+  }
   if (p.key_groups == 2) {
     // the 8-wave shapes the host may choose: non-causal D = 64 and 128,
     // causal D = 96 and 128
@@ -1000,7 +1168,8 @@ hipError_t launch(const Problem& p, hipStream_t stream) {
 // workgroup (two waves of two workgroups sit on two SIMDs only); with D = 96
 // or 128 one workgroup fills the LDS, so those sizes take the one-workgroup
 // shapes only.  128-key tiles take 128 KiB of LDS at D = 64 (one workgroup
-// per CU) and do not fit at D = 96 or 128; key groups take 64-key tiles.
+// per CU) and do not fit at D = 96 or 128; two key groups take 64-key
+// tiles, four take 32-key tiles.
 template <typename T, bool SPLIT_P, int D, bool CAUSAL, int BN>
 hipError_t launch_shape_bn(const Args& a, int64_t BH, int nw, int occ, int ks, hipStream_t s) {
   if (ks == 1) {
@@ -1016,6 +1185,8 @@ hipError_t launch_shape_bn(const Args& a, int64_t BH, int nw, int occ, int ks, h
     if constexpr (D == 64) {
       if (nw == 4 && occ == 2) return launch_one<T, D, CAUSAL, SPLIT_P, 4, 2, 2>(a, BH, s);
     }
+  } else if (ks == 4 && BN == 32) {
+    if (nw == 8 && occ == 1) return launch_one<T, D, CAUSAL, SPLIT_P, 8, 1, 4, 32>(a, BH, s);
   }
   return hipErrorInvalidValue;
 }
