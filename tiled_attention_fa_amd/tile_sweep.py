@@ -9,7 +9,7 @@ memory.  On MI355X a wave owns 32 query rows (the 32x32 matrix-core
 tile); what is calibrated is the number of keys staged in LDS per tile and
 barrier (32, 64 or 128), how many waves share a workgroup (and so its K/V
 tiles in LDS), how many workgroups share a CU, and whether the waves split
-the key tiles in two groups (for grids that leave CUs idle).  This tool times every shape that the calibration
+the key tiles in two or four groups (for grids that leave CUs idle).  This tool times every shape that the calibration
 library (libfa_tune.so) instantiates, for each head dimension, storage
 type and mask, on synthetic inputs drawn by the workload generator, and
 writes a table:
@@ -19,6 +19,8 @@ writes a table:
 It checks every shape's output against libfa.so's fa_forward on the same
 inputs (the library's own choice), and reports fa_forward's time beside the
 sweep so the table shows whether the shipped choice is the fastest.
+`--from-json <out>` rewrites <out>.md from a sweep's saved <out>.json
+without a device.
 """
 
 import argparse
@@ -112,6 +114,53 @@ def tune_forward(lib, q, k, v, o, scale, causal, code, waves, occ, key_groups, b
         raise RuntimeError(f"fa_tune_forward status {st}")
 
 
+def markdown(meta, rows, rows32):
+    """The sweep's tables as Markdown, from the records main() prints and
+    saves (the JSON file holds the same meta, cases and f32_cases)."""
+    lines = [f"# Tile calibration sweep ({meta['arch']}, {meta['cus']} CUs)", "",
+             f"Command (repository root): `{meta['command']}`", "",
+             f"Mean microseconds per launch over {meta['launches_per_timing']} back-to-back launches (HIP events), "
+             f"best of {meta.get('rounds', 3)} interleaved rounds, after 0.25 s of untimed launches per case; "
+             "every workgroup shape of libfa_tune.so: `Nw` = N waves per workgroup (32 query rows "
+             "each), `occK` = waves_per_eu hint K, `ksG` = the waves in G key groups over 1/G as many "
+             "rows, every G-th key tile each, `bnB` = B keys per LDS tile (one barrier each). "
+             "`fa_forward` is the shipped library's own choice on the same inputs. The first table "
+             "gives the fastest shape per key-tile size, the second every shape.", "",
+             "| case | fa_forward | best bn32 | best bn64 | best bn128 | best shape |",
+             "|---|---|---|---|---|---|"]
+
+    def label(s):
+        return (f"{s['waves']}w occ{s['waves_per_eu']}" + (f" ks{s['key_groups']}" if s["key_groups"] > 1 else "")
+                + f" bn{s['block_n']}")
+
+    for r in rows:
+        bb = {int(b): us for b, us in r["best_us_by_block_n"].items()}  # JSON keys are strings
+        cell = lambda b: str(bb[b]) if b in bb else "-"
+        lines.append(f"| {r['case']} | {r['fa_forward_us']} | {cell(32)} | {cell(64)} | {cell(128)} | "
+                     f"{label(r['best'])} |")
+    nmax = max([len(r["shapes"]) for r in rows] or [0])
+    if rows:
+        lines += ["", "| case | " + " | ".join(["shape / us"] * nmax) + " |", "|---|" + "---|" * nmax]
+    for r in rows:
+        cells = [f"{label(s)}: {s['us']}" for s in r["shapes"]]
+        cells += [""] * (nmax - len(cells))
+        lines.append(f"| {r['case']} | " + " | ".join(cells) + " |")
+    worst = max([s["max_abs_diff_vs_fa_forward"] for r in rows for s in r["shapes"]] or [0.0])
+    lines += ["", f"Largest difference of any 16-bit shape's O from fa_forward's: {worst:.3e}."]
+    if rows32:
+        lines += ["", "fp32 (vector kernel: 64 query rows per workgroup, 16-key tiles dealt round-robin to the "
+                  "waves, merged at the end), microseconds per launch:", "",
+                  "| case | fa_forward | 2 waves | 4 waves | 8 waves | best |", "|---|---|---|---|---|---|"]
+        for r in rows32:
+            by = {s["waves"]: s["us"] for s in r["shapes"]}
+            cell = lambda wv: str(by[wv]) if wv in by else "-"
+            lines.append(f"| {r['case']} | {r['fa_forward_us']} | {cell(2)} | {cell(4)} | {cell(8)} | "
+                         f"{r['best']['waves']} waves |")
+        w32 = max(s["max_abs_diff_vs_fa_forward"] for r in rows32 for s in r["shapes"])
+        lines += ["", f"Largest difference of any fp32 shape's O from fa_forward's: {w32:.3e}."]
+    return "\n".join(lines) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--out", default="", help="write <out>.json and <out>.md")
@@ -120,7 +169,13 @@ def main():
                     help="interleaved rounds over fa_forward and the shapes; the best round counts")
     ap.add_argument("--only", default="",
                     help="comma-separated substrings: sweep only the cases whose name contains one")
+    ap.add_argument("--from-json", default="",
+                    help="write <from-json>.md from the saved <from-json>.json and stop (no device)")
     args = ap.parse_args()
+    if args.from_json:
+        saved = json.load(open(args.from_json + ".json"))
+        open(args.from_json + ".md", "w").write(markdown(saved["meta"], saved["cases"], saved.get("f32_cases", [])))
+        return
     only = [x for x in args.only.split(",") if x]
 
     sys.path.insert(0, ROOT)
@@ -259,51 +314,10 @@ def main():
     if args.out:
         prop = torch.cuda.get_device_properties(dev)
         meta = {"device": prop.name, "arch": getattr(prop, "gcnArchName", ""), "cus": prop.multi_processor_count,
-                "launches_per_timing": args.launches,
+                "launches_per_timing": args.launches, "rounds": args.rounds,
                 "command": "python -m tiled_attention_fa_amd.tile_sweep --out " + args.out}
         json.dump({"meta": meta, "cases": rows, "f32_cases": rows32}, open(args.out + ".json", "w"), indent=1)
-        lines = [f"# Tile calibration sweep ({meta['arch']}, {meta['cus']} CUs)", "",
-                 f"Command (repository root): `{meta['command']}`", "",
-                 f"Mean microseconds per launch over {args.launches} back-to-back launches (HIP events), "
-                 f"best of {args.rounds} interleaved rounds, after 0.25 s of untimed launches per case; "
-                 "every workgroup shape of libfa_tune.so: `Nw` = N waves per workgroup (32 query rows "
-                 "each), `occK` = waves_per_eu hint K, `ks2` = the waves in two key groups over half as many "
-                 "rows, alternate key tiles each, `bnB` = B keys per LDS tile (one barrier each). "
-                 "`fa_forward` is the shipped library's own choice on the same inputs. The first table "
-                 "gives the fastest shape per key-tile size, the second every shape.", "",
-                 "| case | fa_forward | best bn32 | best bn64 | best bn128 | best shape |",
-                 "|---|---|---|---|---|---|"]
-
-        def label(s):
-            return (f"{s['waves']}w occ{s['waves_per_eu']}" + (" ks2" if s["key_groups"] == 2 else "")
-                    + f" bn{s['block_n']}")
-
-        for r in rows:
-            bb = r["best_us_by_block_n"]
-            cell = lambda b: str(bb[b]) if b in bb else "-"
-            lines.append(f"| {r['case']} | {r['fa_forward_us']} | {cell(32)} | {cell(64)} | {cell(128)} | "
-                         f"{label(r['best'])} |")
-        nmax = max([len(r["shapes"]) for r in rows] or [0])
-        if rows:
-            lines += ["", "| case | " + " | ".join(["shape / us"] * nmax) + " |", "|---|" + "---|" * nmax]
-        for r in rows:
-            cells = [f"{label(s)}: {s['us']}" for s in r["shapes"]]
-            cells += [""] * (nmax - len(cells))
-            lines.append(f"| {r['case']} | " + " | ".join(cells) + " |")
-        worst = max([s["max_abs_diff_vs_fa_forward"] for r in rows for s in r["shapes"]] or [0.0])
-        lines += ["", f"Largest difference of any 16-bit shape's O from fa_forward's: {worst:.3e}."]
-        if rows32:
-            lines += ["", "fp32 (vector kernel: 64 query rows per workgroup, 16-key tiles dealt round-robin to the "
-                      "waves, merged at the end), microseconds per launch:", "",
-                      "| case | fa_forward | 2 waves | 4 waves | 8 waves | best |", "|---|---|---|---|---|---|"]
-            for r in rows32:
-                by = {s["waves"]: s["us"] for s in r["shapes"]}
-                cell = lambda wv: str(by[wv]) if wv in by else "-"
-                lines.append(f"| {r['case']} | {r['fa_forward_us']} | {cell(2)} | {cell(4)} | {cell(8)} | "
-                             f"{r['best']['waves']} waves |")
-            w32 = max(s["max_abs_diff_vs_fa_forward"] for r in rows32 for s in r["shapes"])
-            lines += ["", f"Largest difference of any fp32 shape's O from fa_forward's: {w32:.3e}."]
-        open(args.out + ".md", "w").write("\n".join(lines) + "\n")
+        open(args.out + ".md", "w").write(markdown(meta, rows, rows32))
 
 
 if __name__ == "__main__":
