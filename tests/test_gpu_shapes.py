@@ -1,17 +1,19 @@
-"""GPU: the workgroup shape fa_forward launches for bf16 causal grids in each
+"""GPU: the workgroup shape fa_forward launches for causal grids in each
 fill band, as fa_workgroup_shape names it, and the results on those grids
 against the fp64 oracle.
 
 The sweep of "Flash Attention on Android: tiled SGEMM with RenderScript",
 section "The detail that breaks naive ports: tile calibration" (the best
-tile differs per device and has to be measured), put bf16 causal work on
-other one-key-group shapes than fp16 on MI355X: 2 or 4 waves with 32-key
-tiles at D = 128, one key group at D = 96 where fp16 takes two, and 32-key
-tiles at D = 64 on grids of several passes.  Each case asserts the shape
-(the expected shapes assume a 256-CU MI355X and are skipped on other
-devices) and checks sampled rows (first and last rows, block edges, random
-rows of the first, last and random heads) against the oracle one by one,
-to the elementwise bound of gpu_helpers.parity.
+tile differs per device and has to be measured), put causal work on other
+one-group shapes than the non-causal table on MI355X, depending on how many
+passes the grid makes over the workgroup slots: 2 waves with 32-key tiles
+at D = 128 up to one pass, 4 waves with 32-key tiles beyond it (bf16
+always, fp16 outside two to three passes), 32-key tiles at D = 64 beyond
+one pass and at D = 96 from three passes.  Each case asserts the shape (the
+expected shapes assume a 256-CU MI355X and are skipped on other devices)
+and checks sampled rows (first and last rows, block edges, random rows of
+the first, last and random heads) against the oracle one by one, to the
+elementwise bound of gpu_helpers.parity.
 """
 
 import numpy as np
@@ -30,13 +32,20 @@ CODES = {"f16": 1, "bf16": 2}
 # (B, H, N, D, dtype, (waves, key groups, keys per LDS tile) on 256 CUs)
 CASES = [
     (1, 12, 4096, 128, "bf16", (2, 1, 32)),  # the 8-wave grid fills 3/4 of the slots
-    (1, 14, 4096, 128, "bf16", (4, 1, 32)),  # above 3/4
+    (1, 14, 4096, 128, "bf16", (2, 1, 32)),  # up to one pass
+    (1, 24, 4096, 128, "bf16", (4, 1, 32)),  # beyond
     (1, 4, 4096, 128, "bf16", (8, 4, 32)),  # at most 1/2: four key groups at D = 128
     (1, 12, 2048, 96, "bf16", (4, 1, 64)),  # 3/4 band at D = 96: one group
+    (1, 48, 2048, 96, "bf16", (4, 1, 32)),  # D = 96, three passes: 32-key tiles
     (4, 32, 2048, 64, "bf16", (4, 1, 32)),  # D = 64, four passes: 32-key tiles
     (1, 28, 2048, 64, "bf16", (4, 1, 64)),  # one pass: the table's tiles
-    (1, 12, 4096, 128, "f16", (8, 2, 64)),  # fp16 keeps two groups in the band
+    (1, 12, 4096, 128, "f16", (8, 2, 64)),  # fp16 keeps two groups up to 3/4
+    (1, 14, 4096, 128, "f16", (2, 1, 32)),  # above, up to one pass
+    (1, 20, 4096, 128, "f16", (4, 1, 32)),  # between one and two passes
+    (1, 32, 4096, 128, "f16", (8, 1, 64)),  # two passes: the table's shape
     (1, 12, 2048, 96, "f16", (8, 2, 64)),
+    (1, 48, 2048, 96, "f16", (4, 1, 32)),
+    (4, 32, 2048, 64, "f16", (4, 1, 32)),
 ]
 
 

@@ -238,24 +238,38 @@ int suggest_key_groups(int64_t BH, int64_t N, int64_t D, int dtype, bool causal,
   return 1;
 }
 
-// The one-group shape for bf16 causal grids (measured on MI355X, where it
-// differs from the table): at D = 128, 2 waves (64 rows) with 32-key tiles
-// where the 8-wave grid fills at most three quarters of the workgroup slots
-// (16-17% faster) and 4 waves with 32-key tiles above (1-5%); at D = 64,
-// 32-key tiles on grids of two or more passes over the slots (3%).  fp16
-// keeps the table's shape.  Sets *waves1 and *block_n1 (0 = the table's).
+// The one-group shape of causal grids where it differs from the table
+// (measured on MI355X with the causal calibration sweep; f = the table
+// shape's workgroups over the CUs' workgroup slots):
+//   D = 64:  32-key tiles beyond one pass (f > 1), 4-10% faster;
+//   D = 96:  32-key tiles from three passes (f >= 3), which halves the ring
+//            and fits two workgroups per CU, 15-20% faster;
+//   D = 128: 2 waves with 32-key tiles up to one pass (f <= 1; for fp16 only
+//            above 3/4, where the key groups do not run), 4-21% faster; 4
+//            waves with 32-key tiles beyond: bf16 always (the 8-wave bf16
+//            kernel has too few registers for split P), fp16 for 1 < f < 2
+//            and f >= 3 (2-9%), the table's 8 waves at 2 <= f < 3.
+// Sets *waves1 and *block_n1 (0 = the table's).
 void one_group_shape(int64_t BH, int64_t N, int64_t D, int dtype, bool causal, int cus, int* waves1,
                      int* block_n1) {
   *waves1 = 0;
   *block_n1 = 0;
-  if (dtype != FA_BF16 || !causal || N <= 64) return;
+  if (dtype == FA_F32 || !causal || N <= 64) return;
   const int64_t block_m = 32 * fa::mfma_waves((int)D, causal);
   const int64_t total = BH * ((N + block_m - 1) / block_m);
   const int64_t slots = (int64_t)cus * fa::mfma_wgs_per_cu((int)D, causal);
-  if (D == 128) {
-    *waves1 = 4 * total <= 3 * slots ? 2 : 4;
-    *block_n1 = 32;
-  } else if (D == 64 && total >= 2 * slots) {
+  if (D == 64) {
+    if (total > slots) *block_n1 = 32;
+  } else if (D == 96) {
+    if (total >= 3 * slots) *block_n1 = 32;
+  } else if (D == 128) {
+    if (total <= slots) {
+      *waves1 = 2;
+    } else if (dtype == FA_BF16 || total < 2 * slots || total >= 3 * slots) {
+      *waves1 = 4;
+    } else {
+      return;
+    }
     *block_n1 = 32;
   }
 }

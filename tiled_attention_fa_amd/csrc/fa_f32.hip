@@ -31,7 +31,6 @@ constexpr int kBlockN = 16;          // keys per tile
 // areas (64 rows x D floats each) fit in LDS, else four
 template <int D>
 constexpr int waves_for() { return D <= 64 ? 8 : 4; }
-constexpr int kXcds = 8;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef double f64x2 __attribute__((ext_vector_type(2)));
 
@@ -53,12 +52,6 @@ struct Args {
   float* part_lse;  // splits > 1: [splits, BH, N] partial log-sum-exp
   float* lse;       // splits == 1, optional: [BH, N] log-sum-exp
 };
-
-__device__ __forceinline__ int xcd_remap(int wg, int total) {
-  const int per = total / kXcds, extra = total % kXcds;
-  const int x = wg % kXcds, slot = wg / kXcds;
-  return x * per + (x < extra ? x : extra) + slot;
-}
 
 // LDS writes of one wave made visible to all its lanes.
 __device__ __forceinline__ void wave_sync() {
@@ -91,13 +84,20 @@ __global__ __launch_bounds__(kBlockM * W) void fa_forward_f32_kernel(Args a) {
   [[maybe_unused]] double* Kd = (double*)tiles[wave];
   float* Vs = tiles[wave] + (KW ? 2 : 1) * BN * D;
 
-  const int logical = xcd_remap(blockIdx.x, a.total_tiles);
   const int per_head = a.num_qtiles * a.splits;
-  const int bh = logical / per_head;
-  const int rem = logical - bh * per_head;
-  int qt = rem / a.splits;
-  const int split = rem - qt * a.splits;
-  if (CAUSAL) qt = a.num_qtiles - 1 - qt;
+  int bh, qt, split = 0;
+  if (CAUSAL && a.splits == 1) {
+    const int id = causal_lpt(blockIdx.x, a.total_tiles, a.num_qtiles);
+    bh = id / a.num_qtiles;
+    qt = a.num_qtiles - 1 - (id - bh * a.num_qtiles);
+  } else {
+    const int logical = xcd_remap(blockIdx.x, a.total_tiles);
+    bh = logical / per_head;
+    const int rem = logical - bh * per_head;
+    qt = rem / a.splits;
+    split = rem - qt * a.splits;
+    if (CAUSAL) qt = a.num_qtiles - 1 - qt;  // longest rows first
+  }
   const int N = a.N;
   const int b = bh / a.H, h = bh - b * a.H, hk = h / a.group;
   const float* __restrict__ Q = a.q + b * a.lq.sb + h * a.lq.sh;

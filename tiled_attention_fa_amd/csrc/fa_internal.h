@@ -49,9 +49,9 @@ struct Problem {
   int key_groups = 1;
   int ks_waves = 4;
   // One key group and one key range: the host may replace the table's
-  // workgroup shape (mfma_waves, mfma_block_n) for bf16 causal grids with
-  // waves1 waves (2 or 4) and block_n1 keys per LDS tile (32); 0 keeps the
-  // table's choice.
+  // workgroup shape (mfma_waves, mfma_block_n) for causal grids with
+  // waves1 waves (2 or 4 at D = 128; 0 elsewhere) and block_n1 keys per LDS
+  // tile (32); 0 keeps the table's choice.
   int waves1 = 0;
   int block_n1 = 0;
 };
@@ -82,7 +82,7 @@ constexpr int mfma_waves(int D, bool causal) { return D == 96 || (D == 64 && cau
 // Keys per LDS tile of the one-group kernel, from the same sweep over 32, 64
 // and 128: 64, except bf16 at D = 128 (split P), where the 64-key build of
 // the kernel needs a few more registers than it has.  128-key tiles come
-// within 1% at best.  (For bf16 causal grids the host names 32-key tiles in
+// within 1% at best.  (For causal grids the host names 32-key tiles in
 // more cases: Problem::block_n1.)
 constexpr int mfma_block_n(int D, bool split_p) { return D == 128 && split_p ? 32 : 64; }
 constexpr int mfma_wgs_per_cu(int D, bool causal) { return D == 64 && causal ? 2 : 1; }
@@ -149,5 +149,54 @@ hipError_t launch_f32_shape(const Problem& p, int waves, hipStream_t stream);
 #endif
 hipError_t launch_naive_f16(const NaiveProblem& p, hipStream_t stream);
 hipError_t launch_naive_bf16(const NaiveProblem& p, hipStream_t stream);
+
+// Workgroup placement shared by the kernels.  MI355X has 8 accelerator
+// complex dies (XCDs), each with its own L2; the dispatcher deals
+// workgroups round-robin over them (workgroup id % 8).
+constexpr int kXcds = 8;
+
+// Workgroup id -> logical tile id.  Workgroups are dispatched round-robin
+// over the 8 XCDs (id % 8), each with its own L2; this gives every XCD a
+// contiguous range of logical tiles, so the query tiles of one head, which
+// all read that head's K and V, run on the same XCD and share its L2.
+__device__ __forceinline__ int xcd_remap(int wg, int total) {
+  const int per = total / kXcds, extra = total % kXcds;
+  const int x = wg % kXcds, slot = wg / kXcds;
+  return x * per + (x < extra ? x : extra) + slot;
+}
+
+// Causal launches: the query blocks of one XCD's share (a contiguous range
+// of head-major tile ids, as xcd_remap hands them out) in order of row
+// length, longest first across every head of the range, instead of head by
+// head.  The dispatcher starts workgroups in order as slots free up, so this
+// is longest-processing-time-first list scheduling: the short blocks fill
+// the slots at the end of the launch instead of the last heads' long ones
+// running alone.  Each XCD keeps the same heads, and so its L2 the same K/V.
+// Returns the head-major tile id h * nq + r, where rank r = 0 is a head's
+// longest rows.
+__device__ __forceinline__ int causal_lpt(int wg, int total, int nq) {
+  const int per = total / kXcds, extra = total % kXcds;
+  const int x = wg % kXcds, s = wg / kXcds;
+  const int lo = x * per + (x < extra ? x : extra);
+  const int last = lo + per - (x < extra ? 0 : 1);
+  const int hA = lo / nq, rA = lo - hA * nq;  // first head, its first rank in the range
+  const int hB = last / nq, rB = last - hB * nq;
+  if (hA == hB) return lo + s;
+  const int full = hB - hA - 1;  // heads with all their ranks in the range
+  // tiles of the range with rank below r
+  auto before = [&](int r) { return full * r + (r > rA ? r - rA : 0) + (r < rB + 1 ? r : rB + 1); };
+  int r0 = 0, r1 = nq - 1;  // the largest r with before(r) <= s
+  while (r0 < r1) {
+    const int m = (r0 + r1 + 1) >> 1;
+    if (before(m) <= s) r0 = m;
+    else r1 = m - 1;
+  }
+  int j = s - before(r0);  // position among the tiles of rank r0: head hA, full heads, head hB
+  if (r0 >= rA) {
+    if (j == 0) return hA * nq + r0;
+    --j;
+  }
+  return (j < full ? hA + 1 + j : hB) * nq + r0;
+}
 
 }  // namespace fa

@@ -90,7 +90,6 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
 constexpr int kBlockN = 64;  // keys per LDS tile unless the shape says otherwise
-constexpr int kXcds = 8;     // MI355X: 8 accelerator complex dies, one L2 each
 constexpr float kLazy = 8.f;  // log2 of the largest p the lazy maximum allows
 // bf16: a tile whose weights all stay below this share of the row's running
 // denominator is multiplied with P rounded once (see the tile body)
@@ -175,16 +174,6 @@ struct Ops<__bf16> {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
   }
 };
-
-// Workgroup id -> logical tile id.  Workgroups are dispatched round-robin
-// over the 8 XCDs (id % 8), each with its own L2; this gives every XCD a
-// contiguous range of logical tiles, so the query tiles of one head, which
-// all read that head's K and V, run on the same XCD and share its L2.
-__device__ __forceinline__ int xcd_remap(int wg, int total) {
-  const int per = total / kXcds, extra = total % kXcds;
-  const int x = wg % kXcds, slot = wg / kXcds;
-  return x * per + (x < extra ? x : extra) + slot;
-}
 
 // Combine both 32-lane halves with a symmetric op: after the swap each lane
 // holds its own value and its partner's (lane ^ 32), in some order.
@@ -328,13 +317,20 @@ void fa_forward_kernel(Args a) {
   const int kgrp = KS == 1 ? 0 : wave / NWR;  // key group
   const int rb = wave - kgrp * NWR;            // 32-row block
 
-  const int logical = xcd_remap(blockIdx.x, a.total_tiles);
   const int per_head = a.num_qtiles * a.splits;
-  const int bh = logical / per_head;
-  const int rem = logical - bh * per_head;
-  int qt = rem / a.splits;
-  const int split = rem - qt * a.splits;
-  if (CAUSAL) qt = a.num_qtiles - 1 - qt;  // longest rows first
+  int bh, qt, split = 0;
+  if (CAUSAL && a.splits == 1) {
+    const int id = causal_lpt(blockIdx.x, a.total_tiles, a.num_qtiles);
+    bh = id / a.num_qtiles;
+    qt = a.num_qtiles - 1 - (id - bh * a.num_qtiles);
+  } else {
+    const int logical = xcd_remap(blockIdx.x, a.total_tiles);
+    bh = logical / per_head;
+    const int rem = logical - bh * per_head;
+    qt = rem / a.splits;
+    split = rem - qt * a.splits;
+    if (CAUSAL) qt = a.num_qtiles - 1 - qt;  // longest rows first
+  }
   const int N = a.N;
   const int b = bh / a.H, h = bh - b * a.H, hk = h / a.group;
   const uint16_t* __restrict__ Q = a.q + b * a.lq.sb + h * a.lq.sh;
@@ -1086,9 +1082,9 @@ inline Args make_args(const Problem& p) {
 // (measured on MI355X).  D = 64 causal runs two workgroups per CU (waves_per_eu 2).  With
 // two key groups (p.key_groups == 2, chosen by the host for grids that leave
 // CUs idle) the workgroup is p.ks_waves waves: 2 or 4 row blocks x 2 key
-// groups.  For bf16 causal grids the host may name another one-group shape
-// (p.waves1, p.block_n1): 32-key tiles at D = 64, or 2 or 4 waves with
-// 32-key tiles at D = 128.
+// groups.  For causal grids the host may name another one-group shape
+// (p.waves1, p.block_n1): 32-key tiles at D = 64 and 96, or 2 or 4 waves
+// with 32-key tiles at D = 128.
 template <typename T, bool SPLIT_P>
 hipError_t launch(const Problem& p, hipStream_t stream) {
   const Args a = make_args(p);
@@ -1133,14 +1129,13 @@ hipError_t launch(const Problem& p, hipStream_t stream) {
         return hipErrorInvalidValue;
     }
   }
-  // the host's bf16 causal shapes (p.waves1, p.block_n1)
-  if constexpr (SPLIT_P) {
-    if (p.causal && p.block_n1 == 32) {
-      if (p.D == 64 && p.waves1 == 0) return launch_one<T, 64, true, SPLIT_P, 4, 2, 1, 32>(a, p.BH, stream);
-      if (p.D == 128 && p.waves1 == 2) return launch_one<T, 128, true, SPLIT_P, 2, 1, 1, 32>(a, p.BH, stream);
-      if (p.D == 128 && p.waves1 == 4) return launch_one<T, 128, true, SPLIT_P, 4, 1, 1, 32>(a, p.BH, stream);
-      return hipErrorInvalidValue;
-    }
+  // the host's causal shapes with 32-key tiles (p.waves1, p.block_n1)
+  if (p.causal && p.block_n1 == 32) {
+    if (p.D == 64 && p.waves1 == 0) return launch_one<T, 64, true, SPLIT_P, 4, 2, 1, 32>(a, p.BH, stream);
+    if (p.D == 96 && p.waves1 == 0) return launch_one<T, 96, true, SPLIT_P, 4, 1, 1, 32>(a, p.BH, stream);
+    if (p.D == 128 && p.waves1 == 2) return launch_one<T, 128, true, SPLIT_P, 2, 1, 1, 32>(a, p.BH, stream);
+    if (p.D == 128 && p.waves1 == 4) return launch_one<T, 128, true, SPLIT_P, 4, 1, 1, 32>(a, p.BH, stream);
+    return hipErrorInvalidValue;
   }
   if (p.waves1 != 0 || p.block_n1 != 0) return hipErrorInvalidValue;
   switch (p.D) {

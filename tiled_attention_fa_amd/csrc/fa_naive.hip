@@ -95,7 +95,7 @@ __global__ __launch_bounds__(kNT) void scores_kernel(Args a) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
-  const int logical = mfma::xcd_remap(blockIdx.x, a.total_tiles);
+  const int logical = xcd_remap(blockIdx.x, a.total_tiles);
   const int bh = logical / a.num_qtiles;
   const int qt = logical - bh * a.num_qtiles;
   const int N = a.N, NP = a.NP;
@@ -312,7 +312,7 @@ __global__ __launch_bounds__(kNT) void pv_kernel(Args a) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
-  const int logical = mfma::xcd_remap(blockIdx.x, a.total_tiles);
+  const int logical = xcd_remap(blockIdx.x, a.total_tiles);
   const int bh = logical / a.num_qtiles;
   const int qt = logical - bh * a.num_qtiles;
   const int N = a.N, NP = a.NP;

@@ -37,8 +37,8 @@ TUNE_LIB = os.path.join(PKG, "libfa_tune.so")
 # (B, H, N, D, causal): per head dimension one non-causal and one causal
 # shape at the sizes of the workloads, each in fp16 and bf16, then grids
 # that fill a quarter, half and three quarters of the device with the
-# one-group shapes (where the key groups may pay), and causal grids between
-# half and seven eighths.
+# one-group shapes (where the key groups may pay), and causal grids from
+# half a pass over the workgroup slots to several.
 CASES = [
     (1, 32, 2048, 64, False), (4, 32, 2048, 64, True),
     (2, 8, 1000, 96, False), (1, 16, 4096, 96, True),
@@ -49,6 +49,23 @@ CASES = [
     (1, 8, 2048, 128, False), (1, 4, 4096, 128, True), (1, 12, 4096, 128, True),
     (1, 24, 2048, 64, True), (1, 28, 2048, 64, True), (1, 12, 2048, 96, True), (1, 6, 8192, 128, True),
     (1, 14, 4096, 128, True),
+    (1, 20, 2048, 64, True), (1, 32, 2048, 64, True), (1, 40, 2048, 64, True), (2, 32, 2048, 64, True),
+    (1, 16, 4096, 128, True), (1, 20, 4096, 128, True), (1, 32, 4096, 128, True), (1, 24, 4096, 96, True),
+]
+# The causal calibration set: per head dimension, grids that fill the
+# one-group kernel's workgroup slots (256 CUs) once, one and a half, two,
+# three and four times, at several row lengths.  In a causal launch the
+# blocks differ in length, so the best shape depends on the fill as well as
+# on D and the storage type.
+CAUSAL_CASES = [
+    (1, H, N, 64, True) for N, Hs in ((2048, (32, 48, 64, 96, 128)), (4096, (16, 24, 32, 48)), (8192, (8, 16)))
+    for H in Hs
+] + [
+    (1, H, N, 96, True) for N, Hs in ((2048, (16, 24, 32, 48, 64)), (4096, (8, 12, 16, 24, 32)), (8192, (8, 12)))
+    for H in Hs
+] + [
+    (1, H, N, 128, True) for N, Hs in ((2048, (32, 48, 64, 96)), (4096, (16, 20, 24, 32, 48)), (8192, (8, 12, 16, 24)))
+    for H in Hs
 ]
 DTYPES = ("f16", "bf16")
 # fp32 (vector kernel): the single-head workload, longer rows at each D, and
@@ -169,6 +186,8 @@ def main():
                     help="interleaved rounds over fa_forward and the shapes; the best round counts")
     ap.add_argument("--only", default="",
                     help="comma-separated substrings: sweep only the cases whose name contains one")
+    ap.add_argument("--set", choices=("default", "causal"), default="default",
+                    help="default: the mixed case list; causal: the causal calibration grids (no fp32 cases)")
     ap.add_argument("--from-json", default="",
                     help="write <from-json>.md from the saved <from-json>.json and stop (no device)")
     args = ap.parse_args()
@@ -205,7 +224,7 @@ def main():
         return e0.elapsed_time(e1) / args.launches * 1e3
 
     rows = []
-    for B, H, N, D, causal in CASES:
+    for B, H, N, D, causal in (CASES if args.set == "default" else CAUSAL_CASES):
         for dt in DTYPES:
             w = workloads.Workload(f"sweep_b{B}h{H}n{N}d{D}_{dt}{'_causal' if causal else ''}", B, H, N, D, dt,
                                    causal, seed=50_000 + N + D)
@@ -267,7 +286,7 @@ def main():
             del q, k, v, ref, out
 
     rows32 = []
-    for B, H, N, D, causal in F32_CASES:
+    for B, H, N, D, causal in (F32_CASES if args.set == "default" else []):
         w = workloads.Workload(f"sweep_b{B}h{H}n{N}d{D}_f32{'_causal' if causal else ''}", B, H, N, D, "f32",
                                causal, seed=52_000 + N + D)
         if only and not any(o in w.name for o in only):
@@ -315,7 +334,8 @@ def main():
         prop = torch.cuda.get_device_properties(dev)
         meta = {"device": prop.name, "arch": getattr(prop, "gcnArchName", ""), "cus": prop.multi_processor_count,
                 "launches_per_timing": args.launches, "rounds": args.rounds,
-                "command": "python -m tiled_attention_fa_amd.tile_sweep --out " + args.out}
+                "command": "python -m tiled_attention_fa_amd.tile_sweep "
+                + ("--set causal " if args.set == "causal" else "") + "--out " + args.out}
         json.dump({"meta": meta, "cases": rows, "f32_cases": rows32}, open(args.out + ".json", "w"), indent=1)
         open(args.out + ".md", "w").write(markdown(meta, rows, rows32))
 
