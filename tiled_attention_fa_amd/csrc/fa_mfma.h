@@ -64,8 +64,9 @@
 //    bf16: P is kept as an unevaluated sum of two bf16 numbers (hi + lo)
 //    and two PV products are issued, so P carries ~16 significant bits, as
 //    with fp16, and l sums the fp32 p; except on tiles where every weight
-//    is small against the row's running sum (below kSplitTau of it), which
-//    take P rounded once to bf16 and add the rounded values to l.
+//    is small against the row's sum so far, this tile included (below
+//    kSplitTau of it), which take P rounded once to bf16 and add the
+//    rounded values to l.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -613,23 +614,19 @@ void fa_forward_kernel(Args a) {
       for (int e = 0; e < 16; ++e) p[kb][e] = __builtin_amdgcn_exp2f(x[kb][e]);
     // bf16 keeps 8 significant bits of each weight.  A wave multiplies
     // with P rounded once when no lane's largest p of this tile exceeds
-    // kSplitTau of that lane's share of the row's running denominator (lanes
-    // 0-31 and 32-63 hold the two halves of each row's keys, so the row's
-    // largest weight then stays below kSplitTau of the row's sum so far);
-    // on a row's first tile (denominator 0), and whenever a few keys carry a
-    // large share of the row, it also multiplies with the rounded remainder
-    // lo = p - hi, so that P carries ~16 significant bits.  xmax may be
-    // stale after a rescale of m, which only overstates p.
+    // kSplitTau of that lane's share of the row's denominator, this tile's
+    // rounded weights included (lanes 0-31 and 32-63 hold the two halves of
+    // each row's keys, so the row's largest weight then stays below
+    // kSplitTau of the row's sum so far, and so of its final sum: the
+    // rounding error any one key adds to O is at most 2^-9 kSplitTau |v - O|);
+    // where a few keys carry a large share of the row, as on its first
+    // tiles, it also multiplies with the rounded remainder lo = p - hi, so
+    // that P carries ~16 significant bits.  xmax may be stale after a
+    // rescale of m, which only overstates p.
     // (The eight-wave two-key-group kernels at D = 96 and 128 have no
     // registers to spare for the branch and always take both products,
     // interleaved; with four waves, one per SIMD, they have.)
     constexpr bool ADAPT = SPLIT_P && (KS != 2 || D == 64 || NW == 4);
-    [[maybe_unused]] bool split = false;
-    if constexpr (ADAPT) {
-      const float lane_l = (lp[0] + lp[1]) + (lp[2] + lp[3]);
-      const float pmax = __builtin_amdgcn_exp2f(xmax);
-      split = __builtin_amdgcn_ballot_w64(!(pmax <= kSplitTau * lane_l)) != 0;
-    }
     // P V over the chunks of 16 keys, with P rounded once (RNE); the row
     // sums add the rounded values, so that the weights applied to V sum to
     // one (this matters when a few keys dominate a row).
@@ -661,7 +658,9 @@ void fa_forward_kernel(Args a) {
       }
     }
     if constexpr (ADAPT) {
-      if (split) {
+      const float lane_l = (lp[0] + lp[1]) + (lp[2] + lp[3]);
+      const float pmax = __builtin_amdgcn_exp2f(xmax);
+      if (__builtin_amdgcn_ballot_w64(!(pmax <= kSplitTau * lane_l)) != 0) {
         // the rounded remainders, their products and their row sums
 #pragma unroll
         for (int kc = 0; kc < 2 * KB; ++kc) {
