@@ -152,14 +152,16 @@ hipError_t launch_naive_bf16(const NaiveProblem& p, hipStream_t stream);
 
 // Workgroup placement shared by the kernels.  MI355X has 8 accelerator
 // complex dies (XCDs), each with its own L2; the dispatcher deals
-// workgroups round-robin over them (workgroup id % 8).
+// workgroups round-robin over them (workgroup id % 8).  Both functions are
+// plain integer arithmetic, callable on the host as well, where a test
+// checks them over whole grids.
 constexpr int kXcds = 8;
 
 // Workgroup id -> logical tile id.  Workgroups are dispatched round-robin
 // over the 8 XCDs (id % 8), each with its own L2; this gives every XCD a
 // contiguous range of logical tiles, so the query tiles of one head, which
 // all read that head's K and V, run on the same XCD and share its L2.
-__device__ __forceinline__ int xcd_remap(int wg, int total) {
+__host__ __device__ __forceinline__ int xcd_remap(int wg, int total) {
   const int per = total / kXcds, extra = total % kXcds;
   const int x = wg % kXcds, slot = wg / kXcds;
   return x * per + (x < extra ? x : extra) + slot;
@@ -174,7 +176,7 @@ __device__ __forceinline__ int xcd_remap(int wg, int total) {
 // running alone.  Each XCD keeps the same heads, and so its L2 the same K/V.
 // Returns the head-major tile id h * nq + r, where rank r = 0 is a head's
 // longest rows.
-__device__ __forceinline__ int causal_lpt(int wg, int total, int nq) {
+__host__ __device__ __forceinline__ int causal_lpt(int wg, int total, int nq) {
   const int per = total / kXcds, extra = total % kXcds;
   const int x = wg % kXcds, s = wg / kXcds;
   const int lo = x * per + (x < extra ? x : extra);
