@@ -249,15 +249,20 @@ struct Shape {
 //  * K (read by ds_read_b128, 16 consecutive rows at one logical chunk per
 //    LDS cycle, 64 banks of 4 bytes): with 128-byte rows (DP = 64) rows r
 //    and r+1 start 32 banks apart, so physical chunk = chunk ^ ((row >> 1)
-//    & 7) puts the 16 rows on 16 distinct 4-bank groups; with 256-byte rows
-//    chunk ^ (row & 7) measured faster.
-//  * V (read by ds_read_b64_tr_b16, 4 consecutive rows x 2 adjacent chunks
-//    per 16-lane group): physical chunk = chunk ^ (2 * (row & 3)).
+//    & 7) puts the 16 rows on 16 distinct 4-bank groups; a 256-byte row
+//    (DP = 128) spans all 64 banks, so chunk ^ (row & 15) does.
+//  * V (read by ds_read_b64_tr_b16, 4 consecutive rows x 4 adjacent chunks
+//    per 32 lanes): physical chunk = chunk ^ (2 * (row & 3)) with 128-byte
+//    rows (rows r and r+1 on different bank halves), chunk ^ (4 * (row & 3))
+//    with 256-byte rows, so the 4 rows read 4 disjoint 64-byte bank groups.
 template <int DP>
 __device__ __forceinline__ int k_swz(int row) {
-  return DP == 64 ? (row >> 1) & 7 : row & 7;
+  return DP == 64 ? (row >> 1) & 7 : row & 15;
 }
-__device__ __forceinline__ int v_swz(int row) { return 2 * (row & 3); }
+template <int DP>
+__device__ __forceinline__ int v_swz(int row) {
+  return DP == 64 ? 2 * (row & 3) : 4 * (row & 3);
+}
 
 // FULL: no causal mask and N a multiple of the key tile, so every tile of
 // the loop holds keys for every row and none needs a mask (the host picks
@@ -383,11 +388,11 @@ void fa_forward_kernel(Args a) {
     const int p = i * NT + tid;
     const int row = p / CPR, pc = p % CPR;
     koff[i] = (row * ldk + 8 * (pc ^ k_swz<DP>(row))) * 2;
-    voff[i] = (row * ldv + 8 * (pc ^ v_swz(row))) * 2;
+    voff[i] = (row * ldv + 8 * (pc ^ v_swz<DP>(row))) * 2;
     // whole waves past the tile (fewer chunks than threads) load nothing
     const bool in_tile = S::CHUNKS % NT == 0 || p < S::CHUNKS;
     kpred[i] = in_tile && (DP == D || (pc ^ k_swz<DP>(row)) < D / 8);
-    vpred[i] = in_tile && (DP == D || (pc ^ v_swz(row)) < D / 8);
+    vpred[i] = in_tile && (DP == D || (pc ^ v_swz<DP>(row)) < D / 8);
   }
   // Tiles are loaded once each, in increasing order, so the loads follow a
   // running pointer and byte count (wave-uniform) instead of forming the
@@ -479,7 +484,7 @@ void fa_forward_kernel(Args a) {
   const int tr_row = 4 * hi + (gl >> 2);  // + 16*kc (+ 8 for the second read)
   // chunk of column 32*db + 16*(g&1) + 4*j is 4*db + 2*(g&1) + (j>>1); the
   // row's swizzle depends on row & 3 = gl >> 2 only
-  const int tr_chunk_lo = (2 * (grp & 1) + ((gl & 3) >> 1)) ^ v_swz(tr_row);
+  const int tr_chunk_lo = (2 * (grp & 1) + ((gl & 3) >> 1)) ^ v_swz<DP>(tr_row);
   const int tr_byte = 8 * (gl & 1);
 
   static_assert(!(FULL && CAUSAL), "a causal tile loop has masked tiles");

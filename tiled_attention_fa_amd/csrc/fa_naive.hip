@@ -337,8 +337,8 @@ __global__ __launch_bounds__(kNT) void pv_kernel(Args a) {
   for (int i = 0; i < VLOADS; ++i) {
     const int p = i * NT + tid;
     const int row = p / CPR, pc = p % CPR;
-    voff[i] = (row * D + 8 * (pc ^ mfma::v_swz(row))) * 2;
-    vpred[i] = DP == D || (pc ^ mfma::v_swz(row)) < D / 8;
+    voff[i] = (row * D + 8 * (pc ^ mfma::v_swz<DP>(row))) * 2;
+    vpred[i] = DP == D || (pc ^ mfma::v_swz<DP>(row)) < D / 8;
   }
 #pragma unroll
   for (int i = 0; i < PLOADS; ++i) {
@@ -362,7 +362,7 @@ __global__ __launch_bounds__(kNT) void pv_kernel(Args a) {
 
   const int grp = lane >> 4, gl = lane & 15;
   const int tr_row = 4 * hi + (gl >> 2);
-  const int tr_chunk_lo = (2 * (grp & 1) + ((gl & 3) >> 1)) ^ mfma::v_swz(tr_row);
+  const int tr_chunk_lo = (2 * (grp & 1) + ((gl & 3) >> 1)) ^ mfma::v_swz<DP>(tr_row);
   const int tr_byte = 8 * (gl & 1);
   const int prow = wave * 32 + l32;  // this lane's row of the P tile
 
