@@ -84,6 +84,7 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -827,7 +828,9 @@ void fa_forward_kernel(Args a) {
     // rows in the same lanes, so group 1 leaves its accumulators, its
     // denominator shares and m in LDS lane by lane and group 0 combines
     // them.  Accumulator block (db, rb) takes 4 KiB of the K arrays (DP/32
-    // blocks per array); m and the shares sit in v(0).
+    // blocks per array), as 4 x 64 lanes of 16 bytes (whole 16-byte LDS
+    // accesses, consecutive lanes on consecutive banks); the shares (16
+    // bytes per lane) and m sit in v(0).
     __syncthreads();  // every wave is done with the ring
     constexpr int per_array = DP / 32;
     auto acc_block = [&](int q) -> float* {
@@ -836,32 +839,39 @@ void fa_forward_kernel(Args a) {
                   : arr == 2 ? (float*)kbuf(I2{}) : (float*)kbuf(I3{});
       return base + off;
     };
-    float* const ml = (float*)vbuf(I0{}) + rb * 5 * 64 + lane;
+    float* const mlb = (float*)vbuf(I0{}) + rb * 5 * 64;
+    f32x4* const shares = (f32x4*)mlb + lane;
+    float* const m_at = mlb + 4 * 64 + lane;
     if (kgrp == 1) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        float* blk = acc_block(db * NWR + rb) + lane;
+        f32x4* blk = (f32x4*)acc_block(db * NWR + rb) + lane;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) blk[e * 64] = oacc[db][e];
+        for (int e4 = 0; e4 < 4; ++e4)
+          blk[e4 * 64] = f32x4{oacc[db][4 * e4], oacc[db][4 * e4 + 1], oacc[db][4 * e4 + 2], oacc[db][4 * e4 + 3]};
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ml[i * 64] = lp[i];
-      ml[4 * 64] = m_run;
+      *shares = f32x4{lp[0], lp[1], lp[2], lp[3]};
+      *m_at = m_run;
     }
     __syncthreads();
     if (kgrp == 1) return;
-    const float m1 = ml[4 * 64];
+    const float m1 = *m_at;
     const float M = fmaxf(m_run, m1);
     const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run - M) * c);
     const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m1 - M) * c);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const float* blk = acc_block(db * NWR + rb) + lane;
+      const f32x4* blk = (const f32x4*)acc_block(db * NWR + rb) + lane;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) oacc[db][e] = oacc[db][e] * a0 + blk[e * 64] * a1;
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const f32x4 x = blk[e4 * 64];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) oacc[db][4 * e4 + i] = oacc[db][4 * e4 + i] * a0 + x[i] * a1;
+      }
     }
+    const f32x4 sh = *shares;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lp[i] = lp[i] * a0 + ml[i * 64] * a1;
+    for (int i = 0; i < 4; ++i) lp[i] = lp[i] * a0 + sh[i] * a1;
     m_run = M;
     mc = M == -INFINITY ? 0.f : M * c;
   } else {
@@ -930,11 +940,12 @@ void fa_forward_kernel(Args a) {
     }
 
     // Merge of the four groups by the same rescaling rule: groups 1-3 leave
-    // their accumulators (4 KiB blocks in the ring arrays k0..k7, v1..v7),
-    // denominator shares and m (mlbuf) in LDS, lane by lane; group 0 takes
+    // their accumulators (4 KiB blocks in the ring arrays k0..k7, v1..v7,
+    // 16 bytes per lane access), denominator shares and m (mlbuf) in LDS,
+    // lane by lane; group 0 takes
     // M = max_g m_g and a_g = exp2((m_g - M) c), O = sum_g a_g O_g and
     // l = sum_g a_g l_g (a group that saw no key has weight 0).
-    __shared__ float mlbuf[3 * NWR * 5 * 64];
+    __shared__ __attribute__((aligned(16))) float mlbuf[3 * NWR * 5 * 64];
     __syncthreads();  // every wave is done with the ring
     constexpr int per_array = TILE * 2 / 4096;  // 4 KiB blocks per ring array
     static_assert(per_array >= 1 && 3 * DB * NWR <= 15 * per_array, "merge blocks fit the ring");
@@ -960,18 +971,19 @@ void fa_forward_kernel(Args a) {
       }
       return (float*)base + off;
     };
-    auto ml = [&](int g) -> float* { return mlbuf + ((g - 1) * NWR + rb) * 5 * 64 + lane; };
+    // group g's shares (16 bytes per lane) and m
+    auto shares = [&](int g) -> f32x4* { return (f32x4*)(mlbuf + ((g - 1) * NWR + rb) * 5 * 64) + lane; };
+    auto m_at = [&](int g) -> float* { return mlbuf + ((g - 1) * NWR + rb) * 5 * 64 + 4 * 64 + lane; };
     if (kgrp != 0) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        float* blk = acc_block(((kgrp - 1) * DB + db) * NWR + rb) + lane;
+        f32x4* blk = (f32x4*)acc_block(((kgrp - 1) * DB + db) * NWR + rb) + lane;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) blk[e * 64] = oacc[db][e];
+        for (int e4 = 0; e4 < 4; ++e4)
+          blk[e4 * 64] = f32x4{oacc[db][4 * e4], oacc[db][4 * e4 + 1], oacc[db][4 * e4 + 2], oacc[db][4 * e4 + 3]};
       }
-      float* const mg = ml(kgrp);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mg[i * 64] = lp[i];
-      mg[4 * 64] = m_run;
+      *shares(kgrp) = f32x4{lp[0], lp[1], lp[2], lp[3]};
+      *m_at(kgrp) = m_run;
     }
     __syncthreads();
     if (kgrp != 0) return;
@@ -979,7 +991,7 @@ void fa_forward_kernel(Args a) {
     float M = m_run;
 #pragma unroll
     for (int g = 1; g < 4; ++g) {
-      mo[g - 1] = ml(g)[4 * 64];
+      mo[g - 1] = *m_at(g);
       M = fmaxf(M, mo[g - 1]);
     }
     const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run - M) * c);
@@ -992,13 +1004,17 @@ void fa_forward_kernel(Args a) {
       const float ag = mo[g - 1] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((mo[g - 1] - M) * c);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const float* blk = acc_block(((g - 1) * DB + db) * NWR + rb) + lane;
+        const f32x4* blk = (const f32x4*)acc_block(((g - 1) * DB + db) * NWR + rb) + lane;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[db][e] += blk[e * 64] * ag;
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const f32x4 x = blk[e4 * 64];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) oacc[db][4 * e4 + i] += x[i] * ag;
+        }
       }
-      const float* mg = ml(g);
+      const f32x4 sh = *shares(g);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) lp[i] += mg[i * 64] * ag;
+      for (int i = 0; i < 4; ++i) lp[i] += sh[i] * ag;
     }
     m_run = M;
     mc = M == -INFINITY ? 0.f : M * c;
