@@ -229,7 +229,9 @@ int fa_splitkv_suggest(int64_t B, int64_t H, int64_t N, int64_t D, int dtype, in
  *     for D = 64 and 96) fill at most half of the device's workgroup slots
  *     (one per CU; two for D = 64; 4 at D = 96 and 128, else 2), or at most
  *     three quarters (2), except bf16 at D = 96 and 128 in that last band;
- * else 1.  With 2 the waves of a workgroup (64 query rows, or 128 on the
+ * for FA_F32, 2 when N >= 256 (eight waves over 64 query rows, two groups
+ * of four taking alternate 32-key tiles); else 1.  With 2 the waves of a
+ * 16-bit workgroup (64 query rows, or 128 on the
  * fuller of those grids) form two groups that take alternate key tiles;
  * with 4, eight waves over 64 query rows form four groups that take every
  * fourth 32-key tile.  The groups' running maxima, denominators and

@@ -54,13 +54,13 @@ int fa_tune_forward(const void* q, const void* k, const void* v, void* o, int64_
                     int occupancy, int key_groups, int block_n, void* stream);
 
 /*
- * fa_tune_f32_shapes -- the workgroup shapes of the fp32 (vector) kernel
- * the sweep covers for head dimension D: writes up to `capacity` wave
- * counts into waves[] (may be NULL) and returns how many there are (3 for
- * D = 64: 2, 4, 8; 2 for D = 96 and 128: 2, 4), or FA_ERR_UNSUPPORTED_D.  A
- * workgroup owns 64 query rows, one per lane of each wave; its key tiles
- * (16 keys) are dealt round-robin to the waves, which merge their partial
- * results at the end.  Host only.
+ * fa_tune_f32_shapes -- the workgroup shapes of the fp32 (matrix-core)
+ * kernel the sweep covers for head dimension D: writes up to `capacity`
+ * wave counts into waves[] (may be NULL) and returns how many there are (2:
+ * 4 and 8), or FA_ERR_UNSUPPORTED_D.  A workgroup owns 64 query rows, 16 per
+ * wave: 4 waves take every key tile (32 keys) of the rows, 8 waves form two
+ * key groups that take alternate tiles and merge their results at the end.
+ * Host only.
  */
 int fa_tune_f32_shapes(int64_t D, int* waves, int capacity);
 

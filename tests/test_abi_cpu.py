@@ -350,9 +350,9 @@ def test_tune_library_exports_its_header():
     assert tile_sweep.shapes(lib, 96) == wide
     assert tile_sweep.shapes(lib, 128) == wide
     assert lib.fa_tune_shapes(80, None, None, None, None, 0) == -3
-    assert tile_sweep.f32_shapes(lib, 64) == [2, 4, 8]
-    assert tile_sweep.f32_shapes(lib, 96) == [2, 4]
-    assert tile_sweep.f32_shapes(lib, 128) == [2, 4]
+    assert tile_sweep.f32_shapes(lib, 64) == [4, 8]
+    assert tile_sweep.f32_shapes(lib, 96) == [4, 8]
+    assert tile_sweep.f32_shapes(lib, 128) == [4, 8]
     assert lib.fa_tune_f32_shapes(80, None, 0) == -3
 
 
@@ -383,13 +383,13 @@ def test_tune_split_merge_validation(args, status):
     (dict(B=0), "FA_ERR_DIM"),
     (dict(D=80), "FA_ERR_UNSUPPORTED_D"),
     (dict(waves=3), "FA_ERR_UNSUPPORTED_D"),
-    (dict(D=128, waves=8), "FA_ERR_UNSUPPORTED_D"),
-    (dict(D=96, waves=8), "FA_ERR_UNSUPPORTED_D"),
+    (dict(D=128, waves=2), "FA_ERR_UNSUPPORTED_D"),
+    (dict(D=96, waves=16), "FA_ERR_UNSUPPORTED_D"),
     (dict(q=0), "FA_ERR_NULL"),
     (dict(o=A), "FA_ERR_ALIAS"),
     (dict(N=0, q=0, k=0, v=0, o=0), "FA_OK"),
     (dict(), "FA_ERR_DEVICE"),
-    (dict(D=128, waves=2), "FA_ERR_DEVICE"),
+    (dict(D=128, waves=4), "FA_ERR_DEVICE"),
 ])
 def test_tune_forward_f32_validation(args, status):
     from tiled_attention_fa_amd import tile_sweep

@@ -212,3 +212,25 @@ def test_strided_gqa_both_paths(dtype, D, causal):
                                   bits_to(vb, dtype, lv, pad=8), o, scale=w.scale, causal=causal)
             torch.cuda.synchronize()
             parity(to_numpy64(o), tile_heads(ref, Hq), dtype, f"{w.name} causal={causal} H={Hq} {layouts}")
+
+
+@pytest.mark.parametrize("N,want", [(64, 1), (255, 1), (256, 2), (1000, 2)])
+@pytest.mark.parametrize("D", [64, 96, 128])
+def test_f32_key_groups_and_parity(N, want, D):
+    """fp32: two groups of four waves once the rows have 8 or more 32-key
+    tiles, one below; both against the oracle with fa_forward (dense) and
+    fa_forward_ex (log-sum-exp), causal and not."""
+    assert fa.fa_key_groups_suggest(1, 3, N, D, fa.FA_F32, False) == want
+    for causal in (False, True):
+        w = Workload(f"kg_f32_d{D}_n{N}", 1, 3, N, D, "f32", causal, seed=73_000 + N + D)
+        x = make_inputs(w)
+        ref, ref_lse = oracle.forward(x["q"], x["k"], x["v"], "f32", w.scale, causal, return_lse=True)
+        q, k, v = (to_device(x[n], "f32") for n in "qkv")
+        _say(f"[key groups {want}] {w.name} causal={causal}")
+        o = fa.forward(q, k, v, scale=w.scale, causal=causal)
+        o2, lse = fa.forward_ex(q, k, v, scale=w.scale, causal=causal, num_splits=1, lse=True)
+        torch.cuda.synchronize()
+        parity(to_numpy64(o), ref, "f32", f"{w.name} causal={causal}")
+        parity(to_numpy64(o2), ref, "f32", f"{w.name} causal={causal} (ex)")
+        err = float(np.abs(lse.double().cpu().numpy() - ref_lse).max())
+        assert err <= LSE_TOL, f"{w.name} causal={causal}: lse error {err:.3e}"

@@ -1,22 +1,22 @@
-// FlashAttention forward for fp32 storage, on the vector ALUs (scores in
-// fp64, everything else in fp32).
+// FlashAttention forward for fp32 storage on the matrix cores: scores in
+// fp64 (v_mfma_f64_16x16x4f64: the products of two fp32 values are exact in
+// fp64 and the sums run in fp64, so large logits keep their absolute
+// precision), the weights P in fp32, and O in fp32 (v_mfma_f32_16x16x4f32).
 //
-// Same tile loop as the matrix-core kernel ("Android Transformer
-// Optimization: Attention and Mobile GPU Bottlenecks", section "A Complete
-// Tile Loop"): per tile the scores are formed, the running maximum and
-// denominator are updated, the accumulator is rescaled by exp(m_old - m_new)
-// and exp(S - m_new) V is added; O is divided by the denominator once at the
-// end.
+// Same tile loop as the 16-bit kernel ("Android Transformer Optimization:
+// Attention and Mobile GPU Bottlenecks", section "A Complete Tile Loop"): per
+// tile the scores are formed, the running maximum and denominator are
+// updated, the accumulator is rescaled by exp(m_old - m_new) and
+// exp(S - m_new) V is added; O is divided by the denominator once at the end.
 //
-// A workgroup owns 64 query rows, one per lane, and has eight waves (four
-// for D > 64).  The key tiles (16 keys) are dealt round-robin to the waves:
-// each wave keeps its own running maximum, denominator and accumulator for
-// the 64 rows over its share of the keys, staging its tiles in an LDS region
-// of its own (so the waves never wait for each other inside the loop).  At
-// the end the waves' partial results are merged with the same rescaling
-// rule: with M the largest of the waves' maxima, O = sum_w exp(m_w - M)
-// acc_w / sum_w exp(m_w - M) l_w.  Every K and V element a wave reads is the
-// same for all its lanes, which LDS serves as a broadcast.
+// A workgroup owns 64 query rows, 16 per wave, in one or two key groups of
+// four waves; group g takes the key tiles (32 keys) g, g + KG, ... and the
+// groups' results are merged at the end by the same rescaling rule.  A wave
+// forms S^T = K Q^T for 16 keys x its 16 rows per block: lane l holds the
+// scores of row l & 15 for keys (l >> 4) + 4e, e = 0..3.  Those four scores
+// are exactly the P^T operand of the four k-steps of O^T += V^T P^T (k-step e
+// takes keys (l >> 4) + 4e of every lane group), so P never moves between
+// lanes; V is read from LDS in the matching key order.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -25,14 +25,21 @@
 namespace fa {
 namespace f32k {
 
-constexpr int kBlockM = kF32BlockM;  // query rows per workgroup (= lanes)
-constexpr int kBlockN = 16;          // keys per tile
-// waves per workgroup, each a share of the keys: eight while their merge
-// areas (64 rows x D floats each) fit in LDS, else four
-template <int D>
-constexpr int waves_for() { return D <= 64 ? 8 : 4; }
+constexpr int kBlockM = kF32BlockM;  // query rows per workgroup: four waves of 16
+constexpr int kRowWaves = kBlockM / 16;
+constexpr int kBlockN = 32;          // keys per LDS tile: two blocks of 16
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef double f64x2 __attribute__((ext_vector_type(2)));
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+// LDS row pitches (floats).  The K operand of a k-step is row l & 15, column
+// 4s + (l >> 4) for lane l: a pitch of 4 (mod 64) words puts the 64 lanes on
+// 64 distinct banks.  The V operand is row (l >> 4) + 4e, column 16 db +
+// (l & 15): a pitch of 16 (mod 64) words does.  D = 96 takes the D = 128
+// pitches.
+template <int D>
+constexpr int k_pitch() { return D <= 64 ? 68 : 132; }
+template <int D>
+constexpr int v_pitch() { return D <= 64 ? 80 : 144; }
 
 struct Args {
   const float* q;
@@ -53,36 +60,34 @@ struct Args {
   float* lse;       // splits == 1, optional: [BH, N] log-sum-exp
 };
 
-// LDS writes of one wave made visible to all its lanes.
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+__device__ __forceinline__ double lanes_max(double x) {  // over lanes l, l ^ 16, l ^ 32, l ^ 48
+  x = fmax(x, __shfl_xor(x, 16));
+  return fmax(x, __shfl_xor(x, 32));
+}
+__device__ __forceinline__ float lanes_sum(float x) {
+  x += __shfl_xor(x, 16);
+  return x + __shfl_xor(x, 32);
 }
 
-template <int D, bool CAUSAL, int W = waves_for<D>()>
-__global__ __launch_bounds__(kBlockM * W) void fa_forward_f32_kernel(Args a) {
-  constexpr int BN = kBlockN;
-  constexpr int kWaves = W;
-  static_assert((D / W) % 4 == 0, "each wave merges whole 16-byte column groups");
-  static_assert(D % 16 == 0 && D <= 128, "head dim");
-  // Per wave: a K tile and a V tile; after the loop the same memory holds
-  // the waves' accumulators (64 rows x D) for the merge.
-  __shared__ __attribute__((aligned(16))) float tiles[kWaves][kBlockM * D];
-  __shared__ double m_part[kWaves][kBlockM];
-  __shared__ float l_part[kWaves][kBlockM];
-  static_assert(3 * BN * D <= kBlockM * D, "tiles fit in the merge area");
+template <int D, bool CAUSAL, int KG>
+__global__ __launch_bounds__(64 * kRowWaves * KG) void fa_forward_f32_kernel(Args a) {
+  constexpr int BN = kBlockN, PK = k_pitch<D>(), PV = v_pitch<D>();
+  constexpr int NT = 64 * kRowWaves;  // threads of one key group
+  constexpr int DS = D / 4;           // k-steps of S^T = K Q^T (4 head dims each)
+  constexpr int DB = D / 16;          // 16-column blocks of O
+  constexpr int CH = BN * D / 4 / NT; // 16-byte loads per thread, operand and tile
+  static_assert(KG == 1 || KG == 2, "key groups");
+  static_assert(D % 32 == 0 && D <= 128 && CH * NT * 4 == BN * D, "head dim");
+  __shared__ __attribute__((aligned(16))) float Ks[KG][BN * PK];
+  __shared__ __attribute__((aligned(16))) float Vs[KG][BN * PV];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  // D > 64: K is staged already widened to fp64, each element converted
-  // once instead of once per query row (15-16% faster at D = 96 and 128);
-  // at D = 64 the doubled LDS reads cost more than the conversions saved
-  constexpr bool KW = D > 64;
-  float* Ks = tiles[wave];
-  [[maybe_unused]] double* Kd = (double*)tiles[wave];
-  float* Vs = tiles[wave] + (KW ? 2 : 1) * BN * D;
+  const int kgrp = KG == 1 ? 0 : wave / kRowWaves;  // key group
+  const int rw = wave - kgrp * kRowWaves;           // 16-row block
+  const int gtid = tid - kgrp * NT;                 // thread within the key group
+  const int c16 = lane & 15, lg = lane >> 4;
 
   const int per_head = a.num_qtiles * a.splits;
   int bh, qt, split = 0;
@@ -106,167 +111,158 @@ __global__ __launch_bounds__(kBlockM * W) void fa_forward_f32_kernel(Args a) {
   float* __restrict__ O = a.o + b * a.lo.sb + h * a.lo.sh;
   const int ldq = a.lq.sn, ldk = a.lk.sn, ldv = a.lv.sn, ldo = a.lo.sn;  // row strides
   const double cd = a.c;
-  const int qrow = qt * kBlockM + lane;
+  const int q0 = qt * kBlockM + 16 * rw;  // first query row of this wave
+  const int row = q0 + c16;               // this lane's query row
 
-  float q[D];
+  // Q^T operand: k-step s takes head dims 4s .. 4s+3; lane l holds row
+  // q0 + (l & 15), dim 4s + (l >> 4), widened to fp64 once (exact).
+  double qd[DS];
 #pragma unroll
-  for (int d = 0; d < D; d += 4) {
-    f32x4 x = {0.f, 0.f, 0.f, 0.f};
-    if (qrow < N) x = *(const f32x4*)(Q + (size_t)qrow * ldq + d);
-    q[d] = x[0] * a.qsign;
-    q[d + 1] = x[1] * a.qsign;
-    q[d + 2] = x[2] * a.qsign;
-    q[d + 3] = x[3] * a.qsign;
-  }
-  float acc[D];
+  for (int s = 0; s < DS; ++s) qd[s] = row < N ? (double)(Q[(size_t)row * ldq + 4 * s + lg] * a.qsign) : 0.0;
+
+  f32x4 o[DB];
 #pragma unroll
-  for (int d = 0; d < D; ++d) acc[d] = 0.f;
-  double m_run = -INFINITY;
-  float l_run = 0.f;
+  for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  double m_run = -INFINITY;  // running maximum of the raw scores of the row
+  float l_part = 0.f;        // this lane's share of the row's denominator
 
   const int kv_end = CAUSAL ? min(N, qt * kBlockM + kBlockM) : N;
   const int ntiles = (kv_end + BN - 1) / BN;
   // this workgroup's share of the key tiles (all of them when splits == 1)
   const int t_lo = split * ntiles / a.splits;
   const int t_hi = (split + 1) * ntiles / a.splits;
-  for (int t = t_lo + wave; t < t_hi; t += kWaves) {
-    const int k0 = t * BN;
-    // this wave's tile: 16 rows of K and of V, 16 bytes per lane per load
-    for (int idx = lane; idx < BN * D / 4; idx += 64) {
-      const int r = idx / (D / 4), c4 = idx - r * (D / 4);
-      f32x4 kx = {0.f, 0.f, 0.f, 0.f}, vx = {0.f, 0.f, 0.f, 0.f};
-      if (k0 + r < N) {
-        kx = *(const f32x4*)(K + (size_t)(k0 + r) * ldk + 4 * c4);
-        vx = *(const f32x4*)(V + (size_t)(k0 + r) * ldv + 4 * c4);
-      }
-      if constexpr (KW) {
-        *(f64x2*)(Kd + r * D + 4 * c4) = f64x2{(double)kx[0], (double)kx[1]};
-        *(f64x2*)(Kd + r * D + 4 * c4 + 2) = f64x2{(double)kx[2], (double)kx[3]};
-      } else {
-        *(f32x4*)(Ks + r * D + 4 * c4) = kx;
-      }
-      *(f32x4*)(Vs + r * D + 4 * c4) = vx;
-    }
-    wave_sync();
 
-    // Scores in fp64: the products of two fp32 values are exact in fp64 and
-    // the D-term sum keeps ~1e-16 relative error, so large logits do not
-    // lose absolute precision before the exponential.  Two partial sums
-    // per key halve the dependent chain.
-    double s[BN];
+  // Tile t of the key group: loaded by its threads into registers (16 bytes
+  // each, zero past key N), then stored to the group's LDS tile.
+  f32x4 kr[CH], vr[CH];
+  auto fetch = [&](int t) {
+    const int k0 = t * BN;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int idx = i * NT + gtid, r = idx / (D / 4), c4 = idx - r * (D / 4);
+      kr[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      vr[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (k0 + r < N) {
+        kr[i] = *(const f32x4*)(K + (size_t)(k0 + r) * ldk + 4 * c4);
+        vr[i] = *(const f32x4*)(V + (size_t)(k0 + r) * ldv + 4 * c4);
+      }
+    }
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int idx = i * NT + gtid, r = idx / (D / 4), c4 = idx - r * (D / 4);
+      *(f32x4*)(&Ks[kgrp][r * PK + 4 * c4]) = kr[i];
+      *(f32x4*)(&Vs[kgrp][r * PV + 4 * c4]) = vr[i];
+    }
+  };
+
+  auto tile = [&](int t) {
+    const int k0 = t * BN;
+    const float* ks = Ks[kgrp];
+    const float* vs = Vs[kgrp];
+    // S^T for the two 16-key blocks: element e of block kb is the score of
+    // key k0 + 16 kb + (l >> 4) + 4e against this lane's row
+    double sc[2][4];
     double mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < BN; ++j) {
-      double d0 = 0.0, d1 = 0.0;
+    for (int kb = 0; kb < 2; ++kb) {
+      f64x4 acc = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-      for (int d = 0; d < D; d += 4) {
-        f32x4 qx = {q[d], q[d + 1], q[d + 2], q[d + 3]};
-        if constexpr (KW) {
-          // the widened Q row (2 D registers) would not fit beside the
-          // accumulator: an opaque copy keeps its widening per use
-          asm volatile("" : "+v"(qx));
-          const f64x2 k01 = *(const f64x2*)(Kd + j * D + d);
-          const f64x2 k23 = *(const f64x2*)(Kd + j * D + d + 2);
-          d0 = __builtin_fma((double)qx[0], k01[0], d0);
-          d1 = __builtin_fma((double)qx[1], k01[1], d1);
-          d0 = __builtin_fma((double)qx[2], k23[0], d0);
-          d1 = __builtin_fma((double)qx[3], k23[1], d1);
-        } else {
-          const f32x4 kx = *(const f32x4*)(Ks + j * D + d);
-          d0 = __builtin_fma((double)qx[0], (double)kx[0], d0);
-          d1 = __builtin_fma((double)qx[1], (double)kx[1], d1);
-          d0 = __builtin_fma((double)qx[2], (double)kx[2], d0);
-          d1 = __builtin_fma((double)qx[3], (double)kx[3], d1);
-        }
+      for (int s = 0; s < DS; ++s)
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)ks[(16 * kb + c16) * PK + 4 * s + lg], qd[s], acc, 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int key = k0 + 16 * kb + lg + 4 * e;
+        sc[kb][e] = (key >= N || (CAUSAL && key > row)) ? -INFINITY : acc[e];
+        mx = fmax(mx, sc[kb][e]);
       }
-      double dot = d0 + d1;
-      const int key = k0 + j;
-      if (key >= N || (CAUSAL && key > qrow)) dot = -INFINITY;
-      s[j] = dot;
-      mx = dot > mx ? dot : mx;
     }
-    const double m_new = m_run > mx ? m_run : mx;
-    // exp(scale * (s - m)) = exp2(c * (s - m)); the difference is formed in
-    // fp64 before rounding to fp32, so its error is relative to |s - m|.
-    // A row with no visible key in this tile keeps m_new = m_run.
-    const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((float)((m_run - m_new) * cd));
+    const double m_new = fmax(m_run, lanes_max(mx));
+    // exp(scale (s - m)) = exp2(c (s - m)), the difference formed in fp64
+    // before rounding to fp32; a row with no visible key so far keeps -inf
+    const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((float)((m_run - m_new) * cd));
     m_run = m_new;
-    float pr[BN];
-    float psum = 0.f;
+    float p[2][4];
+    float ps = 0.f;
 #pragma unroll
-    for (int j = 0; j < BN; ++j) {
-      float p = __builtin_amdgcn_exp2f((float)((s[j] - m_new) * cd));
-      if (s[j] == -INFINITY) p = 0.f;  // masked; also right when c == 0
-      pr[j] = p;
-      psum += p;
-    }
-    l_run = l_run * alpha + psum;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int d = 0; d < D; ++d) acc[d] *= alpha;
-#pragma unroll
-    for (int j = 0; j < BN; ++j) {
-#pragma unroll
-      for (int d = 0; d < D; d += 4) {
-        const f32x4 vx = *(const f32x4*)(Vs + j * D + d);
-        acc[d] = __builtin_fmaf(pr[j], vx[0], acc[d]);
-        acc[d + 1] = __builtin_fmaf(pr[j], vx[1], acc[d + 1]);
-        acc[d + 2] = __builtin_fmaf(pr[j], vx[2], acc[d + 2]);
-        acc[d + 3] = __builtin_fmaf(pr[j], vx[3], acc[d + 3]);
+      for (int e = 0; e < 4; ++e) {
+        p[kb][e] = sc[kb][e] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((float)((sc[kb][e] - m_new) * cd));
+        ps += p[kb][e];
       }
+    l_part = l_part * alpha + ps;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] *= alpha;
+    // O^T += V^T P^T: k-step (kb, e) takes keys 16 kb + j + 4e, j = 0..3,
+    // the j-th from lane group j, which holds it as its element e
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          o[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(vs[(16 * kb + lg + 4 * e) * PV + 16 * db + c16], p[kb][e],
+                                                       o[db], 0, 0, 0);
+  };
+
+  // Every key group runs the same number of steps, so the barriers match.
+  const int steps = (t_hi - t_lo + KG - 1) / KG;
+  int t = t_lo + kgrp;
+  if (t < t_hi) fetch(t);
+  for (int st = 0; st < steps; ++st, t += KG) {
+    __syncthreads();  // every wave is done with the previous tiles
+    if (t < t_hi) stash();
+    __syncthreads();
+    if (t + KG < t_hi) fetch(t + KG);
+    // a causal tile whose first key lies past the wave's last row holds
+    // nothing for it
+    if (t < t_hi && (!CAUSAL || t * BN <= q0 + 15)) tile(t);
+  }
+
+  if constexpr (KG == 2) {
+    // group 1 leaves O, m and its denominator shares in LDS, lane by lane
+    // (16-byte accesses); group 0 merges by the rescaling rule
+    __shared__ __attribute__((aligned(16))) f32x4 mo[DB * NT];
+    __shared__ double mm[NT];
+    __shared__ float ml[NT];
+    if (kgrp == 1) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) mo[db * NT + gtid] = o[db];
+      mm[gtid] = m_run;
+      ml[gtid] = l_part;
     }
-    wave_sync();  // all lanes are done with the tile before the next one lands
+    __syncthreads();
+    if (kgrp == 1) return;
+    const double m1 = mm[gtid];
+    const double M = fmax(m_run, m1);
+    const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((float)((m_run - M) * cd));
+    const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((float)((m1 - M) * cd));
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] = o[db] * a0 + mo[db * NT + gtid] * a1;
+    l_part = l_part * a0 + ml[gtid] * a1;
+    m_run = M;
   }
 
-  // Merge the waves' partial results.  Each wave publishes its maximum,
-  // denominator and accumulator (row-major, 64 rows x D); then each wave
-  // merges D / kWaves of the columns for all 64 rows.
-  __syncthreads();  // every wave is out of its tile loop (the areas are reused)
-  float* accs = tiles[wave];
-#pragma unroll
-  for (int d = 0; d < D; d += 4)
-    *(f32x4*)(accs + lane * D + d) = f32x4{acc[d], acc[d + 1], acc[d + 2], acc[d + 3]};
-  m_part[wave][lane] = m_run;
-  l_part[wave][lane] = l_run;
-  __syncthreads();
-
-  double M = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) M = m_part[w][lane] > M ? m_part[w][lane] : M;
-  float f[kWaves];
-  float L = 0.f;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const double mw = m_part[w][lane];
-    f[w] = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((float)((mw - M) * cd));
-    L += f[w] * l_part[w][lane];
-  }
+  // Epilogue: the row's denominator over the four lane groups, one
+  // reciprocal, O^T element r of block db is O[row][16 db + 4 (l >> 4) + r].
+  const float L = lanes_sum(l_part);
   const float inv = L > 0.f ? 1.f / L : 0.f;
   // log-sum-exp of the row's scaled scores, ln 2 * (M*c + log2 L); -inf
   // when this key range held no key of the row
-  const float lse = L > 0.f ? (float)((M * cd + (double)__builtin_amdgcn_logf(L)) * 0.6931471805599453) : -INFINITY;
-  constexpr int DQ = D / kWaves;  // columns merged by this wave
+  const float lse = L > 0.f ? (float)((m_run * cd + (double)__builtin_amdgcn_logf(L)) * 0.6931471805599453) : -INFINITY;
   const bool part = a.splits > 1;
-  float* dst = part ? a.part_o + ((size_t)split * (a.total_tiles / per_head) * N + (size_t)bh * N) * D : nullptr;
-  if (qrow < N) {
+  if (row < N) {
+    float* dst = part ? a.part_o + ((size_t)split * (a.total_tiles / per_head) + bh) * N * D + (size_t)row * D
+                      : O + (size_t)row * ldo;
 #pragma unroll
-    for (int d = 0; d < DQ; d += 4) {
-      const int col = wave * DQ + d;
-      f32x4 out = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const f32x4 x = *(const f32x4*)(tiles[w] + lane * D + col);
-        out += f[w] * x;
-      }
+    for (int db = 0; db < DB; ++db) *(f32x4*)(dst + 16 * db + 4 * lg) = o[db] * inv;
+    if (lg == 0) {
       if (part)
-        *(f32x4*)(dst + (size_t)qrow * D + col) = out * inv;
-      else
-        *(f32x4*)(O + (size_t)qrow * ldo + col) = out * inv;
-    }
-    if (wave == 0) {
-      if (part)
-        a.part_lse[((size_t)split * (a.total_tiles / per_head) + bh) * N + qrow] = lse;
+        a.part_lse[((size_t)split * (a.total_tiles / per_head) + bh) * N + row] = lse;
       else if (a.lse != nullptr)
-        a.lse[(size_t)bh * N + qrow] = lse;
+        a.lse[(size_t)bh * N + row] = lse;
     }
   }
 }
@@ -300,49 +296,34 @@ f32k::Args f32_args(const Problem& p) {
 }
 }  // namespace
 
-hipError_t launch_f32(const Problem& p, hipStream_t stream) {
+template <int KG>
+hipError_t launch_f32_groups(const Problem& p, hipStream_t stream) {
   using namespace f32k;
   Args a = f32_args(p);
   void (*kern)(Args) = nullptr;
-  int waves = 0;
-  if (p.D == 64) {
-    kern = p.causal ? fa_forward_f32_kernel<64, true> : fa_forward_f32_kernel<64, false>;
-    waves = waves_for<64>();
+  switch (p.D) {
+    case 64: kern = p.causal ? fa_forward_f32_kernel<64, true, KG> : fa_forward_f32_kernel<64, false, KG>; break;
+    case 96: kern = p.causal ? fa_forward_f32_kernel<96, true, KG> : fa_forward_f32_kernel<96, false, KG>; break;
+    case 128: kern = p.causal ? fa_forward_f32_kernel<128, true, KG> : fa_forward_f32_kernel<128, false, KG>; break;
+    default: return hipErrorInvalidValue;
   }
-  if (p.D == 96) {
-    kern = p.causal ? fa_forward_f32_kernel<96, true> : fa_forward_f32_kernel<96, false>;
-    waves = waves_for<96>();
-  }
-  if (p.D == 128) {
-    kern = p.causal ? fa_forward_f32_kernel<128, true> : fa_forward_f32_kernel<128, false>;
-    waves = waves_for<128>();
-  }
-  if (!kern) return hipErrorInvalidValue;
   void* args[] = {&a};
-  return hipLaunchKernel((const void*)kern, dim3(a.total_tiles), dim3(kBlockM * waves), args, 0, stream);
+  return hipLaunchKernel((const void*)kern, dim3(a.total_tiles), dim3(64 * kRowWaves * KG), args, 0, stream);
+}
+
+// One key group of four waves, or two (eight waves) where the host chose
+// them (p.key_groups, grids that leave most CUs idle).
+hipError_t launch_f32(const Problem& p, hipStream_t stream) {
+  return p.key_groups == 2 && p.splits == 1 ? launch_f32_groups<2>(p, stream) : launch_f32_groups<1>(p, stream);
 }
 
 #ifdef FA_TILE_SWEEP
-// The fp32 kernel with the wave count given (the tuning library only): 2, 4
-// or 8 waves at D = 64 (8 fill 128 KiB of LDS), 2 or 4 at D = 96 and 128.
+// The fp32 kernel with the wave count given (the tuning library only): 4
+// waves (one key group) or 8 (two).
 hipError_t launch_f32_shape(const Problem& p, int waves, hipStream_t stream) {
-  using namespace f32k;
-  Args a = f32_args(p);
-  void (*kern)(Args) = nullptr;
-  if (p.D == 64) {
-    if (waves == 2) kern = p.causal ? fa_forward_f32_kernel<64, true, 2> : fa_forward_f32_kernel<64, false, 2>;
-    if (waves == 4) kern = p.causal ? fa_forward_f32_kernel<64, true, 4> : fa_forward_f32_kernel<64, false, 4>;
-    if (waves == 8) kern = p.causal ? fa_forward_f32_kernel<64, true, 8> : fa_forward_f32_kernel<64, false, 8>;
-  } else if (p.D == 96) {
-    if (waves == 2) kern = p.causal ? fa_forward_f32_kernel<96, true, 2> : fa_forward_f32_kernel<96, false, 2>;
-    if (waves == 4) kern = p.causal ? fa_forward_f32_kernel<96, true, 4> : fa_forward_f32_kernel<96, false, 4>;
-  } else if (p.D == 128) {
-    if (waves == 2) kern = p.causal ? fa_forward_f32_kernel<128, true, 2> : fa_forward_f32_kernel<128, false, 2>;
-    if (waves == 4) kern = p.causal ? fa_forward_f32_kernel<128, true, 4> : fa_forward_f32_kernel<128, false, 4>;
-  }
-  if (!kern) return hipErrorInvalidValue;
-  void* args[] = {&a};
-  return hipLaunchKernel((const void*)kern, dim3(a.total_tiles), dim3(kBlockM * waves), args, 0, stream);
+  if (waves == 4) return launch_f32_groups<1>(p, stream);
+  if (waves == 8 && p.splits == 1) return launch_f32_groups<2>(p, stream);
+  return hipErrorInvalidValue;
 }
 #endif
 

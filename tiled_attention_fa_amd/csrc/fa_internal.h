@@ -42,7 +42,7 @@ struct Problem {
   // Optional [BH, N] log-sum-exp of each row's scaled scores (splits == 1;
   // with splits > 1 the merge kernel writes it).
   float* lse = nullptr;
-  // Key groups per workgroup of the matrix-core kernel (1 or 2; 2 only with
+  // Key groups per workgroup (matrix-core kernel: 1, 2 or 4; fp32: 1 or 2; more than one only with
   // splits == 1): two wave groups share the query rows of a workgroup and
   // take alternate key tiles, merged in LDS at the end; ks_waves is that
   // workgroup's wave count (4, or 8 for D = 96 and 128).
@@ -141,10 +141,10 @@ hipError_t launch_mfma_shape_f16(const Problem& p, int waves, int occupancy, int
                                   hipStream_t stream);
 hipError_t launch_mfma_shape_bf16(const Problem& p, int waves, int occupancy, int key_groups, int block_n,
                                    hipStream_t stream);
-// The fp32 kernel's shapes: waves per workgroup (64 query rows, the key
-// tiles dealt round-robin to the waves).
-constexpr int kTuneF32Waves64[] = {2, 4, 8};
-constexpr int kTuneF32WavesWide[] = {2, 4};
+// The fp32 kernel's shapes: waves per workgroup (64 query rows, 16 per
+// wave): 4 (one key group) or 8 (two key groups taking alternate tiles).
+constexpr int kTuneF32Waves64[] = {4, 8};
+constexpr int kTuneF32WavesWide[] = {4, 8};
 hipError_t launch_f32_shape(const Problem& p, int waves, hipStream_t stream);
 #endif
 hipError_t launch_naive_f16(const NaiveProblem& p, hipStream_t stream);

@@ -165,13 +165,13 @@ def markdown(meta, rows, rows32):
     worst = max([s["max_abs_diff_vs_fa_forward"] for r in rows for s in r["shapes"]] or [0.0])
     lines += ["", f"Largest difference of any 16-bit shape's O from fa_forward's: {worst:.3e}."]
     if rows32:
-        lines += ["", "fp32 (vector kernel: 64 query rows per workgroup, 16-key tiles dealt round-robin to the "
-                  "waves, merged at the end), microseconds per launch:", "",
-                  "| case | fa_forward | 2 waves | 4 waves | 8 waves | best |", "|---|---|---|---|---|---|"]
+        lines += ["", "fp32 (matrix-core kernel: 64 query rows per workgroup, 16 per wave; 4 waves take every "
+                  "32-key tile, 8 waves form two key groups over alternate tiles), microseconds per launch:", "",
+                  "| case | fa_forward | 4 waves | 8 waves | best |", "|---|---|---|---|---|"]
         for r in rows32:
             by = {s["waves"]: s["us"] for s in r["shapes"]}
             cell = lambda wv: str(by[wv]) if wv in by else "-"
-            lines.append(f"| {r['case']} | {r['fa_forward_us']} | {cell(2)} | {cell(4)} | {cell(8)} | "
+            lines.append(f"| {r['case']} | {r['fa_forward_us']} | {cell(4)} | {cell(8)} | "
                          f"{r['best']['waves']} waves |")
         w32 = max(s["max_abs_diff_vs_fa_forward"] for r in rows32 for s in r["shapes"])
         lines += ["", f"Largest difference of any fp32 shape's O from fa_forward's: {w32:.3e}."]
