@@ -31,11 +31,12 @@
 extern "C" {
 #endif
 
-/* Storage type of q, k, v and o (all four share it).  Arithmetic is fp32
- * (scores, softmax, accumulators) whatever the storage type; 16-bit inputs
- * are multiplied on the matrix cores with fp32 accumulation (the mixed
- * precision that "Optimizing for Mobile GPUs", section "Exploit 16-bit
- * Precision", recommends: 16-bit storage, fp32 accumulation). */
+/* Storage type of q, k, v and o (all four share it).  16-bit inputs are
+ * multiplied on the matrix cores with fp32 accumulation, softmax and
+ * accumulators in fp32 (the mixed precision that "Optimizing for Mobile
+ * GPUs", section "Exploit 16-bit Precision", recommends: 16-bit storage,
+ * fp32 accumulation).  fp32 inputs form their scores on the fp64 matrix
+ * cores (exact products, fp64 sums) and the rest in fp32. */
 typedef enum fa_dtype {
   FA_F32 = 0,  /* IEEE binary32 */
   FA_F16 = 1,  /* IEEE binary16 */

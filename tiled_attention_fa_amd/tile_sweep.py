@@ -68,8 +68,8 @@ CAUSAL_CASES = [
     for H in Hs
 ]
 DTYPES = ("f16", "bf16")
-# fp32 (vector kernel): the single-head workload, longer rows at each D, and
-# a grid of several workgroups per CU
+# fp32 (matrix-core kernel, 4 or 8 waves): the single-head workload, longer
+# rows at each D, and a grid of several workgroups per CU
 F32_CASES = [
     (1, 1, 128, 64, False), (1, 8, 1024, 64, False), (1, 32, 2048, 64, True),
     (1, 2, 512, 128, False), (2, 8, 1000, 96, False), (1, 16, 1024, 128, True),
