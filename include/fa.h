@@ -229,7 +229,9 @@ int fa_splitkv_suggest(int64_t B, int64_t H, int64_t N, int64_t D, int dtype, in
  *   - causal: B*H times the one-group kernel's query blocks (256 rows; 128
  *     for D = 64 and 96) fill at most half of the device's workgroup slots
  *     (one per CU; two for D = 64; 4 at D = 96 and 128, else 2), or at most
- *     three quarters (2), except bf16 at D = 96 and 128 in that last band;
+ *     three quarters (2), except bf16 at D = 96 and 128 in that last band,
+ *     or at most once with N >= 4096 (2; 4 at D = 96; bf16 at D = 128
+ *     excepted);
  * for FA_F32, 2 when N >= 256 (eight waves over 64 query rows, two groups
  * of four taking alternate 32-key tiles); else 1.  With 2 the waves of a
  * 16-bit workgroup (64 query rows, or 128 on the

@@ -8,8 +8,11 @@ tile differs per device and has to be measured), put causal work on other
 one-group shapes than the non-causal table on MI355X, depending on how many
 passes the grid makes over the workgroup slots: 2 waves with 32-key tiles
 at D = 128 up to one pass, 4 waves with 32-key tiles beyond it (bf16
-always, fp16 outside two to three passes), 32-key tiles at D = 64 beyond
-one pass and at D = 96 from three passes.  Each case asserts the shape (the
+always, fp16 outside two to three passes and below 8192-key rows), 32-key
+tiles at D = 64 beyond a pass and a quarter (fp16 at about two passes: 8
+waves with 64-key tiles) and at D = 96 from three passes; one pass
+of rows of 4096 keys or more runs two key groups in 8-wave workgroups (four
+at D = 96; bf16 at D = 128 excepted).  Each case asserts the shape (the
 expected shapes assume a 256-CU MI355X and are skipped on other devices)
 and checks sampled rows (first and last rows, block edges, random rows of
 the first, last and random heads) against the oracle one by one, to the
@@ -39,13 +42,23 @@ CASES = [
     (1, 48, 2048, 96, "bf16", (4, 1, 32)),  # D = 96, three passes: 32-key tiles
     (4, 32, 2048, 64, "bf16", (4, 1, 32)),  # D = 64, four passes: 32-key tiles
     (1, 28, 2048, 64, "bf16", (4, 1, 64)),  # one pass: the table's tiles
+    (1, 24, 2048, 64, "bf16", (4, 1, 64)),  # three quarters at D = 64: one group
+    (1, 40, 2048, 64, "f16", (4, 1, 64)),  # a pass and a quarter: 64-key tiles
+    (1, 48, 2048, 64, "f16", (4, 1, 32)),  # a pass and a half: 32-key tiles
     (1, 12, 4096, 128, "f16", (8, 2, 64)),  # fp16 keeps two groups up to 3/4
-    (1, 14, 4096, 128, "f16", (2, 1, 32)),  # above, up to one pass
+    (1, 14, 4096, 128, "f16", (8, 2, 64)),  # above, up to one pass, rows of 4096+: two groups
+    (1, 8, 8192, 128, "f16", (8, 2, 64)),
+    (1, 8, 8192, 128, "bf16", (2, 1, 32)),  # bf16 at D = 128 keeps one group
+    (1, 8, 8192, 64, "f16", (8, 2, 64)),  # D = 64, one pass of long rows: 8 waves, two groups
+    (1, 8, 4096, 96, "f16", (8, 4, 32)),  # D = 96: four groups
     (1, 20, 4096, 128, "f16", (4, 1, 32)),  # between one and two passes
     (1, 32, 4096, 128, "f16", (8, 1, 64)),  # two passes: the table's shape
+    (1, 12, 8192, 128, "f16", (8, 1, 64)),  # 1.5 passes of 8192-key rows: the table's shape
     (1, 12, 2048, 96, "f16", (8, 2, 64)),
     (1, 48, 2048, 96, "f16", (4, 1, 32)),
     (4, 32, 2048, 64, "f16", (4, 1, 32)),
+    (1, 32, 4096, 64, "f16", (8, 1, 64)),  # fp16 D = 64 at two passes: 8 waves, 64-key tiles
+    (1, 32, 4096, 64, "bf16", (4, 1, 32)),
 ]
 
 

@@ -203,7 +203,9 @@ int suggest_splits(int64_t BH, int64_t N, int64_t D, int dtype, bool causal, int
 //    the rows that see every key set the time, 4 waves at D = 64 and 8 at
 //    D = 96 and 128 (2-29% faster), except bf16 at D = 96 and 128, which
 //    runs one group in that band too (its two-group kernels always form the
-//    two-term P; one group runs 6-17% faster); fuller grids run one group.
+//    two-term P; one group runs 6-17% faster); up to one pass with rows of
+//    4096 keys or more, 8-wave workgroups in two groups (four at D = 96;
+//    bf16 at D = 128 excepted); fuller grids run one group.
 //  * At D = 96 and 128, where those rules take the 4-wave two-group shape,
 //    four groups of two 32-row blocks with 32-key tiles run instead (8
 //    waves, two per SIMD, each chain a quarter of the keys; 1.5-7% faster
@@ -233,10 +235,20 @@ int suggest_key_groups(int64_t BH, int64_t N, int64_t D, int dtype, bool causal,
   const int64_t total = BH * ((N + block_m - 1) / block_m);
   const int64_t slots = (int64_t)cus * fa::mfma_wgs_per_cu((int)D, causal);
   if (2 * total <= slots) return small();
-  if (4 * total <= 3 * slots) {
+  // (at D = 64 a grid of exactly three quarters runs one group: 4-8% faster)
+  if (4 * total < 3 * slots || (D != 64 && 4 * total == 3 * slots)) {
     if (dtype == FA_BF16 && D != 64) return 1;
     if (D != 64) *ks_waves = 8;
     return 2;
+  }
+  // up to one pass with rows of 4096 keys or more: the blocks that see
+  // every key set the time, and 8-wave workgroups in two groups (four at
+  // D = 96) halve (quarter) their chains: 3-12% faster at N = 4096 and 8192
+  // (bf16 at D = 128 keeps one group: its two-group kernel splits P on
+  // every tile)
+  if (total <= slots && N >= 4096 && !(dtype == FA_BF16 && D == 128)) {
+    *ks_waves = 8;
+    return D == 96 ? 4 : 2;
   }
   return 1;
 }
@@ -244,14 +256,17 @@ int suggest_key_groups(int64_t BH, int64_t N, int64_t D, int dtype, bool causal,
 // The one-group shape of causal grids where it differs from the table
 // (measured on MI355X with the causal calibration sweep; f = the table
 // shape's workgroups over the CUs' workgroup slots):
-//   D = 64:  32-key tiles beyond one pass (f > 1), 4-10% faster;
+//   D = 64:  32-key tiles beyond a pass and a quarter (f > 1.25), 4-10%
+//            faster; fp16 at about two passes (1.5 < f <= 2.5) 8 waves with
+//            64-key tiles instead, 4-6% faster;
 //   D = 96:  32-key tiles from three passes (f >= 3), which halves the ring
 //            and fits two workgroups per CU, 15-20% faster;
 //   D = 128: 2 waves with 32-key tiles up to one pass (f <= 1; for fp16 only
 //            above 3/4, where the key groups do not run), 4-21% faster; 4
 //            waves with 32-key tiles beyond: bf16 always (the 8-wave bf16
 //            kernel has too few registers for split P), fp16 for 1 < f < 2
-//            and f >= 3 (2-9%), the table's 8 waves at 2 <= f < 3.
+//            with rows below 8192 keys and for f >= 3 (2-9%), the table's 8
+//            waves otherwise.
 // Sets *waves1 and *block_n1 (0 = the table's).
 void one_group_shape(int64_t BH, int64_t N, int64_t D, int dtype, bool causal, int cus, int* waves1,
                      int* block_n1) {
@@ -262,13 +277,17 @@ void one_group_shape(int64_t BH, int64_t N, int64_t D, int dtype, bool causal, i
   const int64_t total = BH * ((N + block_m - 1) / block_m);
   const int64_t slots = (int64_t)cus * fa::mfma_wgs_per_cu((int)D, causal);
   if (D == 64) {
-    if (total > slots) *block_n1 = 32;
+    if (dtype == FA_F16 && 2 * total > 3 * slots && 2 * total <= 5 * slots) {
+      *waves1 = 8;  // about two passes: 8 waves, 64-key tiles (4-6%)
+      return;
+    }
+    if (4 * total > 5 * slots) *block_n1 = 32;
   } else if (D == 96) {
     if (total >= 3 * slots) *block_n1 = 32;
   } else if (D == 128) {
     if (total <= slots) {
       *waves1 = 2;
-    } else if (dtype == FA_BF16 || total < 2 * slots || total >= 3 * slots) {
+    } else if (dtype == FA_BF16 || (total < 2 * slots && N < 8192) || total >= 3 * slots) {
       *waves1 = 4;
     } else {
       return;

@@ -50,8 +50,8 @@ struct Problem {
   int ks_waves = 4;
   // One key group and one key range: the host may replace the table's
   // workgroup shape (mfma_waves, mfma_block_n) for causal grids with
-  // waves1 waves (2 or 4 at D = 128; 0 elsewhere) and block_n1 keys per LDS
-  // tile (32); 0 keeps the table's choice.
+  // waves1 waves (2 or 4 at D = 128, 8 at D = 64; 0 elsewhere) and block_n1
+  // keys per LDS tile (32); 0 keeps the table's choice.
   int waves1 = 0;
   int block_n1 = 0;
 };

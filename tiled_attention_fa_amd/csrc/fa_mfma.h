@@ -1103,8 +1103,8 @@ inline Args make_args(const Problem& p) {
 // two key groups (p.key_groups == 2, chosen by the host for grids that leave
 // CUs idle) the workgroup is p.ks_waves waves: 2 or 4 row blocks x 2 key
 // groups.  For causal grids the host may name another one-group shape
-// (p.waves1, p.block_n1): 32-key tiles at D = 64 and 96, or 2 or 4 waves
-// with 32-key tiles at D = 128.
+// (p.waves1, p.block_n1): 32-key tiles at D = 64 and 96, 8 waves at D = 64,
+// or 2 or 4 waves with 32-key tiles at D = 128.
 template <typename T, bool SPLIT_P>
 hipError_t launch(const Problem& p, hipStream_t stream) {
   const Args a = make_args(p);
@@ -1127,12 +1127,14 @@ hipError_t launch(const Problem& p, hipStream_t stream) {
   }
   if (p.key_groups == 2) {
     // the 8-wave shapes the host may choose: non-causal D = 64 and 128,
-    // causal D = 96 and 128
+    // causal at every D
     constexpr int W = mfma_ks_waves;
     const bool w8 = p.ks_waves == 8;
     switch (p.D) {
       case 64:
-        if (p.causal) return launch_one<T, 64, true, SPLIT_P, W, mfma_ks_occupancy(64), 2>(a, p.BH, stream);
+        if (p.causal)
+          return w8 ? launch_one<T, 64, true, SPLIT_P, 8, 1, 2>(a, p.BH, stream)
+                    : launch_one<T, 64, true, SPLIT_P, W, mfma_ks_occupancy(64), 2>(a, p.BH, stream);
         return w8 ? launch_one<T, 64, false, SPLIT_P, 8, 1, 2>(a, p.BH, stream)
                   : launch_one<T, 64, false, SPLIT_P, W, mfma_ks_occupancy(64), 2>(a, p.BH, stream);
       case 96:
@@ -1149,7 +1151,9 @@ hipError_t launch(const Problem& p, hipStream_t stream) {
         return hipErrorInvalidValue;
     }
   }
-  // the host's causal shapes with 32-key tiles (p.waves1, p.block_n1)
+  // the host's causal one-group shapes (p.waves1, p.block_n1)
+  if (p.causal && p.D == 64 && p.waves1 == 8 && p.block_n1 == 0)
+    return launch_one<T, 64, true, SPLIT_P, 8, 1, 1, 64>(a, p.BH, stream);
   if (p.causal && p.block_n1 == 32) {
     if (p.D == 64 && p.waves1 == 0) return launch_one<T, 64, true, SPLIT_P, 4, 2, 1, 32>(a, p.BH, stream);
     if (p.D == 96 && p.waves1 == 0) return launch_one<T, 96, true, SPLIT_P, 4, 1, 1, 32>(a, p.BH, stream);
