@@ -212,7 +212,9 @@ int64_t fa_forward_ex_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D
  * device: 1 when B*H times the query blocks already occupy every resident
  * workgroup slot, else enough ranges to do so, at most 16 and leaving each
  * range at least 16 key tiles (shorter ranges lose more to the merge than
- * they gain).  Returns >= 1, or a negative fa_status
+ * they gain); for FA_F32 also 1 where fa_forward's own workgroup shape
+ * (fa_workgroup_shape: fewer rows, more key groups) leaves less key-tile
+ * work on one SIMD than the ranges would.  Returns >= 1, or a negative fa_status
  * (FA_ERR_DTYPE, FA_ERR_DIM, FA_ERR_UNSUPPORTED_D, FA_ERR_TOO_LARGE,
  * FA_ERR_DEVICE when no device is current).
  */
@@ -232,9 +234,15 @@ int fa_splitkv_suggest(int64_t B, int64_t H, int64_t N, int64_t D, int dtype, in
  *     three quarters (2), except bf16 at D = 96 and 128 in that last band,
  *     or at most once with N >= 4096 (2; 4 at D = 96; bf16 at D = 128
  *     excepted);
- * for FA_F32, 2 when N >= 256 (eight waves over 64 query rows, two groups
- * of four taking alternate 32-key tiles); else 1.  With 2 the waves of a
- * 16-bit workgroup (64 query rows, or 128 on the
+ * for FA_F32 (16 query rows per wave, 32-key tiles; f = B*H times the
+ * blocks of 64 rows over the CUs): for f < 1, and causal f <= 1, the shape
+ * with the least key-tile work per SIMD among 32 rows in four groups, 16
+ * rows in four, 32 rows in two and 64 rows in two (4 or 2); causal with
+ * 1 < f <= 2, 2 (32 rows per group at D = 64, 64 at D = 96 and 128);
+ * non-causal D = 128 with f >= 2, 1; else 2 when N >= 256 (64 rows in each
+ * group), 1 below, and 1 whenever N <= 32 (fa_workgroup_shape names the
+ * rows).  With 2 the waves of
+ * a 16-bit workgroup (64 query rows, or 128 on the
  * fuller of those grids) form two groups that take alternate key tiles;
  * with 4, eight waves over 64 query rows form four groups that take every
  * fourth 32-key tile.  The groups' running maxima, denominators and
@@ -250,16 +258,16 @@ int fa_key_groups_suggest(int64_t B, int64_t H, int64_t N, int64_t D, int dtype,
 /*
  * fa_workgroup_shape -- the workgroup shape fa_forward (and fa_forward_ex
  * with one key range, and fa_forward_strided) launches on the current
- * device for these sizes, for dtype FA_F16 or FA_BF16: *waves wave64s per
- * workgroup, *key_groups (1, 2 or 4, as fa_key_groups_suggest) and *block_n
- * keys per LDS tile (32 or 64), the tile loop of "Android Transformer
- * Optimization: Attention and Mobile GPU Bottlenecks", section "A Complete
- * Tile Loop", sized as "Flash Attention on Android: tiled SGEMM with
- * RenderScript", section "The detail that breaks naive ports: tile
- * calibration", asks (measured per device).  Each wave owns 32 query rows of
- * its group.  Any output pointer may be NULL.  Host only; returns FA_OK or
- * FA_ERR_DTYPE, FA_ERR_DIM, FA_ERR_UNSUPPORTED_D, FA_ERR_TOO_LARGE,
- * FA_ERR_DEVICE.
+ * device for these sizes: *waves wave64s per workgroup, *key_groups (1, 2
+ * or 4, as fa_key_groups_suggest) and *block_n keys per LDS tile (32 or
+ * 64), the tile loop of "Android Transformer Optimization: Attention and
+ * Mobile GPU Bottlenecks", section "A Complete Tile Loop", sized as "Flash
+ * Attention on Android: tiled SGEMM with RenderScript", section "The detail
+ * that breaks naive ports: tile calibration", asks (measured per device).
+ * Each wave owns 32 query rows of its group for FA_F16 and FA_BF16, 16 for
+ * FA_F32 (always 32-key tiles).  Any output pointer may be NULL.  Host
+ * only; returns FA_OK or FA_ERR_DTYPE, FA_ERR_DIM, FA_ERR_UNSUPPORTED_D,
+ * FA_ERR_TOO_LARGE, FA_ERR_DEVICE.
  */
 int fa_workgroup_shape(int64_t B, int64_t H, int64_t N, int64_t D, int dtype, int causal, int* waves,
                        int* key_groups, int* block_n);

@@ -56,22 +56,25 @@ int fa_tune_forward(const void* q, const void* k, const void* v, void* o, int64_
 /*
  * fa_tune_f32_shapes -- the workgroup shapes of the fp32 (matrix-core)
  * kernel the sweep covers for head dimension D: writes up to `capacity`
- * wave counts into waves[] (may be NULL) and returns how many there are (2:
- * 4 and 8), or FA_ERR_UNSUPPORTED_D.  A workgroup owns 64 query rows, 16 per
- * wave: 4 waves take every key tile (32 keys) of the rows, 8 waves form two
- * key groups that take alternate tiles and merge their results at the end.
- * Host only.
+ * pairs into row_waves[] and key_groups[] (either may be NULL) and returns
+ * how many there are (5: (4, 1), (4, 2), (2, 2), (2, 4), (1, 4)), or
+ * FA_ERR_UNSUPPORTED_D.  A workgroup owns 16 * row_waves query rows, 16
+ * per wave, in key_groups groups of row_waves waves that take every
+ * key_groups-th key tile (32 keys) of the rows and merge their results at
+ * the end.  Host only.
  */
-int fa_tune_f32_shapes(int64_t D, int* waves, int capacity);
+int fa_tune_f32_shapes(int64_t D, int* row_waves, int* key_groups, int capacity);
 
 /*
  * fa_tune_forward_f32 -- fa_forward with dtype FA_F32 (same arguments
  * otherwise, same checks and status codes, dense [B, H, N, D]) on the fp32
- * kernel with `waves` waves per workgroup.  A count that fa_tune_f32_shapes
- * does not list for D returns FA_ERR_UNSUPPORTED_D.  One kernel on `stream`.
+ * kernel with the shape (row_waves, key_groups).  A pair that
+ * fa_tune_f32_shapes does not list returns FA_ERR_UNSUPPORTED_D.  One
+ * kernel on `stream`.
  */
 int fa_tune_forward_f32(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H,
-                        int64_t N, int64_t D, float scale, int causal, int waves, void* stream);
+                        int64_t N, int64_t D, float scale, int causal, int row_waves, int key_groups,
+                        void* stream);
 
 /*
  * fa_tune_split_merge -- the merge kernel of fa_forward_ex's split-KV path

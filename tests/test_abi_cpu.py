@@ -273,7 +273,8 @@ def test_workgroup_shape_without_device(lib):
         pytest.skip("a device is present")
     assert fa.STATUS_NAMES[got] == "FA_ERR_DEVICE"
     assert fa.STATUS_NAMES[fa.fa_workgroup_shape(1, 8, 1000, 80, 1, False)] == "FA_ERR_UNSUPPORTED_D"
-    assert fa.STATUS_NAMES[fa.fa_workgroup_shape(1, 8, 1000, 64, 0, False)] == "FA_ERR_DTYPE"
+    assert fa.STATUS_NAMES[fa.fa_workgroup_shape(1, 8, 1000, 64, 7, False)] == "FA_ERR_DTYPE"
+    assert fa.STATUS_NAMES[fa.fa_workgroup_shape(1, 8, 1000, 64, fa.FA_F32, False)] == "FA_ERR_DEVICE"
     assert fa.STATUS_NAMES[fa.fa_workgroup_shape(1, 0, 1000, 64, 2, True)] == "FA_ERR_DIM"
 
 
@@ -350,10 +351,11 @@ def test_tune_library_exports_its_header():
     assert tile_sweep.shapes(lib, 96) == wide
     assert tile_sweep.shapes(lib, 128) == wide
     assert lib.fa_tune_shapes(80, None, None, None, None, 0) == -3
-    assert tile_sweep.f32_shapes(lib, 64) == [4, 8]
-    assert tile_sweep.f32_shapes(lib, 96) == [4, 8]
-    assert tile_sweep.f32_shapes(lib, 128) == [4, 8]
-    assert lib.fa_tune_f32_shapes(80, None, 0) == -3
+    f32 = [(4, 1), (4, 2), (2, 2), (2, 4), (1, 4)]
+    assert tile_sweep.f32_shapes(lib, 64) == f32
+    assert tile_sweep.f32_shapes(lib, 96) == f32
+    assert tile_sweep.f32_shapes(lib, 128) == f32
+    assert lib.fa_tune_f32_shapes(80, None, None, 0) == -3
 
 
 @pytest.mark.parametrize("args,status", [
@@ -382,22 +384,24 @@ def test_tune_split_merge_validation(args, status):
 @pytest.mark.parametrize("args,status", [
     (dict(B=0), "FA_ERR_DIM"),
     (dict(D=80), "FA_ERR_UNSUPPORTED_D"),
-    (dict(waves=3), "FA_ERR_UNSUPPORTED_D"),
-    (dict(D=128, waves=2), "FA_ERR_UNSUPPORTED_D"),
-    (dict(D=96, waves=16), "FA_ERR_UNSUPPORTED_D"),
+    (dict(rw=1, kg=1), "FA_ERR_UNSUPPORTED_D"),
+    (dict(D=128, rw=4, kg=4), "FA_ERR_UNSUPPORTED_D"),
+    (dict(D=96, rw=8, kg=2), "FA_ERR_UNSUPPORTED_D"),
     (dict(q=0), "FA_ERR_NULL"),
     (dict(o=A), "FA_ERR_ALIAS"),
     (dict(N=0, q=0, k=0, v=0, o=0), "FA_OK"),
     (dict(), "FA_ERR_DEVICE"),
-    (dict(D=128, waves=4), "FA_ERR_DEVICE"),
+    (dict(D=128, rw=4, kg=1), "FA_ERR_DEVICE"),
+    (dict(rw=1, kg=4), "FA_ERR_DEVICE"),
+    (dict(D=96, rw=2, kg=2), "FA_ERR_DEVICE"),
 ])
 def test_tune_forward_f32_validation(args, status):
     from tiled_attention_fa_amd import tile_sweep
     lib = tile_sweep.load_tune()
-    kw = dict(q=A, k=B_, v=C, o=O, B=1, H=1, N=64, D=64, waves=8)
+    kw = dict(q=A, k=B_, v=C, o=O, B=1, H=1, N=64, D=64, rw=4, kg=2)
     kw.update(args)
     got = lib.fa_tune_forward_f32(kw["q"] or None, kw["k"] or None, kw["v"] or None, kw["o"] or None, kw["B"],
-                                  kw["H"], kw["N"], kw["D"], 0.125, 0, kw["waves"], None)
+                                  kw["H"], kw["N"], kw["D"], 0.125, 0, kw["rw"], kw["kg"], None)
     if status == "FA_ERR_DEVICE" and got == 0:
         pytest.skip("a gfx950 device is present; the no-device path is not reachable")
     assert fa.STATUS_NAMES[got] == status

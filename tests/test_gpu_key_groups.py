@@ -17,7 +17,9 @@ choice, so every case here asserts which path it runs:
     see no key at all);
   * the same heads repeated until the grid fills the device: one group, on
     the same feature matrix (log-sum-exp output, strided layouts, grouped
-    key/value heads), so that both kernels keep that coverage.
+    key/value heads), so that both kernels keep that coverage;
+  * fp32: 16-row workgroups in four groups on small grids, and one grid per
+    band of the fp32 shape rule (fa_workgroup_shape names the shape).
 
 Tolerances as for fa_forward (gpu_helpers) and the log-sum-exp bound of the
 split-KV tests (1e-3 for 16-bit storage).
@@ -214,23 +216,55 @@ def test_strided_gqa_both_paths(dtype, D, causal):
             parity(to_numpy64(o), tile_heads(ref, Hq), dtype, f"{w.name} causal={causal} H={Hq} {layouts}")
 
 
-@pytest.mark.parametrize("N,want", [(64, 1), (255, 1), (256, 2), (1000, 2)])
+def _f32_check(B, H, N, D, causal, label):
+    w = Workload(f"kg_f32_b{B}h{H}n{N}d{D}", B, H, N, D, "f32", causal, seed=73_000 + H + N + D)
+    x = make_inputs(w)
+    ref, ref_lse = oracle.forward(x["q"], x["k"], x["v"], "f32", w.scale, causal, return_lse=True)
+    q, k, v = (to_device(x[n], "f32") for n in "qkv")
+    _say(f"[fp32 {label}] {w.name} causal={causal}")
+    o = fa.forward(q, k, v, scale=w.scale, causal=causal)
+    o2, lse = fa.forward_ex(q, k, v, scale=w.scale, causal=causal, num_splits=1, lse=True)
+    torch.cuda.synchronize()
+    parity(to_numpy64(o), ref, "f32", f"{w.name} causal={causal}")
+    parity(to_numpy64(o2), ref, "f32", f"{w.name} causal={causal} (ex)")
+    err = float(np.abs(lse.double().cpu().numpy() - ref_lse).max())
+    assert err <= LSE_TOL, f"{w.name} causal={causal}: lse error {err:.3e}"
+
+
+@pytest.mark.parametrize("N", [64, 255, 256, 1000])
 @pytest.mark.parametrize("D", [64, 96, 128])
-def test_f32_key_groups_and_parity(N, want, D):
-    """fp32: two groups of four waves once the rows have 8 or more 32-key
-    tiles, one below; both against the oracle with fa_forward (dense) and
-    fa_forward_ex (log-sum-exp), causal and not."""
-    assert fa.fa_key_groups_suggest(1, 3, N, D, fa.FA_F32, False) == want
+def test_f32_small_grid_and_parity(N, D):
+    """fp32 on a grid far smaller than the device (3 heads): 16-row
+    workgroups in four key groups (some of whose groups see no key at N =
+    64), against the oracle with fa_forward (dense) and fa_forward_ex
+    (log-sum-exp), causal and not."""
+    cus, _ = fa.fa_device_info()
+    if 3 * ((N + 63) // 64) < cus:
+        assert fa.fa_key_groups_suggest(1, 3, N, D, fa.FA_F32, False) == 4
+        assert fa.fa_workgroup_shape(1, 3, N, D, fa.FA_F32, False) == (4, 4, 32)
     for causal in (False, True):
-        w = Workload(f"kg_f32_d{D}_n{N}", 1, 3, N, D, "f32", causal, seed=73_000 + N + D)
-        x = make_inputs(w)
-        ref, ref_lse = oracle.forward(x["q"], x["k"], x["v"], "f32", w.scale, causal, return_lse=True)
-        q, k, v = (to_device(x[n], "f32") for n in "qkv")
-        _say(f"[key groups {want}] {w.name} causal={causal}")
-        o = fa.forward(q, k, v, scale=w.scale, causal=causal)
-        o2, lse = fa.forward_ex(q, k, v, scale=w.scale, causal=causal, num_splits=1, lse=True)
-        torch.cuda.synchronize()
-        parity(to_numpy64(o), ref, "f32", f"{w.name} causal={causal}")
-        parity(to_numpy64(o2), ref, "f32", f"{w.name} causal={causal} (ex)")
-        err = float(np.abs(lse.double().cpu().numpy() - ref_lse).max())
-        assert err <= LSE_TOL, f"{w.name} causal={causal}: lse error {err:.3e}"
+        _f32_check(1, 3, N, D, causal, "16r x4")
+
+
+# (H, N, D, causal) -> (waves, key groups) on a 256-CU device: one grid per
+# band of the fp32 shape rule
+F32_BANDS = [
+    (8, 1024, 64, False, (8, 4)),    # half the CUs: a tie, 32 rows in four groups
+    (16, 1024, 96, True, (8, 4)),    # causal, one 64-row block per CU
+    (16, 2048, 64, True, (4, 2)),    # causal, two per CU, D = 64: 32 rows in two groups
+    (32, 1024, 128, True, (8, 2)),   # causal, two per CU, D = 128: 64 rows in two groups
+    (16, 1024, 64, False, (8, 2)),   # full grid: 64 rows in two groups
+    (32, 1024, 128, False, (4, 1)),  # non-causal D = 128, two per CU: one group
+]
+
+
+@pytest.mark.parametrize("H,N,D,causal,want", F32_BANDS)
+def test_f32_shape_bands_and_parity(H, N, D, causal, want):
+    """The fp32 shape rule on a 256-CU device (the MI355X), one grid per
+    band, and every output element of each against the oracle."""
+    cus, _ = fa.fa_device_info()
+    if cus == 256:
+        waves, groups, bn = fa.fa_workgroup_shape(1, H, N, D, fa.FA_F32, causal)
+        assert (waves, groups, bn) == (*want, 32)
+        assert fa.fa_key_groups_suggest(1, H, N, D, fa.FA_F32, causal) == want[1]
+    _f32_check(1, H, N, D, causal, f"{want[0]} waves x{want[1]}")

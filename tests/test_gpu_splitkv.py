@@ -106,6 +106,26 @@ def test_few_heads_long_rows_split_auto():
     lse_parity(lse.reshape(2, w.N)[bh, ri], ref_lse, w.dtype, "few heads split auto")
 
 
+@pytest.mark.parametrize("N,D,causal,want", [(1024, 128, False, 1), (4096, 64, False, 4),
+                                             (2048, 64, True, 4)])
+def test_f32_split_suggestion_against_key_groups(N, D, causal, want):
+    """fp32, one head: the suggestion keeps one range where the 16-row
+    four-group workgroups leave less key-tile work per SIMD than the ranges
+    (N = 1024, D = 128), and splits where the two tie (on a 256-CU device);
+    either way every element of O and the log-sum-exp match the oracle."""
+    cus, _ = fa.fa_device_info()
+    S = fa.fa_splitkv_suggest(1, 1, N, D, fa.FA_F32, causal)
+    _say(f"[ex] fp32 N={N} D={D} causal={causal}: suggested splits {S}")
+    if cus == 256:
+        assert S == want
+    w = Workload(f"ex_f32_auto_n{N}_d{D}", 1, 1, N, D, "f32", causal, seed=31_000 + N + D)
+    x = make_inputs(w)
+    o, lse = run_ex(x, "f32", w.scale, causal, 0)
+    ref_o, ref_lse = oracle.forward(x["q"], x["k"], x["v"], "f32", w.scale, causal, return_lse=True)
+    parity(o, ref_o, "f32", f"{w.name} causal={causal} O")
+    lse_parity(lse, ref_lse, "f32", f"{w.name} causal={causal}")
+
+
 @pytest.mark.parametrize("name,splits", [("prefill_b1h32n2048d64_f16", 2),
                                          ("prefill_causal_b4h32n2048d64_bf16", 3),
                                          ("long_prefill_causal_b1h16n8192d128_f16_sigma3", 4)])

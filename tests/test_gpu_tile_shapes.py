@@ -80,17 +80,19 @@ def test_split_merge_closed_forms(tune, dtype):
 @pytest.mark.parametrize("D", [64, 96, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_every_f32_shape_matches_oracle(tune, D, causal):
-    """The fp32 kernel at every wave count of the sweep: ragged lengths (a
-    partial last 16-key tile, fewer tiles than waves), both masks."""
+    """The fp32 kernel at every shape of the sweep (rows per workgroup, key
+    groups): ragged lengths (a partial last 16-key tile, fewer tiles than
+    key groups), both masks."""
     for N, BH in ((200, (1, 2)), (129, (2, 1)), (1, (1, 1)), (40, (1, 1))):
         w = Workload(f"shape_f32_d{D}_n{N}", BH[0], BH[1], N, D, "f32", causal,
                      seed=61_000 + N + D + (1 if causal else 0))
         x = make_inputs(w)
         ref = oracle.forward(x["q"], x["k"], x["v"], "f32", w.scale, causal)
         q, k, v = (to_device(x[n], "f32") for n in "qkv")
-        for waves in tile_sweep.f32_shapes(tune, D):
-            print(f"[shape] {w.name} causal={causal} fp32 waves={waves}", flush=True)
+        for shape in tile_sweep.f32_shapes(tune, D):
+            label = tile_sweep.f32_label(shape)
+            print(f"[shape] {w.name} causal={causal} fp32 {label}", flush=True)
             o = torch.empty_like(q)
-            tile_sweep.tune_forward_f32(tune, q, k, v, o, w.scale, causal, waves, 0)
+            tile_sweep.tune_forward_f32(tune, q, k, v, o, w.scale, causal, shape, 0)
             torch.cuda.synchronize()
-            parity(to_numpy64(o), ref, "f32", f"{w.name} causal={causal} fp32 {waves} waves")
+            parity(to_numpy64(o), ref, "f32", f"{w.name} causal={causal} fp32 {label}")

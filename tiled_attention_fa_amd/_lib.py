@@ -174,8 +174,8 @@ def fa_key_groups_suggest(B: int, H: int, N: int, D: int, dtype: int, causal: bo
 
 
 def fa_workgroup_shape(B: int, H: int, N: int, D: int, dtype: int, causal: bool):
-    """(waves, key_groups, block_n) of the 16-bit forward kernel for these
-    sizes on the current device, or a negative status (an int)."""
+    """(waves, key_groups, block_n) of the forward kernel for these sizes
+    on the current device, or a negative status (an int)."""
     w, g, bn = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
     st = int(load_library().fa_workgroup_shape(int(B), int(H), int(N), int(D), int(dtype), int(bool(causal)),
                                                ctypes.byref(w), ctypes.byref(g), ctypes.byref(bn)))

@@ -169,6 +169,53 @@ int current_cus() {
   return cus;
 }
 
+// Workgroup shape of the fp32 kernel: key groups (returned) and waves of 16
+// rows per group (*row_waves), from the fp32 calibration sweep on MI355X
+// (22 grids, tile_sweep.py; f = B*H times the blocks of 64 rows over the
+// CUs):
+//  * f < 1, and causal f <= 1: the grid leaves SIMDs idle (or, causal, the
+//    rows that see every key set the time), and the shape with the least
+//    work on one SIMD runs (workgroups per CU x waves per SIMD x key tiles
+//    per group); on a tie, more waves per SIMD: 32 rows in four groups (8
+//    waves), 16 rows in four, 32 rows in two, 64 rows in two.  Up to 2.5x
+//    faster than 64-row workgroups on the smallest grids, 12-35% on causal
+//    grids of one pass.
+//  * causal 1 < f <= 2: D = 64, 32 rows in two groups (20% faster); D = 96
+//    and 128, 64 rows in two groups.
+//  * fuller grids: 64 rows, in two groups once the rows have 8 or more
+//    32-key tiles (5-12% faster there), except non-causal D = 128 from
+//    f = 2 on, where one group runs 8% faster (two 4-wave workgroups per
+//    CU in one pass, against 8-wave workgroups that registers hold to one
+//    per CU).
+int f32_key_groups(int64_t BH, int64_t N, int64_t D, bool causal, int cus, int* row_waves) {
+  *row_waves = 4;
+  const int64_t w4 = BH * ((N + 63) / 64);
+  if (N <= 32) return 1;
+  if (w4 < cus || (causal && w4 <= cus)) {
+    const int64_t nt = (N + 31) / 32;
+    static const int shapes[4][2] = {{2, 4}, {1, 4}, {2, 2}, {4, 2}};
+    int64_t best = INT64_MAX;
+    int kg = 1;
+    for (const auto& sh : shapes) {
+      const int rw = sh[0], g = sh[1];
+      const int64_t wgs = BH * ((N + 16 * rw - 1) / (16 * rw));
+      const int64_t per_simd = (wgs + cus - 1) / cus * (rw * g / 4) * ((nt + g - 1) / g);
+      if (per_simd < best) {
+        best = per_simd;
+        kg = g;
+        *row_waves = rw;
+      }
+    }
+    return kg;
+  }
+  if (causal && w4 <= 2 * (int64_t)cus) {
+    if (D == 64) *row_waves = 2;
+    return 2;
+  }
+  if (!causal && D == 128 && w4 >= 2 * (int64_t)cus) return 1;
+  return N >= 256 ? 2 : 1;
+}
+
 // Key-range splits that fill the device: enough workgroups for every
 // resident slot, while each range keeps at least 16 key tiles (measured on
 // MI355X: below that the partials' round trip through memory and the merge
@@ -185,7 +232,21 @@ int suggest_splits(int64_t BH, int64_t N, int64_t D, int dtype, bool causal, int
   const int64_t by_tiles = ((N + bn - 1) / bn) / 16;
   if (s > by_tiles) s = by_tiles;
   if (s > 16) s = 16;
-  return s < 1 ? 1 : (int)s;
+  if (s < 1) return 1;
+  if (f32) {
+    // fp32: the key-group shapes of one range compete; the ranges (64-row
+    // workgroups, one group) win unless the one-range shape leaves less
+    // key-tile work on one SIMD (3-13% faster on a tie, measured; 35% slower
+    // where the 16-row shape halves it)
+    int rw = 4;
+    const int kg = f32_key_groups(BH, N, D, causal, cus, &rw);
+    const int64_t nt = (N + 31) / 32;
+    const int64_t wgs = BH * ((N + 16 * rw - 1) / (16 * rw));
+    const int64_t one = (wgs + cus - 1) / cus * (rw * kg / 4) * ((nt + kg - 1) / kg);
+    const int64_t split = (total * s + cus - 1) / cus * ((nt + s - 1) / s);
+    if (one < split) return 1;
+  }
+  return (int)s;
 }
 
 // Key groups per workgroup (1, 2 or 4) for the matrix-core kernel, and the
@@ -212,9 +273,10 @@ int suggest_splits(int64_t BH, int64_t N, int64_t D, int dtype, bool causal, int
 //    in the sweep; at D = 64 they are slower).
 int suggest_key_groups(int64_t BH, int64_t N, int64_t D, int dtype, bool causal, int cus, int* ks_waves) {
   *ks_waves = fa::mfma_ks_waves;
-  // fp32: two groups of four waves once the rows have 8 or more 32-key
-  // tiles (5-12% faster there); the merge costs more than it saves below
-  if (dtype == FA_F32) return N >= 256 ? 2 : 1;
+  if (dtype == FA_F32) {
+    int row_waves = 4;
+    return f32_key_groups(BH, N, D, causal, cus, &row_waves);
+  }
   if (N <= 64) return 1;
   // the 4-wave two-group shape, or four groups where they measured faster
   auto small = [&]() {
@@ -299,6 +361,10 @@ void one_group_shape(int64_t BH, int64_t N, int64_t D, int dtype, bool causal, i
 // Key groups and workgroup shape of a forward problem with one key range.
 void choose_shape(fa::Problem& p, int dtype, int cus) {
   const bool causal = p.causal;
+  if (dtype == FA_F32) {
+    p.key_groups = f32_key_groups(p.BH, p.N, p.D, causal, cus, &p.f32_row_waves);
+    return;
+  }
   p.key_groups = suggest_key_groups(p.BH, p.N, p.D, dtype, causal, cus, &p.ks_waves);
   if (p.key_groups == 1) one_group_shape(p.BH, p.N, p.D, dtype, causal, cus, &p.waves1, &p.block_n1);
 }
@@ -410,7 +476,7 @@ int fa_key_groups_suggest(int64_t B, int64_t H, int64_t N, int64_t D, int dtype,
 
 int fa_workgroup_shape(int64_t B, int64_t H, int64_t N, int64_t D, int dtype, int causal, int* waves,
                        int* key_groups, int* block_n) {
-  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
   if (B < 1 || H < 1 || N < 0 || D < 1) return FA_ERR_DIM;
   if (!head_dim_supported(D)) return FA_ERR_UNSUPPORTED_D;
   if (B > ((int64_t)1 << 31) / H) return FA_ERR_TOO_LARGE;
@@ -423,7 +489,10 @@ int fa_workgroup_shape(int64_t B, int64_t H, int64_t N, int64_t D, int dtype, in
   p.causal = causal != 0;
   choose_shape(p, dtype, cus);
   int w = p.ks_waves, g = p.key_groups, bn = p.key_groups == 4 ? 32 : 64;
-  if (p.key_groups == 1) {
+  if (dtype == FA_F32) {
+    w = p.f32_row_waves * p.key_groups;
+    bn = 32;
+  } else if (p.key_groups == 1) {
     g = 1;
     w = p.waves1 ? p.waves1 : fa::mfma_waves(p.D, p.causal);
     bn = p.block_n1 ? p.block_n1 : fa::mfma_block_n(p.D, dtype == FA_BF16);
@@ -622,31 +691,34 @@ int fa_tune_forward(const void* q, const void* k, const void* v, void* o, int64_
   return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
-int fa_tune_f32_shapes(int64_t D, int* waves, int capacity) {
+int fa_tune_f32_shapes(int64_t D, int* row_waves, int* key_groups, int capacity) {
   if (!head_dim_supported(D)) return FA_ERR_UNSUPPORTED_D;
-  const int* s = D == 64 ? fa::kTuneF32Waves64 : fa::kTuneF32WavesWide;
-  const int n = D == 64 ? (int)(sizeof(fa::kTuneF32Waves64) / sizeof(int))
-                        : (int)(sizeof(fa::kTuneF32WavesWide) / sizeof(int));
-  for (int i = 0; i < n && i < capacity; ++i)
-    if (waves) waves[i] = s[i];
-  return n;
+  for (int i = 0; i < fa::kTuneF32ShapesCount && i < capacity; ++i) {
+    if (row_waves) row_waves[i] = fa::kTuneF32Shapes[i][0];
+    if (key_groups) key_groups[i] = fa::kTuneF32Shapes[i][1];
+  }
+  return fa::kTuneF32ShapesCount;
 }
 
 int fa_tune_forward_f32(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H, int64_t N,
-                        int64_t D, float scale, int causal, int waves, void* stream) {
-  int sw[8];
-  const int n = fa_tune_f32_shapes(D, sw, 8);
+                        int64_t D, float scale, int causal, int row_waves, int key_groups, void* stream) {
+  int sr[8], sg[8];
+  const int n = fa_tune_f32_shapes(D, sr, sg, 8);
   bool known = false;
-  for (int i = 0; i < n; ++i) known = known || sw[i] == waves;
+  for (int i = 0; i < n; ++i) known = known || (sr[i] == row_waves && sg[i] == key_groups);
   int64_t BH = 0;
-  const int st = validate(q, k, v, o, B, H, N, D, scale, FA_F32, fa::kF32BlockM, &BH);
+  const int64_t block_m = known ? 16 * (int64_t)row_waves : 16;
+  const int st = validate(q, k, v, o, B, H, N, D, scale, FA_F32, block_m, &BH);
   if (st == 1) return FA_OK;
   if (st != FA_OK) return st;
   if (!known) return FA_ERR_UNSUPPORTED_D;
+  // up to 16 work-items per row here, against the 8 that validate bounds
+  if (BH * ((N + block_m - 1) / block_m) * 64 * row_waves * key_groups > (int64_t)UINT32_MAX)
+    return FA_ERR_TOO_LARGE;
   const int dev = check_device();
   if (dev != FA_OK) return dev;
   fa::Problem p = dense_problem(q, k, v, o, H, BH, N, D, scale, causal);
-  const hipError_t err = fa::launch_f32_shape(p, waves, (hipStream_t)stream);
+  const hipError_t err = fa::launch_f32_shape(p, row_waves, key_groups, (hipStream_t)stream);
   return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

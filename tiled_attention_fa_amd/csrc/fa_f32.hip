@@ -9,9 +9,12 @@
 // updated, the accumulator is rescaled by exp(m_old - m_new) and
 // exp(S - m_new) V is added; O is divided by the denominator once at the end.
 //
-// A workgroup owns 64 query rows, 16 per wave, in one or two key groups of
-// four waves; group g takes the key tiles (32 keys) g, g + KG, ... and the
-// groups' results are merged at the end by the same rescaling rule.  A wave
+// A workgroup owns 16 * RW query rows (RW waves of 16 rows) in KG key groups
+// of RW waves each (KG = 1, 2 or 4); group g takes the key tiles (32 keys)
+// g, g + KG, ... and the groups' results are merged at the end by the same
+// rescaling rule.  The host takes 64-row workgroups (RW = 4) on grids that
+// fill the device and fewer rows in more groups on small ones, so that
+// more SIMDs share the rows' chains of key tiles.  A wave
 // forms S^T = K Q^T for 16 keys x its 16 rows per block: lane l holds the
 // scores of row l & 15 for keys (l >> 4) + 4e, e = 0..3.  Those four scores
 // are exactly the P^T operand of the four k-steps of O^T += V^T P^T (k-step e
@@ -25,9 +28,7 @@
 namespace fa {
 namespace f32k {
 
-constexpr int kBlockM = kF32BlockM;  // query rows per workgroup: four waves of 16
-constexpr int kRowWaves = kBlockM / 16;
-constexpr int kBlockN = 32;          // keys per LDS tile: two blocks of 16
+constexpr int kBlockN = 32;  // keys per LDS tile: two blocks of 16
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
@@ -69,23 +70,41 @@ __device__ __forceinline__ float lanes_sum(float x) {
   return x + __shfl_xor(x, 32);
 }
 
-template <int D, bool CAUSAL, int KG>
-__global__ __launch_bounds__(64 * kRowWaves * KG) void fa_forward_f32_kernel(Args a) {
+// LDS of a workgroup: a K tile and a V tile (padded rows) per key group;
+// after the loop the same bytes carry groups 1 .. KG-1's O, m and
+// denominator shares (lane by lane) to group 0.
+template <int D, int RW, int KG>
+struct Smem {
+  static constexpr int NT = 64 * RW;  // threads of one key group
+  static constexpr int K_FLOATS = KG * kBlockN * k_pitch<D>();
+  static constexpr int TILES = 4 * (K_FLOATS + KG * kBlockN * v_pitch<D>());
+  static constexpr int MO = 0;                               // f32x4 [KG-1][D/16][NT]
+  static constexpr int MM = MO + (KG - 1) * (D / 16) * NT * 16;  // double [KG-1][NT]
+  static constexpr int ML = MM + (KG - 1) * NT * 8;           // float [KG-1][NT]
+  static constexpr int MERGE = ML + (KG - 1) * NT * 4;
+  static constexpr int BYTES = TILES > MERGE ? TILES : MERGE;
+  static_assert(BYTES <= 160 * 1024, "LDS");
+};
+
+template <int D, bool CAUSAL, int RW, int KG>
+__global__ __launch_bounds__(64 * RW * KG) void fa_forward_f32_kernel(Args a) {
   constexpr int BN = kBlockN, PK = k_pitch<D>(), PV = v_pitch<D>();
-  constexpr int NT = 64 * kRowWaves;  // threads of one key group
+  constexpr int BM = 16 * RW;         // query rows per workgroup
+  constexpr int NT = 64 * RW;         // threads of one key group
   constexpr int DS = D / 4;           // k-steps of S^T = K Q^T (4 head dims each)
   constexpr int DB = D / 16;          // 16-column blocks of O
   constexpr int CH = BN * D / 4 / NT; // 16-byte loads per thread, operand and tile
-  static_assert(KG == 1 || KG == 2, "key groups");
+  using Lds = Smem<D, RW, KG>;
+  static_assert(RW == 1 || RW == 2 || RW == 4, "row waves");
+  static_assert(KG == 1 || KG == 2 || KG == 4, "key groups");
   static_assert(D % 32 == 0 && D <= 128 && CH * NT * 4 == BN * D, "head dim");
-  __shared__ __attribute__((aligned(16))) float Ks[KG][BN * PK];
-  __shared__ __attribute__((aligned(16))) float Vs[KG][BN * PV];
+  __shared__ __attribute__((aligned(16))) char smem[Lds::BYTES];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int kgrp = KG == 1 ? 0 : wave / kRowWaves;  // key group
-  const int rw = wave - kgrp * kRowWaves;           // 16-row block
+  const int kgrp = KG == 1 ? 0 : wave / RW;  // key group
+  const int rw = wave - kgrp * RW;           // 16-row block
   const int gtid = tid - kgrp * NT;                 // thread within the key group
   const int c16 = lane & 15, lg = lane >> 4;
 
@@ -111,7 +130,7 @@ __global__ __launch_bounds__(64 * kRowWaves * KG) void fa_forward_f32_kernel(Arg
   float* __restrict__ O = a.o + b * a.lo.sb + h * a.lo.sh;
   const int ldq = a.lq.sn, ldk = a.lk.sn, ldv = a.lv.sn, ldo = a.lo.sn;  // row strides
   const double cd = a.c;
-  const int q0 = qt * kBlockM + 16 * rw;  // first query row of this wave
+  const int q0 = qt * BM + 16 * rw;  // first query row of this wave
   const int row = q0 + c16;               // this lane's query row
 
   // Q^T operand: k-step s takes head dims 4s .. 4s+3; lane l holds row
@@ -126,7 +145,7 @@ __global__ __launch_bounds__(64 * kRowWaves * KG) void fa_forward_f32_kernel(Arg
   double m_run = -INFINITY;  // running maximum of the raw scores of the row
   float l_part = 0.f;        // this lane's share of the row's denominator
 
-  const int kv_end = CAUSAL ? min(N, qt * kBlockM + kBlockM) : N;
+  const int kv_end = CAUSAL ? min(N, qt * BM + BM) : N;
   const int ntiles = (kv_end + BN - 1) / BN;
   // this workgroup's share of the key tiles (all of them when splits == 1)
   const int t_lo = split * ntiles / a.splits;
@@ -134,6 +153,8 @@ __global__ __launch_bounds__(64 * kRowWaves * KG) void fa_forward_f32_kernel(Arg
 
   // Tile t of the key group: loaded by its threads into registers (16 bytes
   // each, zero past key N), then stored to the group's LDS tile.
+  float* const Ks = (float*)smem + kgrp * BN * PK;              // this group's K tile
+  float* const Vs = (float*)smem + Lds::K_FLOATS + kgrp * BN * PV;  // and V tile
   f32x4 kr[CH], vr[CH];
   auto fetch = [&](int t) {
     const int k0 = t * BN;
@@ -152,15 +173,15 @@ __global__ __launch_bounds__(64 * kRowWaves * KG) void fa_forward_f32_kernel(Arg
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int idx = i * NT + gtid, r = idx / (D / 4), c4 = idx - r * (D / 4);
-      *(f32x4*)(&Ks[kgrp][r * PK + 4 * c4]) = kr[i];
-      *(f32x4*)(&Vs[kgrp][r * PV + 4 * c4]) = vr[i];
+      *(f32x4*)(&Ks[r * PK + 4 * c4]) = kr[i];
+      *(f32x4*)(&Vs[r * PV + 4 * c4]) = vr[i];
     }
   };
 
   auto tile = [&](int t) {
     const int k0 = t * BN;
-    const float* ks = Ks[kgrp];
-    const float* vs = Vs[kgrp];
+    const float* ks = Ks;
+    const float* vs = Vs;
     // S^T for the two 16-key blocks: element e of block kb is the score of
     // key k0 + 16 kb + (l >> 4) + 4e against this lane's row
     double sc[2][4];
@@ -221,27 +242,38 @@ __global__ __launch_bounds__(64 * kRowWaves * KG) void fa_forward_f32_kernel(Arg
     if (t < t_hi && (!CAUSAL || t * BN <= q0 + 15)) tile(t);
   }
 
-  if constexpr (KG == 2) {
-    // group 1 leaves O, m and its denominator shares in LDS, lane by lane
-    // (16-byte accesses); group 0 merges by the rescaling rule
-    __shared__ __attribute__((aligned(16))) f32x4 mo[DB * NT];
-    __shared__ double mm[NT];
-    __shared__ float ml[NT];
-    if (kgrp == 1) {
+  if constexpr (KG > 1) {
+    // groups 1 .. KG-1 leave O, m and their denominator shares in LDS, lane
+    // by lane (16-byte accesses), over the tiles once every group is done
+    // with them; group 0 merges by the rescaling rule
+    f32x4* const mo = (f32x4*)(smem + Lds::MO);
+    double* const mm = (double*)(smem + Lds::MM);
+    float* const ml = (float*)(smem + Lds::ML);
+    __syncthreads();
+    if (kgrp > 0) {
+      const int j = kgrp - 1;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) mo[db * NT + gtid] = o[db];
-      mm[gtid] = m_run;
-      ml[gtid] = l_part;
+      for (int db = 0; db < DB; ++db) mo[(j * DB + db) * NT + gtid] = o[db];
+      mm[j * NT + gtid] = m_run;
+      ml[j * NT + gtid] = l_part;
     }
     __syncthreads();
-    if (kgrp == 1) return;
-    const double m1 = mm[gtid];
-    const double M = fmax(m_run, m1);
-    const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((float)((m_run - M) * cd));
-    const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((float)((m1 - M) * cd));
+    if (kgrp > 0) return;
+    double M = m_run;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) o[db] = o[db] * a0 + mo[db * NT + gtid] * a1;
-    l_part = l_part * a0 + ml[gtid] * a1;
+    for (int j = 0; j < KG - 1; ++j) M = fmax(M, mm[j * NT + gtid]);
+    const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((float)((m_run - M) * cd));
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] *= a0;
+    l_part *= a0;
+#pragma unroll
+    for (int j = 0; j < KG - 1; ++j) {
+      const double mj = mm[j * NT + gtid];
+      const float aj = mj == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((float)((mj - M) * cd));
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] += mo[(j * DB + db) * NT + gtid] * aj;
+      l_part += ml[j * NT + gtid] * aj;
+    }
     m_run = M;
   }
 
@@ -270,7 +302,7 @@ __global__ __launch_bounds__(64 * kRowWaves * KG) void fa_forward_f32_kernel(Arg
 }  // namespace f32k
 
 namespace {
-f32k::Args f32_args(const Problem& p) {
+f32k::Args f32_args(const Problem& p, int block_m) {
   using namespace f32k;
   Args a;
   a.q = (const float*)p.q;
@@ -284,7 +316,7 @@ f32k::Args f32_args(const Problem& p) {
   a.H = p.H;
   a.group = p.group;
   a.N = p.N;
-  a.num_qtiles = (p.N + kBlockM - 1) / kBlockM;
+  a.num_qtiles = (p.N + block_m - 1) / block_m;
   a.splits = p.splits;
   a.total_tiles = (int)(p.BH * a.num_qtiles * a.splits);
   a.c = __builtin_fabs((double)p.scale) * 1.4426950408889634;
@@ -294,36 +326,50 @@ f32k::Args f32_args(const Problem& p) {
   a.lse = p.lse;
   return a;
 }
-}  // namespace
 
-template <int KG>
+template <int RW, int KG>
 hipError_t launch_f32_groups(const Problem& p, hipStream_t stream) {
   using namespace f32k;
-  Args a = f32_args(p);
+  Args a = f32_args(p, 16 * RW);
   void (*kern)(Args) = nullptr;
   switch (p.D) {
-    case 64: kern = p.causal ? fa_forward_f32_kernel<64, true, KG> : fa_forward_f32_kernel<64, false, KG>; break;
-    case 96: kern = p.causal ? fa_forward_f32_kernel<96, true, KG> : fa_forward_f32_kernel<96, false, KG>; break;
-    case 128: kern = p.causal ? fa_forward_f32_kernel<128, true, KG> : fa_forward_f32_kernel<128, false, KG>; break;
+    case 64: kern = p.causal ? fa_forward_f32_kernel<64, true, RW, KG> : fa_forward_f32_kernel<64, false, RW, KG>; break;
+    case 96: kern = p.causal ? fa_forward_f32_kernel<96, true, RW, KG> : fa_forward_f32_kernel<96, false, RW, KG>; break;
+    case 128:
+      kern = p.causal ? fa_forward_f32_kernel<128, true, RW, KG> : fa_forward_f32_kernel<128, false, RW, KG>;
+      break;
     default: return hipErrorInvalidValue;
   }
   void* args[] = {&a};
-  return hipLaunchKernel((const void*)kern, dim3(a.total_tiles), dim3(64 * kRowWaves * KG), args, 0, stream);
+  return hipLaunchKernel((const void*)kern, dim3(a.total_tiles), dim3(64 * RW * KG), args, 0, stream);
 }
 
-// One key group of four waves, or two (eight waves) where the host chose
-// them (p.key_groups, grids that leave most CUs idle).
+// The workgroup shapes: (waves per key group, key groups).  More than one
+// key group only with one key range (splits == 1).
+hipError_t launch_f32_rw_kg(const Problem& p, int row_waves, int key_groups, hipStream_t stream) {
+  if (key_groups > 1 && p.splits != 1) return hipErrorInvalidValue;
+  switch (row_waves * 8 + key_groups) {
+    case 4 * 8 + 1: return launch_f32_groups<4, 1>(p, stream);
+    case 4 * 8 + 2: return launch_f32_groups<4, 2>(p, stream);
+    case 2 * 8 + 2: return launch_f32_groups<2, 2>(p, stream);
+    case 2 * 8 + 4: return launch_f32_groups<2, 4>(p, stream);
+    case 1 * 8 + 4: return launch_f32_groups<1, 4>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+}  // namespace
+
+// The host's shape (p.f32_row_waves, p.key_groups); split ranges run the
+// 64-row one-group shape.
 hipError_t launch_f32(const Problem& p, hipStream_t stream) {
-  return p.key_groups == 2 && p.splits == 1 ? launch_f32_groups<2>(p, stream) : launch_f32_groups<1>(p, stream);
+  if (p.splits != 1) return launch_f32_groups<4, 1>(p, stream);
+  return launch_f32_rw_kg(p, p.f32_row_waves, p.key_groups, stream);
 }
 
 #ifdef FA_TILE_SWEEP
-// The fp32 kernel with the wave count given (the tuning library only): 4
-// waves (one key group) or 8 (two).
-hipError_t launch_f32_shape(const Problem& p, int waves, hipStream_t stream) {
-  if (waves == 4) return launch_f32_groups<1>(p, stream);
-  if (waves == 8 && p.splits == 1) return launch_f32_groups<2>(p, stream);
-  return hipErrorInvalidValue;
+// The fp32 kernel with the shape given (the tuning library only).
+hipError_t launch_f32_shape(const Problem& p, int row_waves, int key_groups, hipStream_t stream) {
+  return launch_f32_rw_kg(p, row_waves, key_groups, stream);
 }
 #endif
 

@@ -42,12 +42,14 @@ struct Problem {
   // Optional [BH, N] log-sum-exp of each row's scaled scores (splits == 1;
   // with splits > 1 the merge kernel writes it).
   float* lse = nullptr;
-  // Key groups per workgroup (matrix-core kernel: 1, 2 or 4; fp32: 1 or 2; more than one only with
-  // splits == 1): two wave groups share the query rows of a workgroup and
-  // take alternate key tiles, merged in LDS at the end; ks_waves is that
-  // workgroup's wave count (4, or 8 for D = 96 and 128).
+  // Key groups per workgroup (1, 2 or 4; more than one only with
+  // splits == 1): the wave groups share the query rows of a workgroup and
+  // take alternate key tiles, merged in LDS at the end.  16-bit kernel:
+  // ks_waves is that workgroup's wave count (4, or 8 for D = 96 and 128).
+  // fp32 kernel: f32_row_waves waves of 16 rows per group (4, 2 or 1).
   int key_groups = 1;
   int ks_waves = 4;
+  int f32_row_waves = 4;
   // One key group and one key range: the host may replace the table's
   // workgroup shape (mfma_waves, mfma_block_n) for causal grids with
   // waves1 waves (2 or 4 at D = 128, 8 at D = 64; 0 elsewhere) and block_n1
@@ -116,7 +118,8 @@ struct NaiveProblem {
 // sizes with (larger blocks only mean fewer workgroups).  The matrix-core
 // kernel's smallest block with one key group is 128 rows; its two-key-group
 // shape (64 rows) is chosen only for grids smaller than the device's
-// workgroup slots, far below these bounds.
+// workgroup slots, far below these bounds.  Likewise the fp32 kernel's 16-
+// and 32-row shapes serve only grids smaller than the device's SIMDs.
 constexpr int kMfmaBlockM = 128;
 constexpr int kF32BlockM = 64;
 
@@ -141,11 +144,11 @@ hipError_t launch_mfma_shape_f16(const Problem& p, int waves, int occupancy, int
                                   hipStream_t stream);
 hipError_t launch_mfma_shape_bf16(const Problem& p, int waves, int occupancy, int key_groups, int block_n,
                                    hipStream_t stream);
-// The fp32 kernel's shapes: waves per workgroup (64 query rows, 16 per
-// wave): 4 (one key group) or 8 (two key groups taking alternate tiles).
-constexpr int kTuneF32Waves64[] = {4, 8};
-constexpr int kTuneF32WavesWide[] = {4, 8};
-hipError_t launch_f32_shape(const Problem& p, int waves, hipStream_t stream);
+// The fp32 kernel's shapes: (waves of 16 query rows per key group, key
+// groups taking alternate tiles), the same for every head dim.
+constexpr int kTuneF32Shapes[][2] = {{4, 1}, {4, 2}, {2, 2}, {2, 4}, {1, 4}};
+constexpr int kTuneF32ShapesCount = 5;
+hipError_t launch_f32_shape(const Problem& p, int row_waves, int key_groups, hipStream_t stream);
 #endif
 hipError_t launch_naive_f16(const NaiveProblem& p, hipStream_t stream);
 hipError_t launch_naive_bf16(const NaiveProblem& p, hipStream_t stream);

@@ -68,11 +68,15 @@ CAUSAL_CASES = [
     for H in Hs
 ]
 DTYPES = ("f16", "bf16")
-# fp32 (matrix-core kernel, 4 or 8 waves): the single-head workload, longer
-# rows at each D, and a grid of several workgroups per CU
+# fp32 (matrix-core kernel, five shapes): the single-head workload, grids
+# from a few workgroups to several per CU at each D
 F32_CASES = [
-    (1, 1, 128, 64, False), (1, 8, 1024, 64, False), (1, 32, 2048, 64, True),
-    (1, 2, 512, 128, False), (2, 8, 1000, 96, False), (1, 16, 1024, 128, True),
+    (1, 1, 128, 64, False), (1, 1, 512, 64, False), (1, 4, 256, 64, False), (1, 8, 1024, 64, False),
+    (1, 16, 1024, 64, False), (1, 16, 2048, 64, False), (1, 2, 2048, 64, True), (1, 8, 2048, 64, True),
+    (1, 4, 4096, 64, True), (1, 16, 2048, 64, True), (1, 32, 2048, 64, True), (2, 4, 512, 96, False),
+    (2, 8, 1000, 96, False), (1, 16, 1024, 96, True), (2, 16, 1024, 96, True), (1, 2, 512, 128, False),
+    (1, 1, 1024, 128, False), (1, 32, 1024, 128, False), (1, 8, 2048, 128, True), (1, 4, 4096, 128, True),
+    (1, 16, 1024, 128, True), (1, 32, 1024, 128, True),
 ]
 
 
@@ -88,10 +92,10 @@ def load_tune():
     lib.fa_tune_forward.restype = ctypes.c_int
     lib.fa_tune_split_merge.argtypes = [vp, vp, vp, vp, i64, i64, ctypes.c_int, ctypes.c_int, vp]
     lib.fa_tune_split_merge.restype = ctypes.c_int
-    lib.fa_tune_f32_shapes.argtypes = [i64, ip, ctypes.c_int]
+    lib.fa_tune_f32_shapes.argtypes = [i64, ip, ip, ctypes.c_int]
     lib.fa_tune_f32_shapes.restype = ctypes.c_int
     lib.fa_tune_forward_f32.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float, ctypes.c_int,
-                                        ctypes.c_int, vp]
+                                        ctypes.c_int, ctypes.c_int, vp]
     lib.fa_tune_forward_f32.restype = ctypes.c_int
     return lib
 
@@ -107,18 +111,25 @@ def shapes(lib, D):
 
 
 def f32_shapes(lib, D):
-    """Waves per workgroup of every fp32-kernel shape the library has for D."""
-    w = (ctypes.c_int * 8)()
-    n = lib.fa_tune_f32_shapes(D, w, 8)
+    """(waves of 16 rows per key group, key groups) of every fp32-kernel shape
+    the library has for D."""
+    r, g = (ctypes.c_int * 8)(), (ctypes.c_int * 8)()
+    n = lib.fa_tune_f32_shapes(D, r, g, 8)
     if n < 0:
         raise ValueError(f"no fp32 shapes for D={D}")
-    return [w[i] for i in range(n)]
+    return [(r[i], g[i]) for i in range(n)]
 
 
-def tune_forward_f32(lib, q, k, v, o, scale, causal, waves, stream):
+def f32_label(shape):
+    """'32r x2' = 32 query rows per workgroup in 2 key groups."""
+    rw, kg = shape
+    return f"{16 * rw}r x{kg}"
+
+
+def tune_forward_f32(lib, q, k, v, o, scale, causal, shape, stream):
     B, H, N, D = q.shape
     st = lib.fa_tune_forward_f32(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, H, N, D,
-                                 float(scale), int(causal), waves, stream)
+                                 float(scale), int(causal), shape[0], shape[1], stream)
     if st != 0:
         raise RuntimeError(f"fa_tune_forward_f32 status {st}")
 
@@ -165,14 +176,22 @@ def markdown(meta, rows, rows32):
     worst = max([s["max_abs_diff_vs_fa_forward"] for r in rows for s in r["shapes"]] or [0.0])
     lines += ["", f"Largest difference of any 16-bit shape's O from fa_forward's: {worst:.3e}."]
     if rows32:
-        lines += ["", "fp32 (matrix-core kernel: 64 query rows per workgroup, 16 per wave; 4 waves take every "
-                  "32-key tile, 8 waves form two key groups over alternate tiles), microseconds per launch:", "",
-                  "| case | fa_forward | 4 waves | 8 waves | best |", "|---|---|---|---|---|"]
+        def key32(s):  # records without the pair are the 64-row shapes (4 waves per group)
+            return (s.get("row_waves", 4), s.get("key_groups", s["waves"] // 4))
+        order = []
         for r in rows32:
-            by = {s["waves"]: s["us"] for s in r["shapes"]}
-            cell = lambda wv: str(by[wv]) if wv in by else "-"
-            lines.append(f"| {r['case']} | {r['fa_forward_us']} | {cell(4)} | {cell(8)} | "
-                         f"{r['best']['waves']} waves |")
+            for s in r["shapes"]:
+                if key32(s) not in order:
+                    order.append(key32(s))
+        lines += ["", "fp32 (matrix-core kernel, 16 query rows per wave; `Rr xG` = R query rows per workgroup "
+                  "in G key groups taking every G-th 32-key tile, R/16 waves each), microseconds per launch:", "",
+                  "| case | fa_forward | " + " | ".join(f32_label(k) for k in order) + " | best |",
+                  "|---|---|" + "---|" * len(order) + "---|"]
+        for r in rows32:
+            by = {key32(s): s["us"] for s in r["shapes"]}
+            cells = [str(by[k]) if k in by else "-" for k in order]
+            lines.append(f"| {r['case']} | {r['fa_forward_us']} | " + " | ".join(cells) +
+                         f" | {f32_label(key32(r['best']))} |")
         w32 = max(s["max_abs_diff_vs_fa_forward"] for r in rows32 for s in r["shapes"])
         lines += ["", f"Largest difference of any fp32 shape's O from fa_forward's: {w32:.3e}."]
     return "\n".join(lines) + "\n"
@@ -313,7 +332,8 @@ def main():
         for _ in range(args.rounds):
             best_lib = min(best_lib, timed(call32))
             for wv in variants:
-                targs = base + (out.data_ptr(), B, H, N, D, float(w.scale), int(causal), wv, stream.cuda_stream)
+                targs = base + (out.data_ptr(), B, H, N, D, float(w.scale), int(causal), wv[0], wv[1],
+                                stream.cuda_stream)
                 best[wv] = min(best[wv], timed(lambda: lib.fa_tune_forward_f32(*targs)))
         flops = workloads.flops(w)
         rec = {"case": w.name, "B": B, "H": H, "N": N, "D": D, "dtype": "f32", "causal": causal,
@@ -322,7 +342,8 @@ def main():
             tune_forward_f32(lib, q, k, v, out, w.scale, causal, wv, stream.cuda_stream)
             torch.cuda.synchronize()
             diff = float((out - ref).abs().max().item())
-            rec["shapes"].append({"waves": wv, "rows": 64, "us": round(best[wv], 2),
+            rec["shapes"].append({"row_waves": wv[0], "key_groups": wv[1], "waves": wv[0] * wv[1],
+                                  "rows": 16 * wv[0], "us": round(best[wv], 2),
                                   "tflops": round(flops / (best[wv] * 1e-6) / 1e12, 3),
                                   "max_abs_diff_vs_fa_forward": diff})
         rec["best"] = min(rec["shapes"], key=lambda s: s["us"])
