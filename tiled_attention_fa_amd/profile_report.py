@@ -56,7 +56,8 @@ def steady(trace_csv, rec, filt=FORWARD):
     win = rec.get("trace_window")
     if not win or not os.path.exists(trace_csv):
         return None
-    rows = [r for r in csv.DictReader(open(trace_csv)) if is_forward(r["Kernel_Name"], filt)]
+    every = list(csv.DictReader(open(trace_csv)))
+    rows = [r for r in every if is_forward(r["Kernel_Name"], filt)]
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
     k, after = win["timed_launches"], win["launches_after_timed"]
     timed = rows[len(rows) - after - k:len(rows) - after]
@@ -65,7 +66,13 @@ def steady(trace_csv, rec, filt=FORWARD):
         return None
     mid = len(us) // 2
     med = us[mid] if len(us) % 2 else 0.5 * (us[mid - 1] + us[mid])
-    return {"n": len(us), "mean_us": sum(us) / len(us), "median_us": med,
+    # time the GPU ran no kernel at all between the first and the last timed
+    # launch (kernels of one stream, one after another), per launch
+    t0, t1 = int(timed[0]["Start_Timestamp"]), int(timed[-1]["End_Timestamp"])
+    busy = sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in every
+               if int(r["Start_Timestamp"]) >= t0 and int(r["End_Timestamp"]) <= t1)
+    idle = max(0.0, (t1 - t0 - busy) / 1e3 / max(1, len(timed) - 1))
+    return {"n": len(us), "mean_us": sum(us) / len(us), "median_us": med, "gap_us": idle,
             "bench_ms_per_step_us": rec["ms_per_step"] * 1e3}
 
 
@@ -75,8 +82,12 @@ def steady_md(st):
     return (f"\nSteady state: the {st['n']} timed launches alone (from `run_kernel_trace.csv`, the clock-settle, "
             f"warm-up and\nafter-loop launches left out) average {st['mean_us']:.2f} us, median {st['median_us']:.2f} us, "
             f"against the bench's\n{st['bench_ms_per_step_us']:.3f} us per step "
-            f"({100 * (st['mean_us'] / st['bench_ms_per_step_us'] - 1):+.2f}%; the events also time the gaps between "
-            f"launches).\n")
+            f"({100 * (st['mean_us'] / st['bench_ms_per_step_us'] - 1):+.2f}%; the events also time any other kernels "
+            f"of a step and the gaps between\nlaunches; the GPU ran no kernel for {st.get('gap_us', 0.0):.2f} us per "
+            f"launch here).\n"
+            + ("\nThose idle gaps are longer than a tenth of the kernel: the next launch had not reached the GPU when "
+               "this one\nended, so the bench's events time the launch rate under the tracer, and the kernel durations "
+               "above are\nthe kernel's own.\n" if st.get("gap_us", 0.0) > 0.1 * st["mean_us"] else ""))
 
 
 def warm(W, G):
