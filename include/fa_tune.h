@@ -8,11 +8,12 @@
  * calibration" (the best size differs between devices and has to be
  * measured on each).  This library is built from the same kernel
  * sources as libfa.so, with every workgroup shape of the calibration sweep
- * instantiated (matrix-core kernel: 32 query rows per wave; 32-, 64- or
- * 128-key tiles; one or two key groups; fp32 kernel: 2, 4 or 8 waves over
- * 64 query rows), so that a sweep can time each shape on the device.  libfa.so
- * itself launches the shape its table names and is not changed by loading
- * this library.
+ * instantiated (16-bit kernel: 32 query rows per wave; 32-, 64- or
+ * 128-key tiles; one, two or four key groups; fp32 kernel: 16 query rows
+ * per wave, 64-, 32- or 16-row workgroups in one, two or four key groups),
+ * so that a sweep can time each shape on the device.  libfa.so itself
+ * launches the shape its rules name and is not changed by loading this
+ * library.
  *
  * Status codes are fa_status values from fa.h.  Nothing here allocates.
  */
