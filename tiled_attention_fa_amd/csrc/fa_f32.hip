@@ -30,12 +30,53 @@ namespace f32k {
 
 constexpr int kBlockN = 32;  // keys per LDS tile: two blocks of 16
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
-// LDS row pitches (floats).  The K operand of a k-step is row l & 15, column
-// 4s + (l >> 4) for lane l: a pitch of 4 (mod 64) words puts the 64 lanes on
-// 64 distinct banks.  The V operand is row (l >> 4) + 4e, column 16 db +
-// (l & 15): a pitch of 16 (mod 64) words does.  D = 96 takes the D = 128
+// n consecutive floats from p in 16-byte accesses (p 16-byte aligned).
+template <int n>
+__device__ __forceinline__ void load_run(const float* p, float (&out)[n]) {
+  static_assert(n % 4 == 0, "run length");
+#pragma unroll
+  for (int i = 0; i < n / 4; ++i) {
+    const f32x4 x = *(const f32x4*)(p + 4 * i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[4 * i + j] = x[j];
+  }
+}
+// Row m (0..15) of O^T block db is head dim 64 i + 4 m + j for db = 4 i + j
+// (groups of four blocks), and 64 i + 2 m + j for a last pair of blocks
+// (D = 96).  A lane's operands of every block (its row m) are then DB/4
+// runs of 4 dims and maybe one of 2, and the 16 lanes of one key row read
+// 16 consecutive runs: distinct banks.
+template <int DB>
+__device__ __forceinline__ void load_vrow(const float* row, int m, float (&out)[DB]) {
+#pragma unroll
+  for (int i = 0; i < DB / 4; ++i) {
+    const f32x4 x = *(const f32x4*)(row + 64 * i + 4 * m);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[4 * i + j] = x[j];
+  }
+  if constexpr (DB % 4 != 0) {
+    const f32x2 x = *(const f32x2*)(row + 64 * (DB / 4) + 2 * m);
+    out[DB - 2] = x[0];
+    out[DB - 1] = x[1];
+  }
+}
+template <int DB>
+__device__ __forceinline__ void store_orow(float* row, int m, const float (&in)[DB]) {
+#pragma unroll
+  for (int i = 0; i < DB / 4; ++i)
+    *(f32x4*)(row + 64 * i + 4 * m) = f32x4{in[4 * i], in[4 * i + 1], in[4 * i + 2], in[4 * i + 3]};
+  if constexpr (DB % 4 != 0) *(f32x2*)(row + 64 * (DB / 4) + 2 * m) = f32x2{in[DB - 2], in[DB - 1]};
+}
+
+// LDS row pitches (floats).  Lane l reads the K operands of a block as one
+// run of D/4 floats of row l & 15 (16-byte reads): a pitch of 4 (mod 64)
+// words starts the 16 rows 4 banks apart, so the 16 lanes of one read of
+// the run cover all 64 banks.  The V operands are runs within one row per
+// 16 lanes (load_vrow); a pitch of 16 (mod 64) words puts the rows that the
+// four lane groups read on different banks.  D = 96 takes the D = 128
 // pitches.
 template <int D>
 constexpr int k_pitch() { return D <= 64 ? 68 : 132; }
@@ -86,8 +127,14 @@ struct Smem {
   static_assert(BYTES <= 160 * 1024, "LDS");
 };
 
+// 64-row workgroups at D = 64 are held to 128 VGPRs, four waves per SIMD, so
+// that two 8-wave workgroups fit on a CU (full grids run that way).
+template <int D, int RW>
+constexpr int f32_waves_per_eu() { return D == 64 && RW == 4 ? 4 : 1; }
+
 template <int D, bool CAUSAL, int RW, int KG>
-__global__ __launch_bounds__(64 * RW * KG) void fa_forward_f32_kernel(Args a) {
+__global__ __launch_bounds__(64 * RW * KG) __attribute__((amdgpu_waves_per_eu(f32_waves_per_eu<D, RW>())))
+void fa_forward_f32_kernel(Args a) {
   constexpr int BN = kBlockN, PK = k_pitch<D>(), PV = v_pitch<D>();
   constexpr int BM = 16 * RW;         // query rows per workgroup
   constexpr int NT = 64 * RW;         // threads of one key group
@@ -133,11 +180,18 @@ __global__ __launch_bounds__(64 * RW * KG) void fa_forward_f32_kernel(Args a) {
   const int q0 = qt * BM + 16 * rw;  // first query row of this wave
   const int row = q0 + c16;               // this lane's query row
 
-  // Q^T operand: k-step s takes head dims 4s .. 4s+3; lane l holds row
-  // q0 + (l & 15), dim 4s + (l >> 4), widened to fp64 once (exact).
+  // Q^T operand: k-step s takes head dims DS j + s, j = 0..3; lane l holds
+  // row q0 + (l & 15), dim DS (l >> 4) + s, so that each lane's DS dims are
+  // one contiguous run; widened to fp64 once (exact).
   double qd[DS];
+  {
+    float qr[DS];
 #pragma unroll
-  for (int s = 0; s < DS; ++s) qd[s] = row < N ? (double)(Q[(size_t)row * ldq + 4 * s + lg] * a.qsign) : 0.0;
+    for (int s = 0; s < DS; ++s) qr[s] = 0.f;
+    if (row < N) load_run(Q + (size_t)row * ldq + DS * lg, qr);
+#pragma unroll
+    for (int s = 0; s < DS; ++s) qd[s] = (double)(qr[s] * a.qsign);
+  }
 
   f32x4 o[DB];
 #pragma unroll
@@ -188,10 +242,12 @@ __global__ __launch_bounds__(64 * RW * KG) void fa_forward_f32_kernel(Args a) {
     double mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      // the K operand in the Q operand's dim order: one contiguous run
+      float kr_[DS];
+      load_run(ks + (16 * kb + c16) * PK + DS * lg, kr_);
       f64x4 acc = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-      for (int s = 0; s < DS; ++s)
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)ks[(16 * kb + c16) * PK + 4 * s + lg], qd[s], acc, 0, 0, 0);
+      for (int s = 0; s < DS; ++s) acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)kr_[s], qd[s], acc, 0, 0, 0);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int key = k0 + 16 * kb + lg + 4 * e;
@@ -217,15 +273,17 @@ __global__ __launch_bounds__(64 * RW * KG) void fa_forward_f32_kernel(Args a) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] *= alpha;
     // O^T += V^T P^T: k-step (kb, e) takes keys 16 kb + j + 4e, j = 0..3,
-    // the j-th from lane group j, which holds it as its element e
+    // the j-th from lane group j, which holds it as its element e (lane l
+    // supplies row m = l & 15 of every block, load_vrow's dims)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
+      for (int e = 0; e < 4; ++e) {
+        float vr_[DB];
+        load_vrow(vs + (16 * kb + lg + 4 * e) * PV, c16, vr_);
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-          o[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(vs[(16 * kb + lg + 4 * e) * PV + 16 * db + c16], p[kb][e],
-                                                       o[db], 0, 0, 0);
+        for (int db = 0; db < DB; ++db) o[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(vr_[db], p[kb][e], o[db], 0, 0, 0);
+      }
   };
 
   // Every key group runs the same number of steps, so the barriers match.
@@ -278,7 +336,8 @@ __global__ __launch_bounds__(64 * RW * KG) void fa_forward_f32_kernel(Args a) {
   }
 
   // Epilogue: the row's denominator over the four lane groups, one
-  // reciprocal, O^T element r of block db is O[row][16 db + 4 (l >> 4) + r].
+  // reciprocal; O^T element r of every block is row m = 4 (l >> 4) + r of
+  // the blocks, store_orow's dims of O[row].
   const float L = lanes_sum(l_part);
   const float inv = L > 0.f ? 1.f / L : 0.f;
   // log-sum-exp of the row's scaled scores, ln 2 * (M*c + log2 L); -inf
@@ -289,7 +348,12 @@ __global__ __launch_bounds__(64 * RW * KG) void fa_forward_f32_kernel(Args a) {
     float* dst = part ? a.part_o + ((size_t)split * (a.total_tiles / per_head) + bh) * N * D + (size_t)row * D
                       : O + (size_t)row * ldo;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) *(f32x4*)(dst + 16 * db + 4 * lg) = o[db] * inv;
+    for (int r = 0; r < 4; ++r) {
+      float run[DB];
+#pragma unroll
+      for (int db = 0; db < DB; ++db) run[db] = o[db][r] * inv;
+      store_orow(dst, 4 * lg + r, run);
+    }
     if (lg == 0) {
       if (part)
         a.part_lse[((size_t)split * (a.total_tiles / per_head) + bh) * N + row] = lse;
