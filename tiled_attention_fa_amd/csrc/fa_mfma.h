@@ -1043,7 +1043,51 @@ void fa_forward_kernel(Args a) {
     return;
   }
   if (a.lse != nullptr && qrow < N && hi == 0) a.lse[(size_t)bh * N + qrow] = lse;
-  if (qrow < N) {
+  if constexpr (KS == 1 && !CAUSAL) {
+    // One key group, no mask: every wave gets here after the same work,
+    // and the ring is free once all of them have.  Each wave stages its
+    // 32 x D tile of O (16-bit) in a region of the ring, then stores it row
+    // by row: each store instruction writes 512 contiguous bytes of a dense
+    // O, where storing from the accumulator layout writes 16 bytes into
+    // each of 32 rows (8 MB of O by a full grid: 3.0 against 4.6 us).
+    // (Causal waves finish at different times; making the early ones wait
+    // at the barrier costs more than the stores gain.)
+    __syncthreads();
+    constexpr int REGION = 32 * D;      // elements per wave
+    constexpr int WPA = TILE / REGION;  // regions per ring array
+    constexpr int CPR8 = D / 4;         // 8-byte chunks per row
+    static_assert(WPA >= 1 && (NW + WPA - 1) / WPA <= 8, "O staging fits the ring");
+    const int arr = wave / WPA;
+    uint16_t* base = arr == 0 ? kbuf(I0{}) : arr == 1 ? kbuf(I1{}) : arr == 2 ? kbuf(I2{}) : arr == 3 ? kbuf(I3{})
+                   : arr == 4 ? vbuf(I0{}) : arr == 5 ? vbuf(I1{}) : arr == 6 ? vbuf(I2{}) : vbuf(I3{});
+    base += (wave - arr * WPA) * REGION;
+    // 8-byte chunk c8 of row r sits at chunk pchunk(r, c8) of the row: the
+    // 32 rows that one write instruction touches (one chunk each) and the
+    // rows that one read instruction covers fall on distinct banks
+    auto pchunk = [](int r, int c8) {
+      if constexpr (D == 64) return c8 ^ ((r >> 1) & 15);
+      else if constexpr (D == 96) return (c8 & ~7) | ((c8 ^ (r >> 2)) & 7);
+      else return c8 ^ (r & 31);
+    };
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        // elements 4g..4g+3 are columns 32 db + 8 g + 4 hi .. +3 of row l32
+        const int c8 = 8 * db + 2 * g + hi;
+        const u32x2 out = {Ops<T>::pack(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
+                           Ops<T>::pack(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
+        *(u32x2*)(base + 4 * (l32 * CPR8 + pchunk(l32, c8))) = out;
+      }
+    // the wave's own writes, read back by other lanes of the wave
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < CPR8 / 2; ++i) {
+      const int ci = 64 * i + lane, r = ci / CPR8, c8 = ci - r * CPR8;
+      const u32x2 v = *(const u32x2*)(base + 4 * (r * CPR8 + pchunk(r, c8)));
+      if (q0 + r < N) *(u32x2*)(O + (size_t)(q0 + r) * ldo + 4 * c8) = v;
+    }
+  } else if (qrow < N) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
