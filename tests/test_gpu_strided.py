@@ -110,6 +110,32 @@ def test_output_guard_and_inputs_untouched():
     parity(to_numpy64(o), ref, "f16", "guarded strided output")
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("D", [64, 96, 128])
+def test_full_grid_ragged_rows_guarded(dtype, D):
+    """A full non-causal grid (64 heads, one key group; its waves stage O
+    through LDS and store whole rows) with N = 1000, so the last row block
+    of every head has rows past N: O sits in a buffer with sentinel columns
+    on both sides of each row and a sentinel head after the last one.  The
+    guards stay untouched and every element matches the oracle."""
+    H, N = 64, 1000
+    shape = fa.fa_workgroup_shape(1, H, N, D, {"f16": fa.FA_F16, "bf16": fa.FA_BF16}[dtype], False)
+    assert shape[1] == 1, f"expected one key group, got {shape}"
+    w = Workload(f"str_full_{dtype}_d{D}", 1, H, N, D, dtype, False, seed=4300 + D)
+    x = make_inputs(w)
+    q, k, v = (bits_to(x[n], dtype, "bhnd") for n in "qkv")
+    tdt = torch.float16 if dtype == "f16" else torch.bfloat16
+    buf = torch.full((1, H + 1, N, D + 16), 3.0, dtype=tdt, device="cuda:0")
+    o = buf[:, :H, :, 8:8 + D]
+    _say(f"[strided] {w.name} shape={shape}")
+    fa.fa_forward_strided(q, k, v, o, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.all(buf[..., :8] == 3.0) and torch.all(buf[..., 8 + D:] == 3.0), "row guards written"
+    assert torch.all(buf[:, H] == 3.0), "guard head written"
+    ref = oracle.forward(x["q"], x["k"], x["v"], dtype, w.scale, False)
+    parity(to_numpy64(o), ref, dtype, f"{w.name} full grid, guarded")
+
+
 def test_strided_rejected_calls_raise():
     q = torch.zeros((1, 4, 64, 64), dtype=torch.float16, device="cuda:0")
     kv = torch.zeros((1, 3, 64, 64), dtype=torch.float16, device="cuda:0")
