@@ -232,7 +232,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              f"(heads are independent; see the sharding notes in DESIGN.md)", file=sys.stderr)
+              f"(the library runs on one GPU; heads are independent, so a caller shards them)", file=sys.stderr)
         sys.exit(2)
 
     import torch
